@@ -1,0 +1,30 @@
+"""CPU oracle for the chunked Kimi Delta Attention (KDA) forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, links or runs anything in
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it. It shares no code, headers, tables or constants with the HIP
+library; the two meet only through the seeded inputs of ``workloads.py``.
+
+Contents
+  recurrent.py    fp64 token-by-token recurrence: the definition of the forward.
+  chunked.py      fp64 chunked (WY/UT) form as the pages lay it out, plus the two
+                  unit-lower-triangular inverses (forward substitution and the Neumann
+                  doubling product). Used only as an invariant (chunked == recurrent) and as
+                  a diagnostic of the per-chunk intermediates.
+  exact.py        the recurrence in exact rational arithmetic (fractions.Fraction) for tiny
+                  inputs with rational decays.
+  kda_oracle.c    the fp64 token recurrence in plain C, threaded over independent
+                  (sequence, value head) units; the fast oracle for large workloads.
+  native.py       ctypes loader for the C oracle.
+  build.py        compiles kda_oracle.c with gcc.
+
+Sources (pages, by title): the KDA definition is read off the chunked listing in "手撕KDA"
+("KDA by hand"), section 1 (the FLA naive_chunk_kda routine): a one-token chunk of that
+listing reduces to the recurrence in recurrent.py, and section 5 of the same page names the
+recurrent kernel (fused_recurrent_kda) as the cross-check of the chunked one. The
+Neumann product follows "KDA源码剖析之FlashKDA（上）", part 12 (Neumann series inverse),
+and the FlashKDA Neumann-inverse walkthrough page.
+
+Every function here is pinned by tests/test_oracle.py against closed forms, special cases,
+exact rational arithmetic, hand-worked fixtures (tests/golden/) and library routines.
+"""
