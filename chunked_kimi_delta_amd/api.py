@@ -1,0 +1,114 @@
+"""Python entry points with the same names as the C ABI (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import KDA_BF16, KDA_FP32, KdaFwdArgs, load, strerror
+
+_IO = {torch.bfloat16: KDA_BF16, torch.float32: KDA_FP32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class KdaFwdPlan:
+    """Validated arguments for repeated kda_fwd calls on the same tensors.
+
+    q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV,K]; beta [B,T,HV] (all bf16 or all fp32, on one
+    HIP device); cu_seqlens int64 [N+1] on the device (then B == 1) or None; initial_state fp32
+    [N,HV,K,V] or None. Outputs o (io dtype, like v) and final_state (fp32, or None) and the
+    workspace are allocated once through torch and reused by every call().
+    """
+
+    def __init__(self, q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
+                 output_final_state=True, workspace=None, o=None, final_state=None):
+        self.lib = load()
+        if q.dtype not in _IO:
+            raise TypeError(f"unsupported io dtype {q.dtype} (bf16 or fp32)")
+        dev = q.device
+        if dev.type != "cuda":
+            raise ValueError("inputs must be on a HIP device")
+        B, T, H, K = q.shape
+        HV, V = v.shape[2], v.shape[3]
+        dt = q.dtype
+        _check(q, "q", dt, (B, T, H, K), dev)
+        _check(k, "k", dt, (B, T, H, K), dev)
+        _check(v, "v", dt, (B, T, HV, V), dev)
+        _check(g, "g", dt, (B, T, HV, K), dev)
+        _check(beta, "beta", dt, (B, T, HV), dev)
+        if cu_seqlens is not None:
+            if cu_seqlens.dtype != torch.int64 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+                raise ValueError("cu_seqlens must be a 1-D int64 tensor on the inputs' device")
+            N = cu_seqlens.numel() - 1
+        else:
+            N = B
+        if initial_state is not None:
+            _check(initial_state, "initial_state", torch.float32, (N, HV, K, V), dev)
+        self.o = torch.empty_like(v) if o is None else o
+        _check(self.o, "o", dt, (B, T, HV, V), dev)
+        if output_final_state:
+            self.final_state = (torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+                                if final_state is None else final_state)
+            _check(self.final_state, "final_state", torch.float32, (N, HV, K, V), dev)
+        else:
+            self.final_state = None
+        a = KdaFwdArgs()
+        a.B, a.T, a.N, a.H, a.HV, a.K, a.V, a.io = B, T, N, H, HV, K, V, _IO[dt]
+        a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+        a.scale = float("nan") if scale is None else float(scale)
+        a.cu_seqlens = _ptr(cu_seqlens)
+        a.initial_state = _ptr(initial_state)
+        a.o = _ptr(self.o)
+        a.final_state = _ptr(self.final_state)
+        self.args = a
+        self._keep = (q, k, v, g, beta, cu_seqlens, initial_state)
+        need = int(self.lib.kda_fwd_workspace_bytes(ctypes.byref(a)))
+        if need == 0 and B * T > 0:
+            raise ValueError("unsupported shapes (K and V must be 64 or 128; HV % H == 0)")
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        elif workspace.numel() < need:
+            raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+        self.workspace = workspace
+        self.ws_bytes = workspace.numel()
+        self.device = dev
+
+    def __call__(self, stream=None):
+        """Enqueue the forward on `stream` (default: torch's current stream)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        st = self.lib.kda_fwd(ctypes.byref(self.args), ctypes.c_void_p(self.workspace.data_ptr()),
+                              self.ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"kda_fwd failed: {strerror(st)} ({st})")
+        return self.o, self.final_state
+
+
+def kda_fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
+            output_final_state=True, workspace=None):
+    """KDA forward. Returns (o, final_state or None); see KdaFwdPlan for shapes."""
+    plan = KdaFwdPlan(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_final_state,
+                      workspace)
+    return plan()
+
+
+def workspace_bytes(B, T, N, H, HV, K, V, io=KDA_BF16) -> int:
+    """Workspace bytes kda_fwd needs for these shapes (0 if unsupported)."""
+    a = KdaFwdArgs()
+    a.B, a.T, a.N, a.H, a.HV, a.K, a.V, a.io = B, T, N, H, HV, K, V, io
+    return int(load().kda_fwd_workspace_bytes(ctypes.byref(a)))

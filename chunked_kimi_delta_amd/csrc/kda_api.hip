@@ -1,0 +1,138 @@
+// kda_api.hip -- the extern "C" boundary of libkda_fwd (declared in include/kda_fwd.h).
+//
+// Host side only: argument validation, workspace sizing and the two launches on the
+// caller's stream. Launch arguments follow the pages' statement of the problem: shapes and
+// grouping of naive_chunk_kda ("手撕KDA" section 1) and the packed-sequence arguments of the
+// FlashKDA prepare launch ("KDA源码剖析之FlashKDA（上）" parts 3 and 4: scale, total tokens,
+// heads, number of sequences, cu_seqlens, an upper bound on the number of chunk tiles).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kda_fwd.h"
+#include "kda_internal.h"
+
+namespace {
+
+using namespace kda;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Returns KDA_OK and fills the derived sizes, or the status kda_fwd must return.
+kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots,
+                        size_t *chunk_bytes)
+{
+    if (!a) return KDA_ERR_INVALID_ARG;
+    if (a->B < 1 || a->T < 0 || a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H)
+        return KDA_ERR_INVALID_ARG;
+    if (a->cu_seqlens) {
+        if (a->B != 1 || a->N < 1) return KDA_ERR_INVALID_ARG;
+    } else if (a->N != a->B) {
+        return KDA_ERR_INVALID_ARG;
+    }
+    const bool k_ok = a->K == 64 || a->K == 128, v_ok = a->V == 64 || a->V == 128;
+    if (!k_ok || !v_ok) return KDA_ERR_UNSUPPORTED;
+    if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_UNSUPPORTED;
+    const int64_t tt = (int64_t)a->B * a->T;
+    const int64_t ns = tt / CHUNK + a->N;
+    if (ns > INT32_MAX || (int64_t)a->HV > 65535) return KDA_ERR_UNSUPPORTED;
+    size_t cb;
+    if (a->io == KDA_BF16) {
+        cb = a->K == 64 ? (a->V == 64 ? WsBf16<64, 64>::BYTES : WsBf16<64, 128>::BYTES)
+                        : (a->V == 64 ? WsBf16<128, 64>::BYTES : WsBf16<128, 128>::BYTES);
+    } else {
+        cb = a->K == 64 ? (a->V == 64 ? WsF32<64, 64>::BYTES : WsF32<64, 128>::BYTES)
+                        : (a->V == 64 ? WsF32<128, 64>::BYTES : WsF32<128, 128>::BYTES);
+    }
+    *T_total = tt;
+    *n_slots = ns;
+    *chunk_bytes = cb;
+    return KDA_OK;
+}
+
+template <int K, int V>
+hipError_t dispatch(const FwdParams &p, int io, hipStream_t st)
+{
+    hipError_t e;
+    if (io == KDA_BF16) {
+        if (p.seq.T_total > 0 && (e = launch_prepare_bf16<K, V>(p, st)) != hipSuccess) return e;
+        return launch_state_bf16<K, V>(p, st);
+    }
+    if (p.seq.T_total > 0 && (e = launch_prepare_f32<K, V>(p, st)) != hipSuccess) return e;
+    return launch_state_f32<K, V>(p, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_fwd_workspace_bytes(const kda_fwd_args *a)
+{
+    int64_t tt, ns;
+    size_t cb;
+    if (check_shapes(a, &tt, &ns, &cb) != KDA_OK) return 0;
+    return (size_t)ns * (size_t)a->HV * cb;
+}
+
+kda_status kda_fwd(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void *stream)
+{
+    int64_t tt, ns;
+    size_t cb;
+    const kda_status st = check_shapes(a, &tt, &ns, &cb);
+    if (st != KDA_OK) return st;
+    if (a->N > 0 || tt > 0) {
+        const void *ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
+        for (const void *ptr : ptrs)
+            if (tt > 0 && (!ptr || !aligned16(ptr))) return KDA_ERR_INVALID_ARG;
+    }
+    if (a->initial_state && !aligned16(a->initial_state)) return KDA_ERR_INVALID_ARG;
+    if (a->final_state && !aligned16(a->final_state)) return KDA_ERR_INVALID_ARG;
+    if (a->cu_seqlens && !aligned16(a->cu_seqlens)) return KDA_ERR_INVALID_ARG;
+    const size_t need = (size_t)ns * (size_t)a->HV * cb;
+    if (tt > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
+        return KDA_ERR_WORKSPACE;
+    if (a->N == 0) return KDA_OK;
+
+    FwdParams p;
+    p.seq.cu = a->cu_seqlens;
+    p.seq.T = a->T;
+    p.seq.T_total = tt;
+    p.seq.N = a->N;
+    p.seq.n_slots = (int32_t)ns;
+    p.H = a->H;
+    p.HV = a->HV;
+    p.G = a->HV / a->H;
+    p.scale = (a->scale > 0.f && !isnan(a->scale)) ? a->scale : 1.0f / sqrtf((float)a->K);
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.g = a->g;
+    p.beta = a->beta;
+    p.h0 = a->initial_state;
+    p.o = a->o;
+    p.ht = a->final_state;
+    p.ws = (uint8_t *)workspace;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (a->K == 64)
+        e = a->V == 64 ? dispatch<64, 64>(p, a->io, s) : dispatch<64, 128>(p, a->io, s);
+    else
+        e = a->V == 64 ? dispatch<128, 64>(p, a->io, s) : dispatch<128, 128>(p, a->io, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char *kda_strerror(int status)
+{
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (K and V must be 64 or 128)";
+    case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case KDA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+// kda_internal.h -- device-side building blocks of libkda_fwd (gfx950 / CDNA4 only).
+//
+// Layout vocabulary used by every kernel (wave64, 16x16 MFMA tiles; g = lane / 16 is the
+// lane group, r or n = lane % 16 the lane within its 16-lane row):
+//   C-layout    of a 16x16 fp32 tile X: lane (g, n) holds X[4g + i][n], i = 0..3. This is
+//               the accumulator layout of v_mfma_f32_16x16x{16,32}_{bf16,f16}.
+//   A16-layout  (16x16x16 A operand): lane (g, m) holds X[m][4g + i], i = 0..3.
+//   B16-layout  (16x16x16 B operand): lane (g, n) holds X[4g + i][n] == C-layout.
+//   A32/B32     (16x16x32): lane (g, m) holds X[m][kappa = 8g .. 8g + 7] (A) and
+//               X[kappa = 8g .. 8g + 7][n] (B).
+//   Two identities follow and are used throughout: the registers of C(X) ARE the A16-layout
+//   of X^T, so an MFMA with A = C(X) and B = I produces C(X^T) (a register transpose on the
+//   matrix core); and C-layout == B16-layout, so a product's accumulator feeds the next
+//   product as B without moving data between lanes.
+//   TPL         "token per lane": lane (g, r) holds row (token) r, columns 16c + 4g + i for
+//               every 16-column tile c. It is the A16-layout of every tile, and step s of a
+//               16x16x32 product over the column axis pairs tiles (2s, 2s+1):
+//               kappa = 8g + e  <->  column 16(2s + e/4) + 4g + e%4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int CHUNK = 16;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ----------------------------------------------------------------------------- parameters
+
+// Sequence geometry shared by both kernels. Sequence s covers tokens [bos_s, eos_s) of the
+// packed token axis; its chunk c lives in workspace slot floor(bos_s / 16) + s + c. The map is
+// injective and every slot is < T_total / 16 + N (so the prepare grid is that bound).
+struct SeqGeom {
+    const int64_t *cu;   // device [N + 1] or nullptr (dense: bos_s = s * T)
+    int64_t T;           // dense per-sequence length
+    int64_t T_total;     // tokens on the packed axis (B * T)
+    int32_t N;           // sequences
+    int32_t n_slots;     // T_total / 16 + N
+};
+
+struct FwdParams {
+    SeqGeom seq;
+    int32_t H, HV, G;
+    float scale;
+    const void *q, *k, *v, *g, *beta;
+    const float *h0;
+    void *o;
+    float *ht;
+    uint8_t *ws;
+};
+
+// Workspace of one (value head, slot) chunk, bf16 io. All fragments are stored in the exact
+// per-lane order the state kernel's MFMAs consume, so every state-kernel load is a contiguous
+// 64-lane vector load:
+//   W   [K/32][64 lanes][8] fp16   w in TPL; step s holds tiles (2s, 2s+1)
+//   QD  [K/32][64][8]       fp16   scale * q * exp(Gam), same order
+//   KR  [K/32][64][8]       fp16   k * exp(gam - Gam) in C-layout of each 16-key-dim tile
+//                                  (= A16-layout of KR^T); pair s holds tiles (2s, 2s+1)
+//   U   [V/16][64][4]       fp16   u = A v in C-layout (rows = tokens), one 16-column slice
+//   MQK [64][4]             fp16   Mqk in A16-layout
+//   EG  [K]                 fp32   exp(gam), natural key-dim order
+template <int K, int V>
+struct WsBf16 {
+    static constexpr int W = 0;
+    static constexpr int QD = W + 32 * K;
+    static constexpr int KR = QD + 32 * K;
+    static constexpr int U = KR + 32 * K;
+    static constexpr int MQK = U + 32 * V;
+    static constexpr int EG = MQK + 512;
+    static constexpr int END = EG + 4 * K;
+    static constexpr int BYTES = (END + 255) / 256 * 256;
+};
+
+// Workspace of one chunk, fp32 io: plain row-major fp32 arrays.
+//   W [16][K], QD [16][K], KR [16][K], U [16][V], MQK [16][16], EG [K]
+template <int K, int V>
+struct WsF32 {
+    static constexpr int W = 0;
+    static constexpr int QD = W + 64 * K;
+    static constexpr int KR = QD + 64 * K;
+    static constexpr int U = KR + 64 * K;
+    static constexpr int MQK = U + 64 * V;
+    static constexpr int EG = MQK + 1024;
+    static constexpr int END = EG + 4 * K;
+    static constexpr int BYTES = (END + 255) / 256 * 256;
+};
+
+// ----------------------------------------------------------------------------- sequences
+
+__device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+    return x < lo ? lo : (x > hi ? hi : x);
+}
+
+__device__ __forceinline__ int64_t seq_bos(const SeqGeom &sg, int s) {
+    const int64_t b = sg.cu ? sg.cu[s] : (int64_t)s * sg.T;
+    return clamp64(b, 0, sg.T_total);
+}
+
+__device__ __forceinline__ int64_t seq_eos(const SeqGeom &sg, int s, int64_t bos) {
+    const int64_t e = sg.cu ? sg.cu[s + 1] : (int64_t)(s + 1) * sg.T;
+    return clamp64(e, bos, sg.T_total);
+}
+
+__device__ __forceinline__ int64_t slot_base(const SeqGeom &sg, int s) {
+    return seq_bos(sg, s) / CHUNK + s;
+}
+
+// Slot -> (sequence, chunk start, valid rows). Binary search for the last sequence whose
+// first slot is <= slot (the first-slot map is nondecreasing for valid offsets; for invalid
+// ones the search still ends inside [0, N)). Returns false for slots that hold no chunk.
+// Every lane computes the same values (uniform addresses).
+__device__ __forceinline__ bool locate_slot(const SeqGeom &sg, int slot, int *s_out,
+                                            int64_t *bos_out, int *nvalid_out) {
+    if (sg.N <= 0) return false;
+    int lo = 0, hi = sg.N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (slot_base(sg, mid) <= slot) lo = mid; else hi = mid - 1;
+    }
+    const int64_t bos_s = seq_bos(sg, lo);
+    const int64_t eos_s = seq_eos(sg, lo, bos_s);
+    const int64_t c = (int64_t)slot - (bos_s / CHUNK + lo);
+    const int64_t nc = (eos_s - bos_s + CHUNK - 1) / CHUNK;
+    if (c < 0 || c >= nc) return false;
+    *s_out = lo;
+    *bos_out = bos_s + CHUNK * c;
+    const int64_t nv = eos_s - *bos_out;
+    *nvalid_out = (int)(nv < CHUNK ? nv : CHUNK);
+    return true;
+}
+
+// ----------------------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
+    return __uint_as_float((uint32_t)x << 16);
+}
+
+// four consecutive bf16 (8 bytes) -> fp32
+__device__ __forceinline__ void unpack_bf16x4(uint2 raw, float out[4]) {
+    out[0] = bf16lo(raw.x); out[1] = bf16hi(raw.x);
+    out[2] = bf16lo(raw.y); out[3] = bf16hi(raw.y);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(const float x[4]) {
+    bf16x4 r;
+    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+    return r;
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    bf16x4 r;
+    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+    return r;
+}
+__device__ __forceinline__ f16x4 to_f16x4(const float x[4]) {
+    f16x4 r;
+    r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
+    return r;
+}
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
+    f16x4 r;
+    r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
+    return r;
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ----------------------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16x16x16 product on the fp32 matrix core: D = A B + C with A in A16-layout and B in
+// B16-layout (fp32, one value per i), as four v_mfma_f32_16x16x4_f32. Instruction i contracts
+// the columns 4g + i of A with the rows 4g + i of B (its k index is the lane group g), so the
+// A16/B16/C register roles of the 16-bit products carry over unchanged.
+__device__ __forceinline__ f32x4 mm16_f32(f32x4 a, f32x4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+
+// ----------------------------------------------------------------------------- lanes
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lane % 16 = token index). Lanes
+// shifted in from outside the row contribute 0.
+__device__ __forceinline__ float row_inclusive_scan(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return x;
+}
+
+// value of x held by lane `src` (0..63)
+__device__ __forceinline__ float lane_read(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+}  // namespace kda
+
+// Host-side launchers (defined next to their kernels).
+namespace kda {
+template <int K, int V> hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_state_bf16(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_state_f32(const FwdParams &p, hipStream_t st);
+}  // namespace kda

@@ -1,0 +1,336 @@
+// kda_prepare.hip -- stage 1 of the chunked KDA forward: everything that depends only on one
+// 16-token chunk of one value head, computed independently for every (chunk, value head).
+//
+// For a chunk with in-chunk token index i (rows past the end of the sequence are zero with
+// g = 0, "KDA源码剖析之FlashKDA（上）" part 7) the kernel forms
+//     Gam_i = sum_{tau <= i} g_tau      gam = Gam_15                     (part 7: cumsum)
+//     L     = beta_row * strict_tril(kd . ki^T),  Mqk = tril(qd' . ki^T) (parts 9-11)
+//     A     = (I + L)^{-1} diag(beta)  by the Neumann doubling product   (part 12)
+//     w = A (k exp(Gam)),  u = A v,  qd = scale q exp(Gam),  kr = k exp(gam - Gam), exp(gam)
+// which is the per-chunk half of naive_chunk_kda ("手撕KDA" section 1) and of the v8 prepare
+// kernel of "手撕KDA" section 5 (w and u formed in stage 1).
+//
+// gfx950 design (bf16 io). One wave64 per (chunk, value head); no LDS at all:
+//  * q, k, g, v are loaded in TPL (8-byte loads, lane = token row) and upcast to fp32.
+//  * The cumsum over the 16 tokens is a DPP row scan (the 16 lanes of a DPP row are the 16
+//    tokens), in log2 units so every exponential is one v_exp_f32.
+//  * The decayed Gram matrices use factors centred on token 7 (kd' = k 2^(G - G7), ki' = k
+//    2^(G7 - G)): products keep the exact exponent difference while each factor spans only
+//    half the chunk's decay range. The factors are split hi + lo in bf16 and multiplied in
+//    three 16x16x32 MFMA passes (hi.hi + hi.lo + lo.hi), about 16 mantissa bits.
+//  * The Neumann product runs on the fp32 matrix core entirely in registers, using C(X) ==
+//    A-layout of X^T so that every power is formed in both orientations directly (no
+//    transposes through memory); the "+ INV" of each doubling step is the accumulator.
+//  * k exp(Gam), v and kr are moved from TPL to the column-per-lane layout the token-axis
+//    products need by an MFMA against the identity (exact for bf16/fp16 inputs).
+//  * Outputs go to the workspace as fp16 in the state kernel's lane order (kda_internal.h).
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int K, int V>
+__global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
+{
+    constexpr int NK = K / 16;     // 16-wide key-dim tiles
+    constexpr int NV = V / 16;     // 16-wide value-dim tiles
+    constexpr int NS = K / 32;     // 16x16x32 steps over the key dims
+    using WS = WsBf16<K, V>;
+
+    const int lane = threadIdx.x;
+    const int grp = lane >> 4;
+    const int r = lane & 15;       // TPL: token row. C-layout: column index.
+    const int slot = blockIdx.x;
+    const int j = blockIdx.y;
+    const int h = j / p.G;
+
+    int s;
+    int64_t bos;
+    int nvalid;
+    if (!locate_slot(p.seq, slot, &s, &bos, &nvalid)) return;
+    const bool live = r < nvalid;
+    const int64_t tok = bos + r;
+
+    // ---------------------------------------------------------------- loads (TPL)
+    float qf[NK][4], kf[NK][4], gl[NK][4];
+    uint2 vraw[NV];
+    float beta_r = 0.f;
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { qf[c][i] = 0.f; kf[c][i] = 0.f; gl[c][i] = 0.f; }
+#pragma unroll
+    for (int c = 0; c < NV; ++c) vraw[c] = make_uint2(0u, 0u);
+    if (live) {
+        const uint16_t *qp = (const uint16_t *)p.q + ((tok * p.H + h) * K + 4 * grp);
+        const uint16_t *kp = (const uint16_t *)p.k + ((tok * p.H + h) * K + 4 * grp);
+        const uint16_t *gp = (const uint16_t *)p.g + ((tok * p.HV + j) * K + 4 * grp);
+        const uint16_t *vp = (const uint16_t *)p.v + ((tok * p.HV + j) * V + 4 * grp);
+        uint2 qr[NK], kr[NK], gr[NK];
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            qr[c] = *(const uint2 *)(qp + 16 * c);
+            kr[c] = *(const uint2 *)(kp + 16 * c);
+            gr[c] = *(const uint2 *)(gp + 16 * c);
+        }
+#pragma unroll
+        for (int c = 0; c < NV; ++c) vraw[c] = *(const uint2 *)(vp + 16 * c);
+        beta_r = bf16_bits_to_f32(((const uint16_t *)p.beta)[tok * p.HV + j]);
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            unpack_bf16x4(qr[c], qf[c]);
+            unpack_bf16x4(kr[c], kf[c]);
+            unpack_bf16x4(gr[c], gl[c]);
+        }
+    }
+
+    // ---------------------------------------------------------------- cumsum (log2 units)
+    float G2[NK][4], ref[NK][4], gam[NK][4];
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[c][i] * LOG2E);
+    const int lane7 = (lane & 48) | 7, lane15 = lane | 15;
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ref[c][i] = lane_read(G2[c][i], lane7);
+            gam[c][i] = lane_read(G2[c][i], lane15);
+        }
+
+    // ---------------------------------------------------------------- decay factors
+    const float sc = p.scale;
+    float KD[NK][4], QD[NK][4], KRv[NK][4];
+    bf16x8 kdh[NS], kdl[NS], kih[NS], kil[NS], qdh[NS], qdl[NS];
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float d1 = G2[c][i] - ref[c][i];
+            const float e1 = __builtin_amdgcn_exp2f(d1);
+            const float e2 = __builtin_amdgcn_exp2f(-d1);
+            const float eA = __builtin_amdgcn_exp2f(G2[c][i]);
+            const float eR = __builtin_amdgcn_exp2f(gam[c][i] - G2[c][i]);
+            const float kk = kf[c][i], qq = sc * qf[c][i];
+            KD[c][i] = kk * eA;
+            QD[c][i] = qq * eA;
+            KRv[c][i] = kk * eR;
+            const float xd = kk * e1, xi = kk * e2, xq = qq * e1;
+            const int st = c >> 1, e = (c & 1) * 4 + i;
+            const __bf16 hd = (__bf16)xd, hi_ = (__bf16)xi, hq = (__bf16)xq;
+            kdh[st][e] = hd; kdl[st][e] = (__bf16)(xd - (float)hd);
+            kih[st][e] = hi_; kil[st][e] = (__bf16)(xi - (float)hi_);
+            qdh[st][e] = hq; qdl[st][e] = (__bf16)(xq - (float)hq);
+        }
+
+    // ---------------------------------------------------------------- L and Mqk (C-layout)
+    f32x4 Lacc = zero4(), Macc = zero4();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        Lacc = mfma32(kdh[st], kih[st], Lacc);
+        Macc = mfma32(qdh[st], kih[st], Macc);
+        Lacc = mfma32(kdh[st], kil[st], Lacc);
+        Macc = mfma32(qdh[st], kil[st], Macc);
+        Lacc = mfma32(kdl[st], kih[st], Lacc);
+        Macc = mfma32(qdl[st], kih[st], Macc);
+    }
+    float b4[4], Mq[4];
+    f32x4 L, eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * grp + i;
+        b4[i] = lane_read(beta_r, row);                 // beta of token `row` (lanes 0..15)
+        L[i] = row > r ? b4[i] * Lacc[i] : 0.f;         // beta_i (kd_i . ki_j), i > j
+        Mq[i] = row >= r ? Macc[i] : 0.f;               // qd_i . ki_j, i >= j
+        eye[i] = row == r ? 1.f : 0.f;
+    }
+    const bf16x4 Ib = to_bf16x4(eye);
+    const f16x4 Ih = to_f16x4(eye);
+
+    // ---------------------------------------------------------------- Neumann inverse
+    // M = L^T. INV accumulates (I + M)^{-1} = (I - M)(I + M^2)(I + M^4)(I + M^8), which is
+    // C(((I + L)^{-1})^T); X^T of every power comes from the swapped product. The powers of L
+    // can be far larger than the inverse (keys that are nearly parallel make L^m grow like
+    // binomial coefficients, up to C(14, 7) for m = 8, while (I + L)^{-1} stays O(1)), so the
+    // product is evaluated on the fp32 matrix core: 16-bit operands would lose the inverse to
+    // cancellation.
+    const f32x4 Mf = mm16_f32(L, eye, zero4());         // C(M): transpose on the matrix core
+    const f32x4 P2 = mm16_f32(L, Mf, zero4());          // C(M M)       (A16 of M == C(L))
+    const f32x4 Q2 = mm16_f32(Mf, L, zero4());          // C((M^2)^T)   (A16 of L == C(M))
+    const f32x4 P4 = mm16_f32(Q2, P2, zero4());         // C(M^4)
+    const f32x4 Q4 = mm16_f32(P2, Q2, zero4());         // C((M^4)^T)
+    const f32x4 Q8 = mm16_f32(P4, Q4, zero4());         // C((M^8)^T) == A16 of M^8
+    f32x4 INV = eye - Mf;
+    INV = mm16_f32(Q2, INV, INV);                       // (I + M^2)(I - M)
+    INV = mm16_f32(Q4, INV, INV);                       // (I + M^4) ...
+    INV = mm16_f32(Q8, INV, INV);                       // (I + M^8) ...
+    float AT[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) AT[i] = INV[i] * b4[i];  // A^T = diag(beta) (I + L)^{-T}
+    const bf16x4 ATb = to_bf16x4(AT);                    // B-layout of A^T == A-layout of A
+
+    uint8_t *ws = p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES;
+
+    // ---------------------------------------------------------------- w = A KD  (TPL out)
+    f16x4 wT[NK];
+#pragma unroll
+    for (int c = 0; c < NK; ++c) {
+        const f32x4 kdC = mfma16(to_bf16x4(KD[c]), Ib, zero4());     // C(KD_c)
+        wT[c] = to_f16x4(mfma16(to_bf16x4(kdC), ATb, zero4()));      // C((A KD_c)^T)
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        *(f16x8 *)(ws + WS::W + (st * 64 + lane) * 16) = cat(wT[2 * st], wT[2 * st + 1]);
+
+    // ---------------------------------------------------------------- u = A V  (C-layout)
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+        const bf16x4 vA = __builtin_bit_cast(bf16x4, vraw[c]);
+        const f32x4 vC = mfma16(vA, Ib, zero4());                    // C(V_c)
+        *(f16x4 *)(ws + WS::U + (c * 64 + lane) * 8) =
+            to_f16x4(mfma16(ATb, to_bf16x4(vC), zero4()));           // C(A V_c)
+    }
+
+    // ---------------------------------------------------------------- qd (TPL), kr (C)
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        *(f16x8 *)(ws + WS::QD + (st * 64 + lane) * 16) =
+            cat(to_f16x4(QD[2 * st]), to_f16x4(QD[2 * st + 1]));
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const f32x4 a = mfma16(to_f16x4(KRv[2 * st]), Ih, zero4());
+        const f32x4 b = mfma16(to_f16x4(KRv[2 * st + 1]), Ih, zero4());
+        *(f16x8 *)(ws + WS::KR + (st * 64 + lane) * 16) = cat(to_f16x4(a), to_f16x4(b));
+    }
+
+    // ---------------------------------------------------------------- Mqk (A-layout)
+    *(f16x4 *)(ws + WS::MQK + lane * 8) = to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4()));
+
+    // ---------------------------------------------------------------- exp(gam)
+    if (r == 15) {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            float4 e;
+            e.x = __builtin_amdgcn_exp2f(G2[c][0]);
+            e.y = __builtin_amdgcn_exp2f(G2[c][1]);
+            e.z = __builtin_amdgcn_exp2f(G2[c][2]);
+            e.w = __builtin_amdgcn_exp2f(G2[c][3]);
+            *(float4 *)(ws + WS::EG + (16 * c + 4 * grp) * 4) = e;
+        }
+    }
+}
+
+// =============================================================================== fp32 io
+// Plain fp32 evaluation of the same chunk quantities (a correctness mode: no MFMA, the
+// decayed Gram entries use exp of the exact exponent difference, the inverse is the same
+// Neumann doubling product). One 256-thread block per (chunk, value head).
+template <int K, int V>
+__global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
+{
+    using WS = WsF32<K, V>;
+    __shared__ float sq[16][K + 1], sk[16][K + 1], sG[16][K + 1], sv[16][V + 1];
+    __shared__ float sb[16], sL[16][17], sI[16][17], sP[16][17], sT[16][17];
+    const int tid = threadIdx.x;
+    const int slot = blockIdx.x, j = blockIdx.y, h = j / p.G;
+    int s;
+    int64_t bos;
+    int nvalid;
+    if (!locate_slot(p.seq, slot, &s, &bos, &nvalid)) return;
+
+    const float *q = (const float *)p.q, *k = (const float *)p.k;
+    const float *v = (const float *)p.v, *g = (const float *)p.g;
+    for (int idx = tid; idx < 16 * K; idx += 256) {
+        const int rr = idx / K, d = idx % K;
+        const bool ok = rr < nvalid;
+        const int64_t t = bos + rr;
+        sq[rr][d] = ok ? q[(t * p.H + h) * K + d] : 0.f;
+        sk[rr][d] = ok ? k[(t * p.H + h) * K + d] : 0.f;
+        sG[rr][d] = ok ? g[(t * p.HV + j) * K + d] : 0.f;
+    }
+    for (int idx = tid; idx < 16 * V; idx += 256) {
+        const int rr = idx / V, d = idx % V;
+        sv[rr][d] = rr < nvalid ? v[((bos + rr) * p.HV + j) * V + d] : 0.f;
+    }
+    if (tid < 16) sb[tid] = tid < nvalid ? ((const float *)p.beta)[(bos + tid) * p.HV + j] : 0.f;
+    __syncthreads();
+    for (int d = tid; d < K; d += 256) {               // inclusive cumsum per key dim
+        float acc = 0.f;
+        for (int rr = 0; rr < 16; ++rr) { acc += sG[rr][d]; sG[rr][d] = acc; }
+    }
+    __syncthreads();
+
+    const int i = tid >> 4, jj = tid & 15;
+    float Lij = 0.f, Mij = 0.f;
+    if (i >= jj) {
+        for (int d = 0; d < K; ++d) {
+            const float kd = sk[jj][d] * __expf(sG[i][d] - sG[jj][d]);
+            Lij += sk[i][d] * kd;
+            Mij += sq[i][d] * kd;
+        }
+    }
+    const float Lv = i > jj ? sb[i] * Lij : 0.f;
+    const float Mv = i >= jj ? p.scale * Mij : 0.f;
+    sL[i][jj] = Lv;                   // P = L
+    sI[i][jj] = (i == jj ? 1.f : 0.f) - Lv;
+    __syncthreads();
+    for (int it = 0; it < 3; ++it) {  // P <- P^2 ; INV <- INV + INV P
+        float acc = 0.f;
+        for (int m = 0; m < 16; ++m) acc += sL[i][m] * sL[m][jj];
+        __syncthreads();
+        sL[i][jj] = acc;
+        __syncthreads();
+        float add = 0.f;
+        for (int m = 0; m < 16; ++m) add += sI[i][m] * sL[m][jj];
+        sT[i][jj] = sI[i][jj] + add;
+        __syncthreads();
+        sI[i][jj] = sT[i][jj];
+        __syncthreads();
+    }
+    sP[i][jj] = sI[i][jj] * sb[jj];   // A = INV diag(beta)
+    __syncthreads();
+
+    float *ws = (float *)(p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES);
+    for (int idx = tid; idx < 16 * K; idx += 256) {
+        const int t = idx / K, d = idx % K;
+        float acc = 0.f;
+        for (int m = 0; m < 16; ++m) acc += sP[t][m] * sk[m][d] * __expf(sG[m][d]);
+        ws[WS::W / 4 + t * K + d] = acc;
+        ws[WS::QD / 4 + t * K + d] = p.scale * sq[t][d] * __expf(sG[t][d]);
+        ws[WS::KR / 4 + t * K + d] = sk[t][d] * __expf(sG[15][d] - sG[t][d]);
+    }
+    for (int idx = tid; idx < 16 * V; idx += 256) {
+        const int t = idx / V, d = idx % V;
+        float acc = 0.f;
+        for (int m = 0; m < 16; ++m) acc += sP[t][m] * sv[m][d];
+        ws[WS::U / 4 + t * V + d] = acc;
+    }
+    ws[WS::MQK / 4 + i * 16 + jj] = Mv;
+    for (int d = tid; d < K; d += 256) ws[WS::EG / 4 + d] = __expf(sG[15][d]);
+}
+
+template <int K, int V>
+hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st)
+{
+    dim3 grid(p.seq.n_slots, p.HV);
+    prepare_bf16_kernel<K, V><<<grid, dim3(64), 0, st>>>(p);
+    return hipGetLastError();
+}
+
+template <int K, int V>
+hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st)
+{
+    dim3 grid(p.seq.n_slots, p.HV);
+    prepare_f32_kernel<K, V><<<grid, dim3(256), 0, st>>>(p);
+    return hipGetLastError();
+}
+
+#define KDA_INST(K, V)                                                               \
+    template hipError_t launch_prepare_bf16<K, V>(const FwdParams &, hipStream_t);  \
+    template hipError_t launch_prepare_f32<K, V>(const FwdParams &, hipStream_t);
+KDA_INST(64, 64)
+KDA_INST(64, 128)
+KDA_INST(128, 64)
+KDA_INST(128, 128)
+#undef KDA_INST
+
+}  // namespace kda

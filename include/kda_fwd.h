@@ -1,0 +1,103 @@
+/*
+ * kda_fwd.h -- C ABI of libkda_fwd: the chunked Kimi Delta Attention (KDA) forward on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the KDA definition, read off the chunked listing of "手撕KDA" ("KDA by
+ * hand"), section 1, naive_chunk_kda): for every sequence s and value head j, with q/k head
+ * h = j / (HV / H) and a state S in R^{K x V} that starts at initial_state[s, j] (or zero),
+ * each token t of the sequence does
+ *
+ *     S <- diag(exp(g[t, j, :])) S;   r = v[t, j, :] - S^T k[t, h, :];
+ *     S <- S + beta[t, j] k[t, h, :] r^T;   o[t, j, :] = scale * S^T q[t, h, :]
+ *
+ * and final_state[s, j] is S after the last token. The library evaluates it in the chunked
+ * form of the same section with chunks of 16 tokens: a token-parallel prepare kernel (in-chunk
+ * cumsum of g, decayed q/k, the strictly lower triangular L and the masked Mqk, the inverse of
+ * (I + L) by the Neumann doubling product of "KDA源码剖析之FlashKDA（上）" part 12, and
+ * w = A (exp(G) k), u = A v) followed by a chunk-sequential state kernel.
+ *
+ * Conventions
+ *  - All tensor pointers are DEVICE pointers, caller-owned, contiguous (row-major), and
+ *    16-byte aligned. The library allocates nothing, keeps no global state and is re-entrant
+ *    (concurrent calls must use distinct workspaces and outputs).
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream). Nothing
+ *    synchronises; the caller owns synchronisation. Results are deterministic (no atomics).
+ *  - Errors are reported only through the return value; nothing aborts or throws.
+ */
+#ifndef KDA_FWD_H
+#define KDA_FWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,  /* null required pointer, bad shape, misalignment, B != 1 with
+                                 cu_seqlens, N != B without cu_seqlens, HV % H != 0         */
+    KDA_ERR_UNSUPPORTED = 2,  /* K or V outside {64, 128}, unknown io dtype                  */
+    KDA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than kda_fwd_workspace_bytes()    */
+    KDA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)                    */
+} kda_status;
+
+typedef enum {
+    KDA_BF16 = 0,             /* q, k, v, g, beta, o in bf16; states fp32; fp32 accumulation */
+    KDA_FP32 = 1              /* everything fp32                                             */
+} kda_dtype;
+
+typedef struct {
+    /* Shapes. Dense batch: q is [B, T, H, K] and sequence b spans tokens [b*T, (b+1)*T) of
+       the packed token axis (N must equal B). Varlen: B == 1, T = total tokens, and sequence
+       s spans [cu_seqlens[s], cu_seqlens[s+1]) ("KDA源码剖析之FlashKDA（上）", part 4:
+       sequences packed along one token axis). Any length >= 0 is accepted, including 0 and
+       lengths that are not multiples of 16.                                                */
+    int32_t B, T, N;
+    int32_t H, HV;            /* q/k heads and value heads, HV % H == 0 (grouped value heads,
+                                 "手撕KDA" section 1: value head j uses q/k head j / (HV/H)) */
+    int32_t K, V;             /* head dims, each in {64, 128}                               */
+    int32_t io;               /* kda_dtype                                                  */
+    const void *q;            /* [B, T, H, K]   io dtype                                    */
+    const void *k;            /* [B, T, H, K]   io dtype                                    */
+    const void *v;            /* [B, T, HV, V]  io dtype                                    */
+    const void *g;            /* [B, T, HV, K]  io dtype; per-key-dim decay in natural-log
+                                 units (exp(g) multiplies the state). The chunked
+                                 factorisation needs every 16-token in-chunk sum of g to stay
+                                 above about -170 per key dim (fp32 exponent range); g <= 0 is
+                                 expected but not enforced.                                 */
+    const void *beta;         /* [B, T, HV]     io dtype; used as given (no sigmoid)        */
+    float scale;              /* output scale; <= 0 or NaN selects K^-0.5                   */
+    const int64_t *cu_seqlens;/* device [N + 1] token offsets (cu[0] = 0, nondecreasing,
+                                 cu[N] = T), or NULL for a dense batch. Contents cannot be
+                                 validated without a synchronisation: invalid offsets give
+                                 undefined values but every access stays in bounds.         */
+    const float *initial_state; /* [N, HV, K, V] fp32, or NULL for zeros                    */
+    void *o;                  /* [B, T, HV, V]  io dtype, written for every token            */
+    float *final_state;       /* [N, HV, K, V] fp32, or NULL to skip                        */
+} kda_fwd_args;
+
+/* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
+   Returns 0 for arguments kda_fwd would reject. The workspace holds the prepare kernel's
+   per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma)) for ceil-bounded chunk slots of every
+   value head: (B*T/16 + N) * HV slots of 17,408 B (bf16, K = V = 128). */
+size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
+
+/* Enqueue the forward: prepare kernel, then state kernel, on `stream` (hipStream_t or NULL).
+   `workspace` is a device buffer of at least kda_fwd_workspace_bytes(args) bytes, 256-byte
+   aligned, owned by the caller; its contents on entry do not matter. Returns KDA_OK when both
+   launches were enqueued. */
+kda_status kda_fwd(const kda_fwd_args *args, void *workspace, size_t ws_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_FWD_H */

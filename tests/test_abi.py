@@ -1,0 +1,123 @@
+"""The C-ABI library: loads, exports every symbol include/*.h declares, sizes workspaces and
+rejects bad arguments with status codes (CPU only: no call here reaches a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import chunked_kimi_delta_amd as kda
+from chunked_kimi_delta_amd import _lib
+from chunked_kimi_delta_amd._lib import KdaFwdArgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.library_path()):
+        from chunked_kimi_delta_amd.build import build
+        build()
+    return kda.load()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(kda_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["kda_fwd", "kda_fwd_workspace_bytes", "kda_strerror",
+                                    "kda_version"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def args(**kw):
+    a = KdaFwdArgs()
+    d = dict(B=1, T=4096, N=1, H=16, HV=16, K=128, V=128, io=0)
+    d.update(kw)
+    for key, val in d.items():
+        setattr(a, key, val)
+    return a
+
+
+def test_workspace_bytes(lib):
+    f = lambda a: lib.kda_fwd_workspace_bytes(ctypes.byref(a))
+    assert f(args()) == (4096 // 16 + 1) * 16 * 17408
+    assert f(args(K=64, V=64)) == (4096 // 16 + 1) * 16 * 8960
+    assert f(args(io=1)) == (4096 // 16 + 1) * 16 * 34304
+    assert f(args(B=4, T=8192, N=4, H=16, HV=32)) == (4 * 8192 // 16 + 4) * 32 * 17408
+    assert f(args(T=45, N=1)) == (45 // 16 + 1) * 16 * 17408
+    assert f(args(K=96)) == 0          # unsupported head dim
+    assert f(args(HV=24, H=16)) == 0   # HV % H != 0
+    assert f(args(N=2)) == 0           # dense batch needs N == B
+    assert f(args(B=0)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(V=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(io=7), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(HV=24), _lib.KDA_ERR_INVALID_ARG),
+    (dict(N=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.KDA_ERR_INVALID_ARG),
+    (dict(), _lib.KDA_ERR_INVALID_ARG),            # null tensor pointers
+])
+def test_kda_fwd_rejects_bad_arguments(lib, kw, status):
+    a = args(**kw)
+    assert lib.kda_fwd(ctypes.byref(a), None, 0, None) == status
+
+
+def test_kda_fwd_checks_alignment_and_workspace(lib):
+    a = args(T=32)
+    fake = 1 << 40                                # never dereferenced: rejected before launch
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        setattr(a, name, fake)
+    assert lib.kda_fwd(ctypes.byref(a), None, 0, None) == _lib.KDA_ERR_WORKSPACE
+    need = lib.kda_fwd_workspace_bytes(ctypes.byref(a))
+    assert lib.kda_fwd(ctypes.byref(a), ctypes.c_void_p(fake), need - 1, None) == \
+        _lib.KDA_ERR_WORKSPACE
+    assert lib.kda_fwd(ctypes.byref(a), ctypes.c_void_p(fake + 16), need, None) == \
+        _lib.KDA_ERR_WORKSPACE                   # workspace must be 256-byte aligned
+    a.q = fake + 8                                # 16-byte alignment of tensors
+    assert lib.kda_fwd(ctypes.byref(a), ctypes.c_void_p(fake), need, None) == \
+        _lib.KDA_ERR_INVALID_ARG
+    b = args(T=32, B=2, N=1)
+    b.cu_seqlens = fake                           # varlen requires B == 1
+    assert lib.kda_fwd(ctypes.byref(b), None, 0, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_fwd(None, None, 0, None) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_strerror_and_version(lib):
+    for st in range(5):
+        assert kda._lib.strerror(st)
+    assert "unknown" in kda._lib.strerror(99)
+    assert lib.kda_version() == 100
+
+
+def test_product_path_has_no_fallback(monkeypatch, tmp_path):
+    # with the library missing, the binding raises instead of computing anything itself
+    monkeypatch.setenv("KDA_FWD_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        kda.load()
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "chunked_kimi_delta_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".h", ".cpp")):
+            src = open(path, encoding="utf-8").read()
+            assert not re.search(r"^\s*(from|import)\s+oracle", src, flags=re.M), path
+            assert "kda_oracle" not in src, path

@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Bar (stated once, used everywhere): relative L2 error ||x_gpu - x_ref|| / ||x_ref|| over the
+whole compared tensor, computed in fp64, of o and of final_state:
+    bf16 io  <= 5e-3        fp32 io  <= 1e-4
+Small cases run the oracle over every (sequence, value head); the full-size workloads run the
+launch configuration bench.py times and compare a seeded sample of whole (sequence, value head)
+units (every token of o and the final state of each sampled unit), plus finiteness everywhere.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle.chunked import chunk_prepare
+from oracle.native import kda_oracle_c
+from ws_decode import chunk_bytes, decode_chunk
+
+import chunked_kimi_delta_amd as kda
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": 5e-3, "fp32": 1e-4}
+DEV = "cuda:0"
+
+
+def dev(x):
+    return None if x is None else x.to(DEV).contiguous()
+
+
+def gpu_plan(inp: W.Inputs, scale=None, output_final_state=True):
+    return kda.KdaFwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                          scale=scale, cu_seqlens=dev(inp.cu_seqlens),
+                          initial_state=dev(inp.h0), output_final_state=output_final_state)
+
+
+def gpu_run(inp: W.Inputs, **kw):
+    plan = gpu_plan(inp, **kw)
+    o, fin = plan()
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    fin = None if fin is None else fin.cpu().numpy().astype(np.float64)
+    return o, fin
+
+
+def oracle_run(inp: W.Inputs, units=None, scale=None):
+    f = W.as_f32_numpy
+    return kda_oracle_c(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta),
+                        inp.scale if scale is None else scale,
+                        None if inp.h0 is None else inp.h0.numpy(),
+                        None if inp.cu_seqlens is None else inp.cu_seqlens.numpy(),
+                        units=units)
+
+
+def rel_l2(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+
+def o_flat(o, inp):
+    return o.reshape(-1, o.shape[2], o.shape[3])       # [T_total, HV, V]
+
+
+def check_all(inp, o, fin, o_ref, f_ref, tol):
+    assert np.isfinite(o).all() and np.isfinite(fin).all()
+    eo, ef = rel_l2(o, o_ref), rel_l2(fin, f_ref)
+    assert eo <= tol and ef <= tol, f"rel L2 o={eo:.3e} final={ef:.3e} > {tol}"
+    return eo, ef
+
+
+SMALL = {
+    "tiny_fp32": W.WORKLOADS["tiny_fp32"],
+    "bf16_b2_t100_gva_h0": W.custom(B=2, T=100, H=2, HV=4, K=128, V=128, h0_std=0.1),
+    "bf16_k64v64_t77": W.custom(B=1, T=77, H=3, HV=3, K=64, V=64),
+    "bf16_k64v128_t50": W.custom(B=1, T=50, H=1, HV=2, K=64, V=128),
+    "bf16_k128v64_t50_h0": W.custom(B=1, T=50, H=2, HV=2, K=128, V=64, h0_std=0.1),
+    "bf16_varlen_edges": W.custom(H=1, HV=2, K=128, V=128, h0_std=0.1,
+                                  lengths=(0, 1, 15, 16, 17, 100, 33, 0)),
+    "bf16_strong_decay": W.custom(B=1, T=200, H=2, HV=2, K=128, V=128, g_lo=0.5, g_hi=0.9999,
+                                  beta_std=2.0),
+    "bf16_t1": W.custom(B=3, T=1, H=1, HV=1, K=128, V=128, h0_std=0.1),
+    "fp32_varlen_gva": W.custom(H=2, HV=4, K=128, V=128, dtype="fp32", h0_std=0.1,
+                                lengths=(5, 40, 0, 16)),
+    "fp32_k64v128_t70": W.custom(B=2, T=70, H=1, HV=1, K=64, V=128, dtype="fp32"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    w = SMALL[name]
+    inp = W.make_inputs(w, seed=0)
+    o, fin = gpu_run(inp)
+    o_ref, f_ref = oracle_run(inp)
+    check_all(inp, o, fin, o_ref, f_ref, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_empty_sequences_carry_initial_state(io):
+    w = W.custom(B=2, T=0, H=1, HV=2, K=128, V=64, dtype=io, h0_std=1.0)
+    inp = W.make_inputs(w, seed=3)
+    o, fin = gpu_run(inp)
+    assert o.size == 0
+    assert np.array_equal(fin, inp.h0.numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("case", ["beta0", "g0"])
+def test_degenerate_gates(case):
+    w = W.custom(B=1, T=90, H=2, HV=2, K=128, V=128, h0_std=0.5)
+    kw = {"beta_override": 0.0} if case == "beta0" else {"g_override": 0.0}
+    inp = W.make_inputs(w, seed=5, **kw)
+    o, fin = gpu_run(inp)
+    o_ref, f_ref = oracle_run(inp)
+    check_all(inp, o, fin, o_ref, f_ref, TOL["bf16"])
+    if case == "beta0":   # pure decay: the state never receives a write
+        S0 = inp.h0.numpy().astype(np.float64)
+        cum = np.cumsum(W.as_f32_numpy(inp.g)[0].astype(np.float64), axis=0)[-1]
+        assert rel_l2(fin[0], np.exp(cum)[:, :, None] * S0[0]) <= 1e-3
+
+
+def test_deltanet_retrieval_property():
+    # g = 0, beta = 1 and one fixed unit key shared by all tokens with q = k: each output
+    # returns scale * v_t (the plain delta rule overwrites the memory slot every token)
+    T, K, V = 64, 128, 128
+    gen = torch.Generator().manual_seed(11)
+    kv = torch.randn(K, generator=gen)
+    kv = (kv / kv.norm()).to(torch.bfloat16)
+    kvf = kv.float()
+    kv = (kvf / kvf.norm()).to(torch.bfloat16)   # unit to bf16 precision
+    k = kv.expand(1, T, 1, K).contiguous()
+    inp = W.Inputs(W.custom(B=1, T=T, H=1, HV=1, K=K, V=V), k.clone(), k,
+                   torch.randn(1, T, 1, V, generator=gen).to(torch.bfloat16),
+                   torch.zeros(1, T, 1, K, dtype=torch.bfloat16),
+                   torch.ones(1, T, 1, dtype=torch.bfloat16), None, None, scale=0.5)
+    o, fin = gpu_run(inp, scale=0.5)
+    o_ref, f_ref = oracle_run(inp)
+    check_all(inp, o, fin, o_ref, f_ref, TOL["bf16"])
+    nk2 = float((kv.float() ** 2).sum())
+    assert rel_l2(o[0, :, 0], 0.5 * nk2 * inp.v.float().numpy()[0, :, 0]) <= 2e-2
+
+
+def test_no_final_state_and_explicit_scale():
+    w = W.custom(B=1, T=64, H=1, HV=2, K=128, V=128)
+    inp = W.make_inputs(w, seed=2)
+    o, fin = gpu_run(inp, scale=0.3, output_final_state=False)
+    assert fin is None
+    o_ref, _ = oracle_run(inp, scale=0.3)
+    assert rel_l2(o, o_ref) <= TOL["bf16"]
+
+
+def test_deterministic_and_repeatable():
+    w = W.custom(B=1, T=300, H=2, HV=2, K=128, V=128, h0_std=0.1)
+    inp = W.make_inputs(w, seed=4)
+    plan = gpu_plan(inp)
+    o1, f1 = [x.clone() for x in plan()]
+    o2, f2 = plan()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_prepare_workspace_matches_chunk_oracle():
+    # stage-1 diagnostics: decode w, qd, kr, u, Mqk, exp(gam) of sampled chunks (including a
+    # tail chunk) and compare with the fp64 chunked-form intermediates
+    w = W.custom(B=1, T=37, H=1, HV=2, K=128, V=128)
+    inp = W.make_inputs(w, seed=6)
+    plan = gpu_plan(inp)
+    plan()
+    torch.cuda.synchronize()
+    ws = plan.workspace.cpu().numpy()
+    cb = chunk_bytes(128, 128)
+    n_slots = 37 // 16 + 1
+    f = W.as_f32_numpy
+    for j in range(2):
+        prep = chunk_prepare(f(inp.q)[0, :, 0], f(inp.k)[0, :, 0], f(inp.v)[0, :, j],
+                             f(inp.g)[0, :, j], f(inp.beta)[0, :, j], inp.scale, 16)
+        for c in range(3):
+            off = (j * n_slots + c) * cb
+            got = decode_chunk(ws[off:off + cb], 128, 128)
+            for key in ("w", "qd", "kr", "u", "Mqk", "eg"):
+                ref = prep[key][c]
+                err = rel_l2(got[key], ref)
+                assert err <= 1e-2, f"head {j} chunk {c} {key}: rel L2 {err:.2e}"
+
+
+FULL = {
+    "h16_t4096": None,          # every unit
+    "varlen8_h32": 6,
+    "gva_b4_t8192": 6,
+    "long_t131072": 3,
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_parity(name):
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, seed=0)
+    o, fin = gpu_run(inp)
+    assert np.isfinite(o).all() and np.isfinite(fin).all()
+    nsamp = FULL[name]
+    units = None if nsamp is None else W.sample_units(inp.N, w.HV, nsamp, seed=1)
+    o_ref, f_ref = oracle_run(inp, units=units)
+    if units is None:
+        check_all(inp, o, fin, o_ref, f_ref, TOL[w.dtype])
+        return
+    of, orf = o_flat(o, inp), o_flat(o_ref, inp)
+    bounds = inp.seq_bounds()
+    got_o, ref_o, got_f, ref_f = [], [], [], []
+    for (s, j) in units:
+        a, b = bounds[s]
+        got_o.append(of[a:b, j]); ref_o.append(orf[a:b, j])
+        got_f.append(fin[s, j]); ref_f.append(f_ref[s, j])
+    eo = rel_l2(np.concatenate(got_o), np.concatenate(ref_o))
+    ef = rel_l2(np.stack(got_f), np.stack(ref_f))
+    assert eo <= TOL[w.dtype] and ef <= TOL[w.dtype], f"rel L2 o={eo:.3e} final={ef:.3e}"

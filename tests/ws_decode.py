@@ -1,0 +1,57 @@
+"""Decode the bf16-io workspace of libkda_fwd back into natural-order arrays (test helper).
+
+The layout is the one documented in include/kda_fwd.h's companion source (kda_internal.h,
+WsBf16): per (value head, slot) chunk, fp16 fragments in the state kernel's lane order. This is
+host-side test logic only; it does no KDA arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def chunk_bytes(K, V):
+    end = 32 * K * 3 + 32 * V + 512 + 4 * K
+    return (end + 255) // 256 * 256
+
+
+def decode_chunk(raw: np.ndarray, K: int, V: int):
+    """raw: uint8 bytes of one chunk. Returns dict of float64 arrays w [16,K], qd [16,K],
+    kr [16,K], u [16,V], Mqk [16,16], eg [K]."""
+    off = 0
+    h16 = lambda a, b: raw[a:b].view(np.float16).astype(np.float64)
+    NS, NV = K // 32, V // 16
+    lanes = np.arange(64)
+    g, m = lanes // 16, lanes % 16
+    out = {}
+    for name in ("w", "qd"):
+        frag = h16(off, off + 32 * K).reshape(NS, 64, 8)
+        X = np.full((16, K), np.nan)
+        for s in range(NS):
+            for e in range(8):
+                kd = 16 * (2 * s + e // 4) + 4 * g + e % 4
+                X[m, kd] = frag[s, :, e]
+        out[name] = X
+        off += 32 * K
+    frag = h16(off, off + 32 * K).reshape(NS, 64, 8)
+    X = np.full((16, K), np.nan)
+    for s in range(NS):
+        for e in range(8):
+            c, i = 2 * s + e // 4, e % 4
+            X[4 * g + i, 16 * c + m] = frag[s, :, e]
+    out["kr"] = X
+    off += 32 * K
+    frag = h16(off, off + 32 * V).reshape(NV, 64, 4)
+    X = np.full((16, V), np.nan)
+    for c in range(NV):
+        for i in range(4):
+            X[4 * g + i, 16 * c + m] = frag[c, :, i]
+    out["u"] = X
+    off += 32 * V
+    frag = h16(off, off + 512).reshape(64, 4)
+    X = np.full((16, 16), np.nan)
+    for i in range(4):
+        X[m, 4 * g + i] = frag[:, i]
+    out["Mqk"] = X
+    off += 512
+    out["eg"] = raw[off:off + 4 * K].view(np.float32).astype(np.float64)
+    return out
