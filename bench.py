@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked KDA forward on one MI355X (prints one JSON line).
+
+A step is one full forward (prepare kernel + state kernel, i.e. kda_fwd) over one synthetic
+batch already resident in HBM. Default workload: B=1, T=4096, H=HV=16, K=V=128, bf16 io
+("h16_t4096"). The timed region is exactly --steps back-to-back steps bracketed by
+torch.cuda.synchronize(); inside it every kernel launch is bracketed by HIP events on the stream
+it runs on, which gives each kernel's average duration for the roofline figures.
+
+Extra fields beyond the driver contract:
+  roofline        dominant kernel: achieved algorithmic throughput / MI355X peak
+  roofline_path   the whole forward against the HBM roof (algorithmic bytes / step time)
+  kernels         per-kernel average durations and algorithmic work
+  cold_cache      per-step time when a 1 GiB copy evicts the caches between steps
+  cpu_baseline    the fp64 C oracle on the host cores over a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd tokens/s (all heads) @H=16,T=4096,K=V=128 bf16; HBM GB/s, MFMA %"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense; fp16 == bf16
+CHUNK = 16
+
+
+def algorithmic_work(inp):
+    """Algorithmic bytes and FLOPs of one forward, split by the kernel that must do them.
+
+    Bytes (what the method must move): the prepare kernel reads q, k (once per q/k head), v, g,
+    beta; the state kernel writes o and reads/writes the per-(sequence, value head) states.
+    FLOPs per 16-token chunk of one value head (multiply-add = 2): state kernel
+    6 C K V + 2 C^2 V + K V; prepare kernel L + Mqk + w + u (2 C^2 K + 2 C^2 K + 2 C^2 K + 2 C^2 V)
+    plus the Neumann product (6 products of 16 x 16 x 16).
+    """
+    w = inp.w
+    es = 2 if w.dtype == "bf16" else 4
+    T_total = inp.T_total
+    H, HV, K, V = w.H, w.HV, w.K, w.V
+    N = inp.N
+    n_chunk_heads = sum((b - a + CHUNK - 1) // CHUNK for a, b in inp.seq_bounds()) * HV
+    prep_bytes = T_total * (H * 2 * K * es + HV * (V * es + K * es + es))
+    state_bytes = T_total * HV * V * es + N * HV * K * V * 4 * (1 + (inp.h0 is not None))
+    state_flops = n_chunk_heads * (6 * CHUNK * K * V + 2 * CHUNK * CHUNK * V + K * V)
+    prep_flops = n_chunk_heads * (2 * CHUNK * CHUNK * (3 * K + V) + 6 * 2 * CHUNK ** 3)
+    return dict(prep_bytes=prep_bytes, state_bytes=state_bytes, prep_flops=prep_flops,
+                state_flops=state_flops, n_chunk_heads=n_chunk_heads)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "chunked_kimi_delta_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
+    missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, min_seconds: float):
+    """The fp64 C oracle (unchanged) on the host cores: the whole workload, repeated until at
+    least `min_seconds` of wall time have passed (bounded at 40 repetitions)."""
+    import workloads as W
+    from oracle.native import kda_oracle_c
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))        # a one-GPU machine's CPU share
+    f = W.as_f32_numpy
+    args = [f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta)]
+    h0 = None if inp.h0 is None else inp.h0.numpy()
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        kda_oracle_c(*args, inp.scale, h0, cu, n_threads=cores, want_o=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 40:
+            break
+    return {"value": round(reps * inp.T_total / el, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"full {inp.w.name} forward (all {inp.w.HV} heads, fp64 C recurrence), "
+                      f"repeated {reps}x in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="h16_t4096")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed with a cache-evicting copy between them (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the oracle CPU baseline (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy first (a counter calibration kernel)")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import chunked_kimi_delta_amd as kda
+
+    w = W.WORKLOADS[a.workload]
+    inp = W.make_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    d = lambda x: None if x is None else x.to(dev).contiguous()
+    plan = kda.KdaFwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta),
+                          cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0))
+    stream = torch.cuda.current_stream(dev)
+
+    if a.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        plan.prepare(stream)
+        plan.state(stream)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        plan.prepare(stream)
+        ev[i][1].record(stream)
+        plan.state(stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    prep_ms = statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps))
+    state_ms = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps))
+
+    cold = None
+    if a.cold_steps > 0:
+        fa = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fb = torch.empty_like(fa)
+        cs = []
+        for _ in range(a.cold_steps):
+            fb.copy_(fa)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            plan(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cs.append(e0.elapsed_time(e1))
+        cold_ms = statistics.median(cs)
+        cold = {"ms_per_step_median": round(cold_ms, 5),
+                "tokens_per_s": round(inp.T_total / (cold_ms * 1e-3), 1),
+                "steps": a.cold_steps,
+                "note": "1 GiB device copy between steps evicts L2 and the 256 MB MALL; "
+                        "each step timed alone with HIP events"}
+        del fa, fb
+
+    work = algorithmic_work(inp)
+    es = "bf16" if w.dtype == "bf16" else "fp32"
+    kernels = {
+        "kda_prepare": {"avg_ms": round(prep_ms, 5), "bound": "hbm",
+                        "alg_bytes": work["prep_bytes"], "alg_flops": work["prep_flops"],
+                        "achieved_GBs": round(work["prep_bytes"] / (prep_ms * 1e-3) / 1e9, 1)},
+        "kda_state": {"avg_ms": round(state_ms, 5), "bound": "mfma",
+                      "alg_bytes": work["state_bytes"], "alg_flops": work["state_flops"],
+                      "achieved_TFLOPs": round(work["state_flops"] / (state_ms * 1e-3) / 1e12, 2)},
+    }
+    if state_ms >= prep_ms:
+        ach = work["state_flops"] / (state_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[es]
+        roof = {"kernel": "kda_state", "bound": "mfma", "achieved": round(ach, 3),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 5),
+                "traffic": committed_traffic("kda_state", w.name)}
+    else:
+        ach = work["prep_bytes"] / (prep_ms * 1e-3) / 1e9
+        roof = {"kernel": "kda_prepare", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 5),
+                "traffic": committed_traffic("kda_prepare", w.name)}
+    path_bytes = work["prep_bytes"] + work["state_bytes"]
+    path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
+    roof_path = {"bound": "hbm", "achieved": round(path_gbs, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 5),
+                 "alg_bytes_per_step": path_bytes}
+
+    cpu = None
+    if a.cpu_seconds > 0:
+        cpu = cpu_baseline(inp, a.cpu_seconds)
+
+    value = inp.T_total / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
+                   "K": w.K, "V": w.V, "chunk": CHUNK, "tokens_per_step": inp.T_total,
+                   "parallelism": "single-gpu",
+                   "arithmetic": "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse"},
+        "roofline": roof, "roofline_path": roof_path, "kernels": kernels,
+        "cold_cache": cold, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,10 @@ def load():
     lib.kda_fwd.argtypes = [ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p, ctypes.c_size_t,
                             ctypes.c_void_p]
     lib.kda_fwd.restype = ctypes.c_int
+    for name in ("kda_fwd_prepare", "kda_fwd_state"):
+        f = getattr(lib, name)
+        f.argtypes = lib.kda_fwd.argtypes
+        f.restype = ctypes.c_int
     lib.kda_strerror.argtypes = [ctypes.c_int]
     lib.kda_strerror.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []

@@ -88,14 +88,26 @@ class KdaFwdPlan:
         self.ws_bytes = workspace.numel()
         self.device = dev
 
-    def __call__(self, stream=None):
-        """Enqueue the forward on `stream` (default: torch's current stream)."""
+    def _run(self, fn, name, stream):
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        st = self.lib.kda_fwd(ctypes.byref(self.args), ctypes.c_void_p(self.workspace.data_ptr()),
-                              self.ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+        st = fn(ctypes.byref(self.args), ctypes.c_void_p(self.workspace.data_ptr()),
+                self.ws_bytes, ctypes.c_void_p(stream.cuda_stream))
         if st != 0:
-            raise RuntimeError(f"kda_fwd failed: {strerror(st)} ({st})")
+            raise RuntimeError(f"{name} failed: {strerror(st)} ({st})")
+
+    def __call__(self, stream=None):
+        """Enqueue the forward on `stream` (default: torch's current stream)."""
+        self._run(self.lib.kda_fwd, "kda_fwd", stream)
+        return self.o, self.final_state
+
+    def prepare(self, stream=None):
+        """Enqueue only the prepare kernel (kda_fwd_prepare)."""
+        self._run(self.lib.kda_fwd_prepare, "kda_fwd_prepare", stream)
+
+    def state(self, stream=None):
+        """Enqueue only the state kernel (kda_fwd_state); returns (o, final_state)."""
+        self._run(self.lib.kda_fwd_state, "kda_fwd_state", stream)
         return self.o, self.final_state
 
 

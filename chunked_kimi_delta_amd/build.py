@@ -16,8 +16,12 @@ ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for every device compile (the device pass honours the
 # feature; the host pass prints a harmless "not a recognized feature" warning).
+# MFMA accumulators are formed in ordinary VGPRs: the kernels read and rescale their
+# accumulators with VALU every chunk, and accumulators in AGPRs would cost a v_accvgpr copy
+# each way.
 HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                "-I", os.path.join(ROOT, "include")]
 
 

@@ -49,31 +49,23 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     return KDA_OK;
 }
 
+enum Stage { STAGE_PREPARE = 1, STAGE_STATE = 2, STAGE_BOTH = 3 };
+
 template <int K, int V>
-hipError_t dispatch(const FwdParams &p, int io, hipStream_t st)
+hipError_t dispatch(const FwdParams &p, int io, int stages, hipStream_t st)
 {
     hipError_t e;
+    const bool prep = (stages & STAGE_PREPARE) && p.seq.T_total > 0;
     if (io == KDA_BF16) {
-        if (p.seq.T_total > 0 && (e = launch_prepare_bf16<K, V>(p, st)) != hipSuccess) return e;
-        return launch_state_bf16<K, V>(p, st);
+        if (prep && (e = launch_prepare_bf16<K, V>(p, st)) != hipSuccess) return e;
+        return (stages & STAGE_STATE) ? launch_state_bf16<K, V>(p, st) : hipSuccess;
     }
-    if (p.seq.T_total > 0 && (e = launch_prepare_f32<K, V>(p, st)) != hipSuccess) return e;
-    return launch_state_f32<K, V>(p, st);
+    if (prep && (e = launch_prepare_f32<K, V>(p, st)) != hipSuccess) return e;
+    return (stages & STAGE_STATE) ? launch_state_f32<K, V>(p, st) : hipSuccess;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t kda_fwd_workspace_bytes(const kda_fwd_args *a)
-{
-    int64_t tt, ns;
-    size_t cb;
-    if (check_shapes(a, &tt, &ns, &cb) != KDA_OK) return 0;
-    return (size_t)ns * (size_t)a->HV * cb;
-}
-
-kda_status kda_fwd(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void *stream)
+kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void *stream,
+                      int stages)
 {
     int64_t tt, ns;
     size_t cb;
@@ -115,10 +107,40 @@ kda_status kda_fwd(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (a->K == 64)
-        e = a->V == 64 ? dispatch<64, 64>(p, a->io, s) : dispatch<64, 128>(p, a->io, s);
+        e = a->V == 64 ? dispatch<64, 64>(p, a->io, stages, s)
+                       : dispatch<64, 128>(p, a->io, stages, s);
     else
-        e = a->V == 64 ? dispatch<128, 64>(p, a->io, s) : dispatch<128, 128>(p, a->io, s);
+        e = a->V == 64 ? dispatch<128, 64>(p, a->io, stages, s)
+                       : dispatch<128, 128>(p, a->io, stages, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_fwd_workspace_bytes(const kda_fwd_args *a)
+{
+    int64_t tt, ns;
+    size_t cb;
+    if (check_shapes(a, &tt, &ns, &cb) != KDA_OK) return 0;
+    return (size_t)ns * (size_t)a->HV * cb;
+}
+
+kda_status kda_fwd(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void *stream)
+{
+    return run_stages(a, workspace, ws_bytes, stream, STAGE_BOTH);
+}
+
+kda_status kda_fwd_prepare(const kda_fwd_args *a, void *workspace, size_t ws_bytes,
+                           void *stream)
+{
+    return run_stages(a, workspace, ws_bytes, stream, STAGE_PREPARE);
+}
+
+kda_status kda_fwd_state(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void *stream)
+{
+    return run_stages(a, workspace, ws_bytes, stream, STAGE_STATE);
 }
 
 const char *kda_strerror(int status)

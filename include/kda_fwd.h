@@ -90,6 +90,17 @@ size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
    launches were enqueued. */
 kda_status kda_fwd(const kda_fwd_args *args, void *workspace, size_t ws_bytes, void *stream);
 
+/* The two stages of kda_fwd as separate launches, for callers that schedule or time them
+   individually. kda_fwd_prepare enqueues the token-parallel prepare kernel, which writes the
+   per-chunk quantities of every (chunk, value head) into `workspace`; kda_fwd_state enqueues
+   the chunk-sequential state kernel, which reads them and writes o and final_state. Running
+   kda_fwd_prepare then kda_fwd_state on one stream with the same arguments and workspace is
+   exactly kda_fwd. Same arguments, checks and status codes as kda_fwd. */
+kda_status kda_fwd_prepare(const kda_fwd_args *args, void *workspace, size_t ws_bytes,
+                           void *stream);
+kda_status kda_fwd_state(const kda_fwd_args *args, void *workspace, size_t ws_bytes,
+                         void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_strerror(int status);
 

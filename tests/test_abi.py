@@ -34,8 +34,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["kda_fwd", "kda_fwd_workspace_bytes", "kda_strerror",
-                                    "kda_version"]
+    assert declared_functions() == ["kda_fwd", "kda_fwd_prepare", "kda_fwd_state",
+                                    "kda_fwd_workspace_bytes", "kda_strerror", "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -76,7 +76,8 @@ def test_workspace_bytes(lib):
 ])
 def test_kda_fwd_rejects_bad_arguments(lib, kw, status):
     a = args(**kw)
-    assert lib.kda_fwd(ctypes.byref(a), None, 0, None) == status
+    for fn in (lib.kda_fwd, lib.kda_fwd_prepare, lib.kda_fwd_state):
+        assert fn(ctypes.byref(a), None, 0, None) == status
 
 
 def test_kda_fwd_checks_alignment_and_workspace(lib):
