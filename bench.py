@@ -69,7 +69,7 @@ def source_digest() -> str:
 def committed_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
     missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -79,9 +79,54 @@ def committed_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def summarize_trace(d: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run (run_kernel_stats.csv)."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    out = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+           "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    out += ["", f"kernel sources digest: `{source_digest()}`", ""]
+    return "\n".join(out)
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: str) -> dict:
+    """Per-launch HBM bytes of each libkda_fwd kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+    for the 256 MiB device copy (__amd_rocclr_copyBuffer) that `--copy-calibration` runs."""
+    import csv
+    copy_bytes = 256 << 20
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        vals = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024)
+        copy = [v for k, v in vals.items() if "copyBuffer" in k]
+        if not copy:
+            raise SystemExit(f"no calibration copy kernel in {d}")
+        scale = copy_bytes / statistics.mean(copy[0])
+        for k, v in vals.items():
+            for short in ("prepare", "state"):
+                if f"kda::{short}_" in k:
+                    e = res.setdefault(f"kda_{short}", {})
+                    e[counter.lower() + "_raw_bytes"] = statistics.mean(v)
+                    e[counter.lower() + "_scale"] = round(scale, 4)
+                    e[counter.lower() + "_bytes"] = statistics.mean(v) * scale
+    for k, e in res.items():
+        e["hbm_bytes_per_launch"] = e["fetch_size_bytes"] + e["write_size_bytes"]
+        e.update(kernel=k, workload=workload, source_digest=source_digest(), command=command)
+    return res
+
+
 def cpu_baseline(inp, min_seconds: float):
     """The fp64 C oracle (unchanged) on the host cores: the whole workload, repeated until at
-    least `min_seconds` of wall time have passed (bounded at 40 repetitions)."""
+    least `min_seconds` of wall time have passed (bounded at 1000 repetitions)."""
     import workloads as W
     from oracle.native import kda_oracle_c
     try:
@@ -98,7 +143,7 @@ def cpu_baseline(inp, min_seconds: float):
         kda_oracle_c(*args, inp.scale, h0, cu, n_threads=cores, want_o=True)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or reps >= 40:
+        if el >= min_seconds or reps >= 1000:
             break
     return {"value": round(reps * inp.T_total / el, 2), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
@@ -118,7 +163,26 @@ def main():
                     help="minimum wall time of the oracle CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (a counter calibration kernel)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --stats output dir and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<kernel>_<workload>.txt from two --pmc runs")
+    ap.add_argument("--command", default="", help="the profiling command, for the summaries")
     a = ap.parse_args()
+
+    if a.summarize_trace:
+        print(summarize_trace(a.summarize_trace, a.command))
+        return
+    if a.summarize_traffic:
+        res = summarize_traffic(a.summarize_traffic[0], a.summarize_traffic[1], a.workload,
+                                a.command)
+        for k, e in res.items():
+            path = os.path.join(ROOT, "profiles", f"traffic_{k}_{a.workload}.txt")
+            with open(path, "w") as f:
+                json.dump(e, f, indent=1)
+                f.write("\n")
+            print(path, json.dumps(e))
+        return
 
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "

@@ -8,7 +8,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/kda_fwd.h"
+#include "kda_fwd.h"
 #include "kda_internal.h"
 
 namespace {

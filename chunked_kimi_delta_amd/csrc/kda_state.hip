@@ -122,6 +122,12 @@ __device__ __forceinline__ void chain_step(ChainFrag<K, V> &f, const ChunkPtr<K,
         Sh[st] = cat(to_f16x4(S[2 * st]), to_f16x4(S[2 * st + 1]));
         ho.sh[par][st][lane] = Sh[st];
     }
+    // decay in place now: S is needed only as the update's accumulator from here on, and the
+    // multiplies overlap the w S products instead of delaying the update
+#pragma unroll
+    for (int t = 0; t < NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
     f32x4 X0 = zero4(), X1 = zero4();
 #pragma unroll
     for (int st = 0; st < NS; st += 2) {
@@ -139,8 +145,6 @@ __device__ __forceinline__ void chain_step(ChainFrag<K, V> &f, const ChunkPtr<K,
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
         const f16x8 &kp = f.kr[t >> 1];
         const f16x4 ka = (t & 1) ? __builtin_shufflevector(kp, kp, 4, 5, 6, 7)
                                  : __builtin_shufflevector(kp, kp, 0, 1, 2, 3);
