@@ -31,28 +31,31 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA fwd tokens/s (all heads) @H=16,T=4096,K=V=128 bf16; HBM GB/s, MFMA %"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense; fp16 == bf16
-CHUNK = 16
 
 
-def algorithmic_work(inp):
-    """Algorithmic bytes and FLOPs of one forward, split by the kernel that must do them.
+def algorithmic_work(inp, C):
+    """Algorithmic bytes and FLOPs of one forward with chunks of C tokens, split by the kernel
+    that must do them.
 
     Bytes (what the method must move): the prepare kernel reads q, k (once per q/k head), v, g,
     beta; the state kernel writes o and reads/writes the per-(sequence, value head) states.
-    FLOPs per 16-token chunk of one value head (multiply-add = 2): state kernel
-    6 C K V + 2 C^2 V + K V; prepare kernel L + Mqk + w + u (2 C^2 K + 2 C^2 K + 2 C^2 K + 2 C^2 V)
-    plus the Neumann product (6 products of 16 x 16 x 16).
+    FLOPs per C-token chunk of one value head (multiply-add = 2): state kernel
+    6 C K V + 2 C^2 V + K V (w S, qd S, kr^T delta, Mqk delta, decay); prepare kernel
+    L + Mqk + w + u (2 C^2 K + 2 C^2 K + 2 C^2 K + 2 C^2 V) plus the inverse (the Neumann
+    product of each 16 x 16 diagonal block, 6 products of 16 x 16 x 16, and for C = 32 the
+    block substitution, 2 more).
     """
     w = inp.w
     es = 2 if w.dtype == "bf16" else 4
     T_total = inp.T_total
     H, HV, K, V = w.H, w.HV, w.K, w.V
     N = inp.N
-    n_chunk_heads = sum((b - a + CHUNK - 1) // CHUNK for a, b in inp.seq_bounds()) * HV
+    n_chunk_heads = sum((b - a + C - 1) // C for a, b in inp.seq_bounds()) * HV
     prep_bytes = T_total * (H * 2 * K * es + HV * (V * es + K * es + es))
     state_bytes = T_total * HV * V * es + N * HV * K * V * 4 * (1 + (inp.h0 is not None))
-    state_flops = n_chunk_heads * (6 * CHUNK * K * V + 2 * CHUNK * CHUNK * V + K * V)
-    prep_flops = n_chunk_heads * (2 * CHUNK * CHUNK * (3 * K + V) + 6 * 2 * CHUNK ** 3)
+    state_flops = n_chunk_heads * (6 * C * K * V + 2 * C * C * V + K * V)
+    inv_flops = (C // 16) * 6 * 2 * 16 ** 3 + (C // 16 - 1) * 2 * 2 * 16 ** 3
+    prep_flops = n_chunk_heads * (2 * C * C * (3 * K + V) + inv_flops)
     return dict(prep_bytes=prep_bytes, state_bytes=state_bytes, prep_flops=prep_flops,
                 state_flops=state_flops, n_chunk_heads=n_chunk_heads)
 
@@ -157,6 +160,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h16_t4096")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="tokens per serial state step (16, 32; 0 = library default)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed with a cache-evicting copy between them (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -198,7 +203,8 @@ def main():
     dev = torch.device("cuda:0")
     d = lambda x: None if x is None else x.to(dev).contiguous()
     plan = kda.KdaFwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta),
-                          cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0))
+                          cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0), chunk=a.chunk)
+    chunk = a.chunk or (32 if w.dtype == "bf16" else 16)
     stream = torch.cuda.current_stream(dev)
 
     if a.copy_calibration:
@@ -249,7 +255,7 @@ def main():
                         "each step timed alone with HIP events"}
         del fa, fb
 
-    work = algorithmic_work(inp)
+    work = algorithmic_work(inp, chunk)
     es = "bf16" if w.dtype == "bf16" else "fp32"
     kernels = {
         "kda_prepare": {"avg_ms": round(prep_ms, 5), "bound": "hbm",
@@ -287,7 +293,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
-                   "K": w.K, "V": w.V, "chunk": CHUNK, "tokens_per_step": inp.T_total,
+                   "K": w.K, "V": w.V, "chunk": chunk, "tokens_per_step": inp.T_total,
                    "parallelism": "single-gpu",
                    "arithmetic": "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse"},
         "roofline": roof, "roofline_path": roof_path, "kernels": kernels,

@@ -22,6 +22,7 @@ class KdaFwdArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("cu_seqlens", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("chunk", ctypes.c_int32),
     ]
 
 

@@ -36,7 +36,7 @@ class KdaFwdPlan:
     """
 
     def __init__(self, q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
-                 output_final_state=True, workspace=None, o=None, final_state=None):
+                 output_final_state=True, workspace=None, o=None, final_state=None, chunk=0):
         self.lib = load()
         if q.dtype not in _IO:
             raise TypeError(f"unsupported io dtype {q.dtype} (bf16 or fp32)")
@@ -75,11 +75,13 @@ class KdaFwdPlan:
         a.initial_state = _ptr(initial_state)
         a.o = _ptr(self.o)
         a.final_state = _ptr(self.final_state)
+        a.chunk = int(chunk)
         self.args = a
         self._keep = (q, k, v, g, beta, cu_seqlens, initial_state)
         need = int(self.lib.kda_fwd_workspace_bytes(ctypes.byref(a)))
         if need == 0 and B * T > 0:
-            raise ValueError("unsupported shapes (K and V must be 64 or 128; HV % H == 0)")
+            raise ValueError("unsupported shapes or chunk (K, V in {64, 128}; HV % H == 0; "
+                             "chunk 16, or 32 with bf16 io)")
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         elif workspace.numel() < need:
@@ -112,15 +114,16 @@ class KdaFwdPlan:
 
 
 def kda_fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
-            output_final_state=True, workspace=None):
+            output_final_state=True, workspace=None, chunk=0):
     """KDA forward. Returns (o, final_state or None); see KdaFwdPlan for shapes."""
     plan = KdaFwdPlan(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_final_state,
-                      workspace)
+                      workspace, chunk=chunk)
     return plan()
 
 
-def workspace_bytes(B, T, N, H, HV, K, V, io=KDA_BF16) -> int:
+def workspace_bytes(B, T, N, H, HV, K, V, io=KDA_BF16, chunk=0) -> int:
     """Workspace bytes kda_fwd needs for these shapes (0 if unsupported)."""
     a = KdaFwdArgs()
     a.B, a.T, a.N, a.H, a.HV, a.K, a.V, a.io = B, T, N, H, HV, K, V, io
+    a.chunk = chunk
     return int(load().kda_fwd_workspace_bytes(ctypes.byref(a)))

@@ -17,9 +17,16 @@ using namespace kda;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+template <template <int, int> class WS>
+size_t record_bytes(int K, int V)
+{
+    return K == 64 ? (V == 64 ? WS<64, 64>::BYTES : WS<64, 128>::BYTES)
+                   : (V == 64 ? WS<128, 64>::BYTES : WS<128, 128>::BYTES);
+}
+
 // Returns KDA_OK and fills the derived sizes, or the status kda_fwd must return.
 kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots,
-                        size_t *chunk_bytes)
+                        size_t *chunk_bytes, int *chunk)
 {
     if (!a) return KDA_ERR_INVALID_ARG;
     if (a->B < 1 || a->T < 0 || a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H)
@@ -32,30 +39,35 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     const bool k_ok = a->K == 64 || a->K == 128, v_ok = a->V == 64 || a->V == 128;
     if (!k_ok || !v_ok) return KDA_ERR_UNSUPPORTED;
     if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_UNSUPPORTED;
+    int ct = a->chunk;
+    if (ct == 0) ct = a->io == KDA_BF16 ? 32 : 16;
+    if (ct != 16 && !(ct == 32 && a->io == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
     const int64_t tt = (int64_t)a->B * a->T;
-    const int64_t ns = tt / CHUNK + a->N;
+    const int64_t ns = tt / ct + a->N;
     if (ns > INT32_MAX || (int64_t)a->HV > 65535) return KDA_ERR_UNSUPPORTED;
     size_t cb;
-    if (a->io == KDA_BF16) {
-        cb = a->K == 64 ? (a->V == 64 ? WsBf16<64, 64>::BYTES : WsBf16<64, 128>::BYTES)
-                        : (a->V == 64 ? WsBf16<128, 64>::BYTES : WsBf16<128, 128>::BYTES);
-    } else {
-        cb = a->K == 64 ? (a->V == 64 ? WsF32<64, 64>::BYTES : WsF32<64, 128>::BYTES)
-                        : (a->V == 64 ? WsF32<128, 64>::BYTES : WsF32<128, 128>::BYTES);
-    }
+    if (a->io == KDA_BF16)
+        cb = ct == 32 ? record_bytes<WsBf16x32>(a->K, a->V) : record_bytes<WsBf16>(a->K, a->V);
+    else
+        cb = record_bytes<WsF32>(a->K, a->V);
     *T_total = tt;
     *n_slots = ns;
     *chunk_bytes = cb;
+    *chunk = ct;
     return KDA_OK;
 }
 
 enum Stage { STAGE_PREPARE = 1, STAGE_STATE = 2, STAGE_BOTH = 3 };
 
 template <int K, int V>
-hipError_t dispatch(const FwdParams &p, int io, int stages, hipStream_t st)
+hipError_t dispatch(const FwdParams &p, int io, int chunk, int stages, hipStream_t st)
 {
     hipError_t e;
     const bool prep = (stages & STAGE_PREPARE) && p.seq.T_total > 0;
+    if (io == KDA_BF16 && chunk == 32) {
+        if (prep && (e = launch_prepare32_bf16<K, V>(p, st)) != hipSuccess) return e;
+        return (stages & STAGE_STATE) ? launch_state32_bf16<K, V>(p, st) : hipSuccess;
+    }
     if (io == KDA_BF16) {
         if (prep && (e = launch_prepare_bf16<K, V>(p, st)) != hipSuccess) return e;
         return (stages & STAGE_STATE) ? launch_state_bf16<K, V>(p, st) : hipSuccess;
@@ -69,7 +81,8 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
 {
     int64_t tt, ns;
     size_t cb;
-    const kda_status st = check_shapes(a, &tt, &ns, &cb);
+    int ct;
+    const kda_status st = check_shapes(a, &tt, &ns, &cb, &ct);
     if (st != KDA_OK) return st;
     if (a->N > 0 || tt > 0) {
         const void *ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
@@ -107,11 +120,11 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (a->K == 64)
-        e = a->V == 64 ? dispatch<64, 64>(p, a->io, stages, s)
-                       : dispatch<64, 128>(p, a->io, stages, s);
+        e = a->V == 64 ? dispatch<64, 64>(p, a->io, ct, stages, s)
+                       : dispatch<64, 128>(p, a->io, ct, stages, s);
     else
-        e = a->V == 64 ? dispatch<128, 64>(p, a->io, stages, s)
-                       : dispatch<128, 128>(p, a->io, stages, s);
+        e = a->V == 64 ? dispatch<128, 64>(p, a->io, ct, stages, s)
+                       : dispatch<128, 128>(p, a->io, ct, stages, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -123,7 +136,8 @@ size_t kda_fwd_workspace_bytes(const kda_fwd_args *a)
 {
     int64_t tt, ns;
     size_t cb;
-    if (check_shapes(a, &tt, &ns, &cb) != KDA_OK) return 0;
+    int ct;
+    if (check_shapes(a, &tt, &ns, &cb, &ct) != KDA_OK) return 0;
     return (size_t)ns * (size_t)a->HV * cb;
 }
 
@@ -148,13 +162,14 @@ const char *kda_strerror(int status)
     switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_INVALID_ARG: return "invalid argument";
-    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (K and V must be 64 or 128)";
+    case KDA_ERR_UNSUPPORTED:
+        return "unsupported configuration (K, V in {64, 128}; chunk 16, or 32 with bf16 io)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
     }
 }
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 101; }
 
 }  // extern "C"

@@ -36,14 +36,15 @@ constexpr float LOG2E = 1.4426950408889634f;
 // ----------------------------------------------------------------------------- parameters
 
 // Sequence geometry shared by both kernels. Sequence s covers tokens [bos_s, eos_s) of the
-// packed token axis; its chunk c lives in workspace slot floor(bos_s / 16) + s + c. The map is
-// injective and every slot is < T_total / 16 + N (so the prepare grid is that bound).
+// packed token axis; with chunks of CT tokens its chunk c lives in workspace slot
+// floor(bos_s / CT) + s + c. The map is injective and every slot is < T_total / CT + N (so the
+// prepare grid is that bound).
 struct SeqGeom {
     const int64_t *cu;   // device [N + 1] or nullptr (dense: bos_s = s * T)
     int64_t T;           // dense per-sequence length
     int64_t T_total;     // tokens on the packed axis (B * T)
     int32_t N;           // sequences
-    int32_t n_slots;     // T_total / 16 + N
+    int32_t n_slots;     // T_total / CT + N
 };
 
 struct FwdParams {
@@ -79,6 +80,33 @@ struct WsBf16 {
     static constexpr int BYTES = (END + 255) / 256 * 256;
 };
 
+// Workspace of one (value head, slot) 32-token chunk, bf16 io. The chunk is two 16-token row
+// blocks a (tokens 0..15) and b (16..31). Products over the 32 tokens use 16x16x32 MFMAs whose
+// reduction index pairs the blocks: kappa = 8g + e is token 4g + e of block a for e < 4 and
+// token 4g + e - 4 of block b for e >= 4.
+//   W    [2 blocks][K/32][64][8] fp16   W rows of each block in TPL (as WsBf16::W)
+//   QD   [2][K/32][64][8]        fp16
+//   KR   [K/16][64][8]           fp16   KR^T tile t as a 16x16x32 A operand over the 32 tokens
+//   NU   [2][V/16][64][4]        fp32   -U rows of each block, C-layout per 16-column slice
+//                                       (negated and fp32: it is the accumulator the state
+//                                       kernel starts W S from, so delta = -(W S - U) costs no
+//                                       VALU work)
+//   MQKA [64][4]                 fp16   Mqk_aa in A16-layout
+//   MQKB [64][8]                 fp16   [Mqk_ba | Mqk_bb] as a 16x16x32 A operand
+//   EG   [K]                     fp32   exp(gamma) of the whole 32-token chunk
+template <int K, int V>
+struct WsBf16x32 {
+    static constexpr int W = 0;
+    static constexpr int QD = W + 64 * K;
+    static constexpr int KR = QD + 64 * K;
+    static constexpr int NU = KR + 64 * K;
+    static constexpr int MQKA = NU + 128 * V;
+    static constexpr int MQKB = MQKA + 512;
+    static constexpr int EG = MQKB + 1024;
+    static constexpr int END = EG + 4 * K;
+    static constexpr int BYTES = (END + 255) / 256 * 256;
+};
+
 // Workspace of one chunk, fp32 io: plain row-major fp32 arrays.
 //   W [16][K], QD [16][K], KR [16][K], U [16][V], MQK [16][16], EG [K]
 template <int K, int V>
@@ -109,31 +137,33 @@ __device__ __forceinline__ int64_t seq_eos(const SeqGeom &sg, int s, int64_t bos
     return clamp64(e, bos, sg.T_total);
 }
 
+template <int CT = CHUNK>
 __device__ __forceinline__ int64_t slot_base(const SeqGeom &sg, int s) {
-    return seq_bos(sg, s) / CHUNK + s;
+    return seq_bos(sg, s) / CT + s;
 }
 
-// Slot -> (sequence, chunk start, valid rows). Binary search for the last sequence whose
-// first slot is <= slot (the first-slot map is nondecreasing for valid offsets; for invalid
-// ones the search still ends inside [0, N)). Returns false for slots that hold no chunk.
-// Every lane computes the same values (uniform addresses).
+// Slot -> (sequence, chunk start, valid rows) for chunks of CT tokens. Binary search for the
+// last sequence whose first slot is <= slot (the first-slot map is nondecreasing for valid
+// offsets; for invalid ones the search still ends inside [0, N)). Returns false for slots that
+// hold no chunk. Every lane computes the same values (uniform addresses).
+template <int CT = CHUNK>
 __device__ __forceinline__ bool locate_slot(const SeqGeom &sg, int slot, int *s_out,
                                             int64_t *bos_out, int *nvalid_out) {
     if (sg.N <= 0) return false;
     int lo = 0, hi = sg.N - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (slot_base(sg, mid) <= slot) lo = mid; else hi = mid - 1;
+        if (slot_base<CT>(sg, mid) <= slot) lo = mid; else hi = mid - 1;
     }
     const int64_t bos_s = seq_bos(sg, lo);
     const int64_t eos_s = seq_eos(sg, lo, bos_s);
-    const int64_t c = (int64_t)slot - (bos_s / CHUNK + lo);
-    const int64_t nc = (eos_s - bos_s + CHUNK - 1) / CHUNK;
+    const int64_t c = (int64_t)slot - (bos_s / CT + lo);
+    const int64_t nc = (eos_s - bos_s + CT - 1) / CT;
     if (c < 0 || c >= nc) return false;
     *s_out = lo;
-    *bos_out = bos_s + CHUNK * c;
+    *bos_out = bos_s + CT * c;
     const int64_t nv = eos_s - *bos_out;
-    *nvalid_out = (int)(nv < CHUNK ? nv : CHUNK);
+    *nvalid_out = (int)(nv < CT ? nv : CT);
     return true;
 }
 
@@ -197,6 +227,20 @@ __device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Vector loads through a buffer resource: the address is resource base (scalar) + soffset
+// (scalar) + voffset (per lane), so per-chunk address arithmetic stays on the scalar unit.
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+
 // 16x16x16 product on the fp32 matrix core: D = A B + C with A in A16-layout and B in
 // B16-layout (fp32, one value per i), as four v_mfma_f32_16x16x4_f32. Instruction i contracts
 // the columns 4g + i of A with the rows 4g + i of B (its k index is the lane group g), so the
@@ -234,4 +278,6 @@ template <int K, int V> hipError_t launch_prepare_bf16(const FwdParams &p, hipSt
 template <int K, int V> hipError_t launch_state_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state_f32(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st);
 }  // namespace kda

@@ -1,0 +1,317 @@
+// kda_prepare32.hip -- stage 1 with 32-token chunks: everything that depends only on one
+// 32-token chunk of one value head, so that the state kernel takes one serial step per 32
+// tokens ("手撕KDA" section 1 chunks at 64 by default; the FlashKDA kernel of
+// "KDA源码剖析之FlashKDA（上）" uses 16-token tiles and a 16x16 Neumann inverse).
+//
+// The chunk is two 16-token row blocks a (tokens 0..15) and b (16..31), one wave each. With
+// Gam the cumsum of g from the chunk start and gam its value at the last token,
+//     L   = beta_row * strict_tril(k e^{Gam} . (k e^{-Gam})^T)    (32 x 32, block lower
+//           triangular: L_aa, L_bb strictly lower, L_ba full, L_ab = 0)
+//     X   = (I + L)^{-1} = [[X_aa, 0], [X_ba, X_bb]],  X_aa, X_bb by the Neumann doubling product
+//           of "KDA源码剖析之FlashKDA（上）" part 12, X_ba = -X_bb L_ba X_aa (block forward
+//           substitution; every factor stays as bounded as the inverse itself)
+//     A   = X diag(beta),  W = A (k e^{Gam}),  U = A v,  QD = scale q e^{Gam},
+//     KR  = k e^{gam - Gam},  Mqk = tril(QD' . KI'^T) (32 x 32),  e^{gam}
+// (U is stored negated in fp32, see WsBf16x32)
+// which is the chunk half of naive_chunk_kda ("手撕KDA" section 1) for a 32-token chunk.
+//
+// The per-block work is the 16-token kernel of kda_prepare.hip (same layouts, same numerics:
+// token-centred hi+lo bf16 factors, fp32 Neumann, identity-MFMA layout changes). Block b also
+// needs block a's cumsum total, its k e^{-Gam} factors, X_aa, its column-per-lane k e^{Gam} and
+// v tiles and its beta, which wave a hands over through LDS (about 19 KB).
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int K, int V>
+struct Prep32Share {
+    float tot_a[K];              // Gam (log2 units) at the last token of block a
+    float tot_ab[K];             // Gam at the last token of the chunk
+    bf16x8 kih[K / 32][64];      // block a: k e^{ref - Gam}, hi part, 16x16x32 B operand
+    bf16x8 kil[K / 32][64];      //          lo part
+    f32x4 xaa[64];               // C(X_aa)
+    bf16x4 kdc[K / 16][64];      // C(KD_a tile c): column-per-lane k e^{Gam} of block a
+    bf16x4 vc[V / 16][64];       // C(V_a tile c)
+    float beta_a[16];
+};
+
+template <int K, int V>
+__global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
+{
+    constexpr int NK = K / 16, NV = V / 16, NS = K / 32;
+    using WS = WsBf16x32<K, V>;
+    __shared__ Prep32Share<K, V> sh;
+
+    const int wave = threadIdx.x >> 6;      // row block: 0 = a, 1 = b
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4;
+    const int r = lane & 15;                 // TPL: token row in the block; C-layout: column
+    const int slot = blockIdx.x;
+    const int j = blockIdx.y;
+    const int h = j / p.G;
+
+    int s;
+    int64_t bos;
+    int nvalid;
+    if (!locate_slot<32>(p.seq, slot, &s, &bos, &nvalid)) return;   // whole workgroup
+    const int row = 16 * wave + r;
+    const bool live = row < nvalid;
+    const int64_t tok = bos + row;
+
+    // ---------------------------------------------------------------- loads (TPL)
+    float qf[NK][4], kf[NK][4], gl[NK][4];
+    uint2 vraw[NV];
+    float beta_r = 0.f;
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { qf[c][i] = 0.f; kf[c][i] = 0.f; gl[c][i] = 0.f; }
+#pragma unroll
+    for (int c = 0; c < NV; ++c) vraw[c] = make_uint2(0u, 0u);
+    if (live) {
+        const uint16_t *qp = (const uint16_t *)p.q + ((tok * p.H + h) * K + 4 * grp);
+        const uint16_t *kp = (const uint16_t *)p.k + ((tok * p.H + h) * K + 4 * grp);
+        const uint16_t *gp = (const uint16_t *)p.g + ((tok * p.HV + j) * K + 4 * grp);
+        const uint16_t *vp = (const uint16_t *)p.v + ((tok * p.HV + j) * V + 4 * grp);
+        uint2 qr[NK], kr[NK], gr[NK];
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            qr[c] = *(const uint2 *)(qp + 16 * c);
+            kr[c] = *(const uint2 *)(kp + 16 * c);
+            gr[c] = *(const uint2 *)(gp + 16 * c);
+        }
+#pragma unroll
+        for (int c = 0; c < NV; ++c) vraw[c] = *(const uint2 *)(vp + 16 * c);
+        beta_r = bf16_bits_to_f32(((const uint16_t *)p.beta)[tok * p.HV + j]);
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            unpack_bf16x4(qr[c], qf[c]);
+            unpack_bf16x4(kr[c], kf[c]);
+            unpack_bf16x4(gr[c], gl[c]);
+        }
+    }
+
+    // ---------------------------------------------------------------- cumsum over 32 tokens
+    float G2[NK][4];
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[c][i] * LOG2E);
+    if (wave == 0) {
+        if (r == 15) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sh.tot_a[16 * c + 4 * grp + i] = G2[c][i];
+        }
+        if (grp == 0) sh.beta_a[r] = beta_r;
+    }
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            const float4 t = *(const float4 *)&sh.tot_a[16 * c + 4 * grp];
+            G2[c][0] += t.x; G2[c][1] += t.y; G2[c][2] += t.z; G2[c][3] += t.w;
+        }
+        if (r == 15) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sh.tot_ab[16 * c + 4 * grp + i] = G2[c][i];
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- decay factors
+    // reference point: the cumsum at the block boundary (token 15), the middle of the chunk
+    const float sc = p.scale;
+    float KD[NK][4], QD[NK][4], KRv[NK][4];
+    bf16x8 kdh[NS], kdl[NS], kih[NS], kil[NS], qdh[NS], qdl[NS];
+#pragma unroll
+    for (int c = 0; c < NK; ++c) {
+        const float4 rf = *(const float4 *)&sh.tot_a[16 * c + 4 * grp];
+        const float4 gm = *(const float4 *)&sh.tot_ab[16 * c + 4 * grp];
+        const float ref[4] = {rf.x, rf.y, rf.z, rf.w};
+        const float gam[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float d1 = G2[c][i] - ref[i];
+            const float e1 = __builtin_amdgcn_exp2f(d1);
+            const float e2 = __builtin_amdgcn_exp2f(-d1);
+            const float eA = __builtin_amdgcn_exp2f(G2[c][i]);
+            const float eR = __builtin_amdgcn_exp2f(gam[i] - G2[c][i]);
+            const float kk = kf[c][i], qq = sc * qf[c][i];
+            KD[c][i] = kk * eA;
+            QD[c][i] = qq * eA;
+            KRv[c][i] = kk * eR;
+            const float xd = kk * e1, xi = kk * e2, xq = qq * e1;
+            const int st = c >> 1, e = (c & 1) * 4 + i;
+            const __bf16 hd = (__bf16)xd, hi_ = (__bf16)xi, hq = (__bf16)xq;
+            kdh[st][e] = hd; kdl[st][e] = (__bf16)(xd - (float)hd);
+            kih[st][e] = hi_; kil[st][e] = (__bf16)(xi - (float)hi_);
+            qdh[st][e] = hq; qdl[st][e] = (__bf16)(xq - (float)hq);
+        }
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) { sh.kih[st][lane] = kih[st]; sh.kil[st][lane] = kil[st]; }
+    }
+
+    // ---------------------------------------------------------------- diagonal blocks
+    f32x4 Lacc = zero4(), Macc = zero4();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        Lacc = mfma32(kdh[st], kih[st], Lacc);
+        Macc = mfma32(qdh[st], kih[st], Macc);
+        Lacc = mfma32(kdh[st], kil[st], Lacc);
+        Macc = mfma32(qdh[st], kil[st], Macc);
+        Lacc = mfma32(kdl[st], kih[st], Lacc);
+        Macc = mfma32(qdl[st], kih[st], Macc);
+    }
+    float b4[4], Mq[4];
+    f32x4 L, eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * grp + i;
+        b4[i] = lane_read(beta_r, rr);                   // beta of row rr of this block
+        L[i] = rr > r ? b4[i] * Lacc[i] : 0.f;
+        Mq[i] = rr >= r ? Macc[i] : 0.f;
+        eye[i] = rr == r ? 1.f : 0.f;
+    }
+    const bf16x4 Ib = to_bf16x4(eye);
+    const f16x4 Ih = to_f16x4(eye);
+
+    // Neumann product of the diagonal block on the fp32 matrix core (see kda_prepare.hip):
+    // INV = C(X^T); block a also forms C(X) for block b's off-diagonal solve
+    const f32x4 Mf = mm16_f32(L, eye, zero4());
+    const f32x4 P2 = mm16_f32(L, Mf, zero4());
+    const f32x4 Q2 = mm16_f32(Mf, L, zero4());
+    const f32x4 P4 = mm16_f32(Q2, P2, zero4());
+    const f32x4 Q4 = mm16_f32(P2, Q2, zero4());
+    const f32x4 Q8 = mm16_f32(P4, Q4, zero4());
+    f32x4 INV = eye - Mf;
+    INV = mm16_f32(Q2, INV, INV);
+    INV = mm16_f32(Q4, INV, INV);
+    INV = mm16_f32(Q8, INV, INV);
+    if (wave == 0) {
+        const f32x4 P8 = mm16_f32(Q4, P4, zero4());       // C(M^8) == A16 of L^8
+        f32x4 XN = eye - L;                                // C(I - L)
+        XN = mm16_f32(P2, XN, XN);                         // (I + L^2)(I - L)
+        XN = mm16_f32(P4, XN, XN);
+        XN = mm16_f32(P8, XN, XN);                         // C(X_aa)
+        sh.xaa[lane] = XN;
+    }
+
+    uint8_t *ws = p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES;
+
+    // column-per-lane KD and V tiles of this block (identity MFMAs)
+    bf16x4 kdC[NK], vC[NV];
+#pragma unroll
+    for (int c = 0; c < NK; ++c) kdC[c] = to_bf16x4(mfma16(to_bf16x4(KD[c]), Ib, zero4()));
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+        vC[c] = to_bf16x4(mfma16(__builtin_bit_cast(bf16x4, vraw[c]), Ib, zero4()));
+    if (wave == 0) {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) sh.kdc[c][lane] = kdC[c];
+#pragma unroll
+        for (int c = 0; c < NV; ++c) sh.vc[c][lane] = vC[c];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- W, U
+    float AT[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) AT[i] = INV[i] * b4[i];     // C(A_xx^T) = diag(beta) X_xx^T
+    const bf16x4 ATb = to_bf16x4(AT);
+    f16x4 wT[NK];
+    f32x4 uT[NV];
+    f16x4 MqbaT = to_f16x4(zero4());
+    if (wave == 0) {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) wT[c] = to_f16x4(mfma16(kdC[c], ATb, zero4()));
+#pragma unroll
+        for (int c = 0; c < NV; ++c) uT[c] = mfma16(ATb, vC[c], zero4());
+    } else {
+        // off-diagonal blocks of L and Mqk: block b rows against block a columns
+        f32x4 Lba = zero4(), Mba = zero4();
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const bf16x8 ah = sh.kih[st][lane], al = sh.kil[st][lane];
+            Lba = mfma32(kdh[st], ah, Lba);
+            Mba = mfma32(qdh[st], ah, Mba);
+            Lba = mfma32(kdh[st], al, Lba);
+            Mba = mfma32(qdh[st], al, Mba);
+            Lba = mfma32(kdl[st], ah, Lba);
+            Mba = mfma32(qdl[st], ah, Mba);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Lba[i] *= b4[i];
+        // X_ba^T = -X_aa^T L_ba^T X_bb^T
+        const f32x4 Pm = mm16_f32(Lba, INV, zero4());       // C(L_ba^T X_bb^T)
+        const f32x4 XbaT = mm16_f32(sh.xaa[lane], Pm, zero4());
+        float ABT[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ABT[i] = -XbaT[i] * sh.beta_a[4 * grp + i];
+        const bf16x4 ABTb = to_bf16x4(ABT);                  // C(A_ba^T)
+        const bf16x8 Arow = cat(ABTb, ATb);                  // [A_ba | A_bb] as A (16 x 32)
+#pragma unroll
+        for (int c = 0; c < NK; ++c)
+            wT[c] = to_f16x4(mfma32(cat(sh.kdc[c][lane], kdC[c]), Arow, zero4()));
+#pragma unroll
+        for (int c = 0; c < NV; ++c) uT[c] = mfma32(Arow, cat(sh.vc[c][lane], vC[c]), zero4());
+        MqbaT = to_f16x4(mfma16(to_f16x4(Mba), Ih, zero4()));  // C(Mqk_ba^T)
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        *(f16x8 *)(ws + WS::W + ((wave * NS + st) * 64 + lane) * 16) =
+            cat(wT[2 * st], wT[2 * st + 1]);
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+        *(f32x4 *)(ws + WS::NU + ((wave * NV + c) * 64 + lane) * 16) = -uT[c];
+
+    // ---------------------------------------------------------------- QD, KR, Mqk, e^{gam}
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        *(f16x8 *)(ws + WS::QD + ((wave * NS + st) * 64 + lane) * 16) =
+            cat(to_f16x4(QD[2 * st]), to_f16x4(QD[2 * st + 1]));
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+        *(f16x4 *)(ws + WS::KR + (c * 64 + lane) * 16 + wave * 8) =
+            to_f16x4(mfma16(to_f16x4(KRv[c]), Ih, zero4()));
+    const f16x4 MqT = to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4()));   // C(Mqk_xx^T)
+    if (wave == 0) {
+        *(f16x4 *)(ws + WS::MQKA + lane * 8) = MqT;
+    } else {
+        *(f16x8 *)(ws + WS::MQKB + lane * 16) = cat(MqbaT, MqT);
+        if (r == 15) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c) {
+                float4 e;
+                e.x = __builtin_amdgcn_exp2f(G2[c][0]);
+                e.y = __builtin_amdgcn_exp2f(G2[c][1]);
+                e.z = __builtin_amdgcn_exp2f(G2[c][2]);
+                e.w = __builtin_amdgcn_exp2f(G2[c][3]);
+                *(float4 *)(ws + WS::EG + (16 * c + 4 * grp) * 4) = e;
+            }
+        }
+    }
+}
+
+template <int K, int V>
+hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st)
+{
+    dim3 grid(p.seq.n_slots, p.HV);
+    prepare32_bf16_kernel<K, V><<<grid, dim3(128), 0, st>>>(p);
+    return hipGetLastError();
+}
+
+#define KDA_INST(K, V) \
+    template hipError_t launch_prepare32_bf16<K, V>(const FwdParams &, hipStream_t);
+KDA_INST(64, 64)
+KDA_INST(64, 128)
+KDA_INST(128, 64)
+KDA_INST(128, 128)
+#undef KDA_INST
+
+}  // namespace kda

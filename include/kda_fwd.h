@@ -38,7 +38,8 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,  /* null required pointer, bad shape, misalignment, B != 1 with
                                  cu_seqlens, N != B without cu_seqlens, HV % H != 0         */
-    KDA_ERR_UNSUPPORTED = 2,  /* K or V outside {64, 128}, unknown io dtype                  */
+    KDA_ERR_UNSUPPORTED = 2,  /* K or V outside {64, 128}, unknown io dtype, chunk not
+                                 offered for this io dtype                                   */
     KDA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than kda_fwd_workspace_bytes()    */
     KDA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)                    */
 } kda_status;
@@ -76,12 +77,18 @@ typedef struct {
     const float *initial_state; /* [N, HV, K, V] fp32, or NULL for zeros                    */
     void *o;                  /* [B, T, HV, V]  io dtype, written for every token            */
     float *final_state;       /* [N, HV, K, V] fp32, or NULL to skip                        */
+    int32_t chunk;            /* tokens per serial step of the state kernel: 16 (the FlashKDA
+                                 tile of "KDA源码剖析之FlashKDA（上）"), 32 (two 16-token blocks
+                                 joined by block forward substitution; bf16 io only), or 0 for
+                                 the default (32 for bf16 io, 16 for fp32 io). Results agree to
+                                 rounding; 32 is faster.                                     */
 } kda_fwd_args;
 
 /* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
    Returns 0 for arguments kda_fwd would reject. The workspace holds the prepare kernel's
    per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma)) for ceil-bounded chunk slots of every
-   value head: (B*T/16 + N) * HV slots of 17,408 B (bf16, K = V = 128). */
+   value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16) or 43,008 B (chunk 32) at
+   bf16 io and K = V = 128. */
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
 
 /* Enqueue the forward: prepare kernel, then state kernel, on `stream` (hipStream_t or NULL).

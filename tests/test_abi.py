@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def args(**kw):
     a = KdaFwdArgs()
-    d = dict(B=1, T=4096, N=1, H=16, HV=16, K=128, V=128, io=0)
+    d = dict(B=1, T=4096, N=1, H=16, HV=16, K=128, V=128, io=0, chunk=16)
     d.update(kw)
     for key, val in d.items():
         setattr(a, key, val)
@@ -59,6 +59,12 @@ def test_workspace_bytes(lib):
     assert f(args(io=1)) == (4096 // 16 + 1) * 16 * 34304
     assert f(args(B=4, T=8192, N=4, H=16, HV=32)) == (4 * 8192 // 16 + 4) * 32 * 17408
     assert f(args(T=45, N=1)) == (45 // 16 + 1) * 16 * 17408
+    assert f(args(chunk=32)) == (4096 // 32 + 1) * 16 * 43008
+    assert f(args(chunk=0)) == f(args(chunk=32))          # bf16 default: 32-token chunks
+    assert f(args(io=1, chunk=0)) == f(args(io=1, chunk=16))
+    assert f(args(chunk=32, T=45)) == (45 // 32 + 1) * 16 * 43008
+    assert f(args(io=1, chunk=32)) == 0                   # fp32 io: 16-token chunks only
+    assert f(args(chunk=64)) == 0
     assert f(args(K=96)) == 0          # unsupported head dim
     assert f(args(HV=24, H=16)) == 0   # HV % H != 0
     assert f(args(N=2)) == 0           # dense batch needs N == B
@@ -69,6 +75,8 @@ def test_workspace_bytes(lib):
     (dict(K=96), _lib.KDA_ERR_UNSUPPORTED),
     (dict(V=32), _lib.KDA_ERR_UNSUPPORTED),
     (dict(io=7), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=8), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(io=1, chunk=32), _lib.KDA_ERR_UNSUPPORTED),
     (dict(HV=24), _lib.KDA_ERR_INVALID_ARG),
     (dict(N=3), _lib.KDA_ERR_INVALID_ARG),
     (dict(T=-1), _lib.KDA_ERR_INVALID_ARG),
@@ -104,7 +112,7 @@ def test_strerror_and_version(lib):
     for st in range(5):
         assert kda._lib.strerror(st)
     assert "unknown" in kda._lib.strerror(99)
-    assert lib.kda_version() == 100
+    assert lib.kda_version() == 101
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):

@@ -16,7 +16,7 @@ import torch
 import workloads as W
 from oracle.chunked import chunk_prepare
 from oracle.native import kda_oracle_c
-from ws_decode import chunk_bytes, decode_chunk
+from ws_decode import chunk_bytes, chunk_bytes32, decode_chunk, decode_chunk32
 
 import chunked_kimi_delta_amd as kda
 
@@ -29,13 +29,15 @@ def dev(x):
     return None if x is None else x.to(DEV).contiguous()
 
 
-def gpu_plan(inp: W.Inputs, scale=None, output_final_state=True):
+def gpu_plan(inp: W.Inputs, scale=None, output_final_state=True, chunk=0):
     return kda.KdaFwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
                           scale=scale, cu_seqlens=dev(inp.cu_seqlens),
-                          initial_state=dev(inp.h0), output_final_state=output_final_state)
+                          initial_state=dev(inp.h0), output_final_state=output_final_state,
+                          chunk=chunk)
 
 
 def gpu_run(inp: W.Inputs, **kw):
+    """Run the forward through the C ABI (kwargs go to KdaFwdPlan) and return fp64 numpy."""
     plan = gpu_plan(inp, **kw)
     o, fin = plan()
     torch.cuda.synchronize()
@@ -87,30 +89,36 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_small_parity(name):
+# chunk lengths the library offers per io dtype (0 = its default)
+CHUNKS = {"bf16": [16, 32], "fp32": [16]}
+SMALL_CASES = [(n, c) for n in SMALL for c in CHUNKS[SMALL[n].dtype]]
+
+
+@pytest.mark.parametrize("name,chunk", SMALL_CASES)
+def test_small_parity(name, chunk):
     w = SMALL[name]
     inp = W.make_inputs(w, seed=0)
-    o, fin = gpu_run(inp)
+    o, fin = gpu_run(inp, chunk=chunk)
     o_ref, f_ref = oracle_run(inp)
     check_all(inp, o, fin, o_ref, f_ref, TOL[w.dtype])
 
 
-@pytest.mark.parametrize("io", ["bf16", "fp32"])
-def test_empty_sequences_carry_initial_state(io):
+@pytest.mark.parametrize("io,chunk", [("bf16", 16), ("bf16", 32), ("fp32", 16)])
+def test_empty_sequences_carry_initial_state(io, chunk):
     w = W.custom(B=2, T=0, H=1, HV=2, K=128, V=64, dtype=io, h0_std=1.0)
     inp = W.make_inputs(w, seed=3)
-    o, fin = gpu_run(inp)
+    o, fin = gpu_run(inp, chunk=chunk)
     assert o.size == 0
     assert np.array_equal(fin, inp.h0.numpy().astype(np.float64))
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("case", ["beta0", "g0"])
-def test_degenerate_gates(case):
+def test_degenerate_gates(case, chunk):
     w = W.custom(B=1, T=90, H=2, HV=2, K=128, V=128, h0_std=0.5)
     kw = {"beta_override": 0.0} if case == "beta0" else {"g_override": 0.0}
     inp = W.make_inputs(w, seed=5, **kw)
-    o, fin = gpu_run(inp)
+    o, fin = gpu_run(inp, chunk=chunk)
     o_ref, f_ref = oracle_run(inp)
     check_all(inp, o, fin, o_ref, f_ref, TOL["bf16"])
     if case == "beta0":   # pure decay: the state never receives a write
@@ -119,7 +127,8 @@ def test_degenerate_gates(case):
         assert rel_l2(fin[0], np.exp(cum)[:, :, None] * S0[0]) <= 1e-3
 
 
-def test_deltanet_retrieval_property():
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_deltanet_retrieval_property(chunk):
     # g = 0, beta = 1 and one fixed unit key shared by all tokens with q = k: each output
     # returns scale * v_t (the plain delta rule overwrites the memory slot every token)
     T, K, V = 64, 128, 128
@@ -133,26 +142,28 @@ def test_deltanet_retrieval_property():
                    torch.randn(1, T, 1, V, generator=gen).to(torch.bfloat16),
                    torch.zeros(1, T, 1, K, dtype=torch.bfloat16),
                    torch.ones(1, T, 1, dtype=torch.bfloat16), None, None, scale=0.5)
-    o, fin = gpu_run(inp, scale=0.5)
+    o, fin = gpu_run(inp, scale=0.5, chunk=chunk)
     o_ref, f_ref = oracle_run(inp)
     check_all(inp, o, fin, o_ref, f_ref, TOL["bf16"])
     nk2 = float((kv.float() ** 2).sum())
     assert rel_l2(o[0, :, 0], 0.5 * nk2 * inp.v.float().numpy()[0, :, 0]) <= 2e-2
 
 
-def test_no_final_state_and_explicit_scale():
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_no_final_state_and_explicit_scale(chunk):
     w = W.custom(B=1, T=64, H=1, HV=2, K=128, V=128)
     inp = W.make_inputs(w, seed=2)
-    o, fin = gpu_run(inp, scale=0.3, output_final_state=False)
+    o, fin = gpu_run(inp, scale=0.3, output_final_state=False, chunk=chunk)
     assert fin is None
     o_ref, _ = oracle_run(inp, scale=0.3)
     assert rel_l2(o, o_ref) <= TOL["bf16"]
 
 
-def test_deterministic_and_repeatable():
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_deterministic_and_repeatable(chunk):
     w = W.custom(B=1, T=300, H=2, HV=2, K=128, V=128, h0_std=0.1)
     inp = W.make_inputs(w, seed=4)
-    plan = gpu_plan(inp)
+    plan = gpu_plan(inp, chunk=chunk)
     o1, f1 = [x.clone() for x in plan()]
     o2, f2 = plan()
     torch.cuda.synchronize()
@@ -164,7 +175,7 @@ def test_prepare_workspace_matches_chunk_oracle():
     # tail chunk) and compare with the fp64 chunked-form intermediates
     w = W.custom(B=1, T=37, H=1, HV=2, K=128, V=128)
     inp = W.make_inputs(w, seed=6)
-    plan = gpu_plan(inp)
+    plan = gpu_plan(inp, chunk=16)
     plan()
     torch.cuda.synchronize()
     ws = plan.workspace.cpu().numpy()
@@ -183,6 +194,28 @@ def test_prepare_workspace_matches_chunk_oracle():
                 assert err <= 1e-2, f"head {j} chunk {c} {key}: rel L2 {err:.2e}"
 
 
+def test_prepare32_workspace_matches_chunk_oracle():
+    # stage-1 diagnostics of the 32-token record (two blocks joined by block substitution)
+    w = W.custom(B=1, T=77, H=1, HV=2, K=128, V=128)
+    inp = W.make_inputs(w, seed=8)
+    plan = gpu_plan(inp, chunk=32)
+    plan()
+    torch.cuda.synchronize()
+    ws = plan.workspace.cpu().numpy()
+    cb = chunk_bytes32(128, 128)
+    n_slots = 77 // 32 + 1
+    f = W.as_f32_numpy
+    for j in range(2):
+        prep = chunk_prepare(f(inp.q)[0, :, 0], f(inp.k)[0, :, 0], f(inp.v)[0, :, j],
+                             f(inp.g)[0, :, j], f(inp.beta)[0, :, j], inp.scale, 32)
+        for c in range(3):
+            off = (j * n_slots + c) * cb
+            got = decode_chunk32(ws[off:off + cb], 128, 128)
+            for key in ("w", "qd", "kr", "u", "Mqk", "eg"):
+                err = rel_l2(got[key], prep[key][c])
+                assert err <= 1e-2, f"head {j} chunk {c} {key}: rel L2 {err:.2e}"
+
+
 FULL = {
     "h16_t4096": None,          # every unit
     "varlen8_h32": 6,
@@ -191,11 +224,12 @@ FULL = {
 }
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled_parity(name):
+def test_full_size_sampled_parity(name, chunk):
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, seed=0)
-    o, fin = gpu_run(inp)
+    o, fin = gpu_run(inp, chunk=chunk)
     assert np.isfinite(o).all() and np.isfinite(fin).all()
     nsamp = FULL[name]
     units = None if nsamp is None else W.sample_units(inp.N, w.HV, nsamp, seed=1)

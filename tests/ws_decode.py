@@ -55,3 +55,57 @@ def decode_chunk(raw: np.ndarray, K: int, V: int):
     off += 512
     out["eg"] = raw[off:off + 4 * K].view(np.float32).astype(np.float64)
     return out
+
+
+def chunk_bytes32(K, V):
+    end = 64 * K * 3 + 128 * V + 512 + 1024 + 4 * K
+    return (end + 255) // 256 * 256
+
+
+def decode_chunk32(raw: np.ndarray, K: int, V: int):
+    """Decode one 32-token chunk record (two 16-row blocks a, b). Returns float64 arrays
+    w [32,K], qd [32,K], kr [32,K], u [32,V], Mqk [32,32] (upper-right block zero: never
+    stored), eg [K]."""
+    h16 = lambda a, b: raw[a:b].view(np.float16).astype(np.float64)
+    NS, NK, NV = K // 32, K // 16, V // 16
+    lanes = np.arange(64)
+    g, m = lanes // 16, lanes % 16
+    out, off = {}, 0
+    for name in ("w", "qd"):
+        frag = h16(off, off + 64 * K).reshape(2, NS, 64, 8)
+        X = np.full((32, K), np.nan)
+        for b in range(2):
+            for s in range(NS):
+                for e in range(8):
+                    X[16 * b + m, 16 * (2 * s + e // 4) + 4 * g + e % 4] = frag[b, s, :, e]
+        out[name] = X
+        off += 64 * K
+    frag = h16(off, off + 64 * K).reshape(NK, 64, 8)
+    X = np.full((32, K), np.nan)
+    for t in range(NK):
+        for e in range(8):
+            tokv = 4 * g + e if e < 4 else 16 + 4 * g + e - 4
+            X[tokv, 16 * t + m] = frag[t, :, e]
+    out["kr"] = X
+    off += 64 * K
+    frag = -raw[off:off + 128 * V].view(np.float32).astype(np.float64).reshape(2, NV, 64, 4)
+    X = np.full((32, V), np.nan)
+    for b in range(2):
+        for c in range(NV):
+            for i in range(4):
+                X[16 * b + 4 * g + i, 16 * c + m] = frag[b, c, :, i]
+    out["u"] = X                       # stored negated, fp32
+    off += 128 * V
+    M = np.zeros((32, 32))
+    fa = h16(off, off + 512).reshape(64, 4)
+    for i in range(4):
+        M[m, 4 * g + i] = fa[:, i]
+    off += 512
+    fb = h16(off, off + 1024).reshape(64, 8)
+    for e in range(8):
+        colv = 4 * g + e if e < 4 else 16 + 4 * g + e - 4
+        M[16 + m, colv] = fb[:, e]
+    out["Mqk"] = M
+    off += 1024
+    out["eg"] = raw[off:off + 4 * K].view(np.float32).astype(np.float64)
+    return out
