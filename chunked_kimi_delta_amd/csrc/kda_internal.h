@@ -270,6 +270,12 @@ __device__ __forceinline__ float lane_read(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
+// Wait for every outstanding vector memory load of this wave (vmcnt 0; the LDS/scalar and
+// export counters are left unconstrained: simm16 = lgkmcnt 15 << 8 | expcnt 7 << 4).
+__device__ __forceinline__ void vm_drain() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
 }  // namespace kda
 
 // Host-side launchers (defined next to their kernels).

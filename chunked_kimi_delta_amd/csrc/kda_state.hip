@@ -227,11 +227,16 @@ __global__ __launch_bounds__(128) void state_bf16_kernel(FwdParams p)
             ChainFrag<K, V> fa, fb;
             at(0).load_w(fa); at(0).load_u(fa); at(0).load_kreg(fa);
             at(1).load_w(fb); at(1).load_u(fb); at(1).load_kreg(fb);
-            for (int c = 0; c < nc; c += 2) {
+            // prologue loads drained and no exit between the loop body's two steps: the loop
+            // header then carries only the loop's own pending loads, so each wait counts back
+            // to the group it needs instead of the loads just issued
+            vm_drain();
+            int c = 0;
+            for (; c + 2 <= nc; c += 2) {
                 chain_step<K, V>(fa, at(c + 2), S, ho, 0, lane);
-                if (c + 1 >= nc) break;
                 chain_step<K, V>(fb, at(c + 3), S, ho, 1, lane);
             }
+            if (c < nc) chain_step<K, V>(fa, at(c + 2), S, ho, 0, lane);
         }
         if (p.ht) {
             float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
@@ -253,11 +258,13 @@ __global__ __launch_bounds__(128) void state_bf16_kernel(FwdParams p)
         OutFrag<K, V> fa, fb;
         at(0).load_out(fa);
         at(1).load_out(fb);
-        for (int c = 0; c < nc; c += 2) {
+        vm_drain();
+        int c = 0;
+        for (; c + 2 <= nc; c += 2) {
             out_step<K, V>(fa, at(c + 2), ho, 0, lane, rows(c), ooff);
-            if (c + 1 >= nc) break;
             out_step<K, V>(fb, at(c + 3), ho, 1, lane, rows(c + 1), ooff);
         }
+        if (c < nc) out_step<K, V>(fa, at(c + 2), ho, 0, lane, rows(c), ooff);
     }
 }
 

@@ -39,10 +39,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *o, int64_t row
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, num, 0x00020000);
 }
 
-__device__ __forceinline__ void vm_drain() {
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
-}
-
 __device__ __forceinline__ void release_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
 }
@@ -52,18 +48,18 @@ __device__ __forceinline__ void acquire_lds() {
 
 template <int K, int V>
 struct ChainFrag32 {
-    static constexpr int EGPL = K / 64;      // exp(gam) values loaded per lane
     f16x8 w[2][K / 32];                      // W rows of blocks a and b
     f16x8 kr[K / 16];                        // KR^T tiles over the 32 tokens
     f32x4 nu[2];                             // -U of blocks a and b, this lane's slice (fp32)
-    float eg[EGPL];
 };
 
 template <int K, int V>
 struct OutFrag32 {
+    static constexpr int EGPL = K / 64;      // exp(gam) values loaded per lane
     f16x8 qd[2][K / 32];
     f16x4 mqa;
     f16x8 mqb;
+    float eg[EGPL];                          // exp(gam) of the chunk two ahead of this one
 };
 
 // One chunk record seen through a buffer resource (scalar base = the record); every field
@@ -72,7 +68,7 @@ struct OutFrag32 {
 template <int K, int V>
 struct Chunk32 {
     using WS = WsBf16x32<K, V>;
-    static constexpr int NS = K / 32, NV = V / 16;
+    static constexpr int NS = K / 32, NV = V / 16, EGPL = K / 64;
     __amdgpu_buffer_rsrc_t rs;
     int lane, slice;
     __device__ __forceinline__ void load_w(ChainFrag32<K, V> &f) const {
@@ -82,15 +78,6 @@ struct Chunk32 {
             for (int st = 0; st < NS; ++st)
                 f.w[b][st] = __builtin_bit_cast(f16x8, bload16(rs, lane * 16,
                                                                WS::W + (b * NS + st) * 1024));
-        if constexpr (ChainFrag32<K, V>::EGPL == 2) {
-            const u32x2 e = bload8(rs, lane * 8, WS::EG);
-            f.eg[0] = __uint_as_float(e[0]);
-            f.eg[1] = __uint_as_float(e[1]);
-        } else {
-            f.eg[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, WS::EG, 0));
-        }
-    }
-    __device__ __forceinline__ void load_nu(ChainFrag32<K, V> &f) const {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
             f.nu[b] = __builtin_bit_cast(f32x4, bload16(rs, lane * 16,
@@ -101,7 +88,17 @@ struct Chunk32 {
         for (int t = 0; t < K / 16; ++t)
             f.kr[t] = __builtin_bit_cast(f16x8, bload16(rs, lane * 16, WS::KR + t * 1024));
     }
-    __device__ __forceinline__ void load_out(OutFrag32<K, V> &f) const {
+    __device__ __forceinline__ void load_eg(float (&eg)[EGPL]) const {
+        if constexpr (EGPL == 2) {
+            const u32x2 e = bload8(rs, lane * 8, WS::EG);
+            eg[0] = __uint_as_float(e[0]);
+            eg[1] = __uint_as_float(e[1]);
+        } else {
+            eg[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, WS::EG, 0));
+        }
+    }
+    // output operands of this chunk and exp(gam) of chunk `ahead` (two chunks later)
+    __device__ __forceinline__ void load_out(OutFrag32<K, V> &f, const Chunk32 &ahead) const {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -110,6 +107,7 @@ struct Chunk32 {
                                                                 WS::QD + (b * NS + st) * 1024));
         f.mqa = __builtin_bit_cast(f16x4, bload8(rs, lane * 8, WS::MQKA));
         f.mqb = __builtin_bit_cast(f16x8, bload16(rs, lane * 16, WS::MQKB));
+        ahead.load_eg(f.eg);
     }
 };
 
@@ -117,53 +115,44 @@ template <int K>
 struct Handoff32 {
     f16x8 sh[2][K / 32][64];     // S (fp16) by chunk parity
     f16x4 dh[2][2][64];          // delta of blocks a and b by chunk parity
-    float eg[2][K];              // chain wave only: exp(gam) by chunk parity, staged for broadcast
+    float eg[2][K];              // exp(gam) by chunk parity, staged by the output wave
 };
 
-// exp(gam) arrives as EGPL values per lane; every lane needs the four values of the S rows
-// 16t + 4g + i it holds, so the chain wave stages the row in LDS one chunk ahead and reads it
-// back as broadcast vector loads (LDS accesses of one wave are processed in order).
-template <int K, int V>
-__device__ __forceinline__ void stage_eg(const ChainFrag32<K, V> &f, Handoff32<K> &ho, int par,
+// exp(gam) arrives as K/64 values per lane, but every chain lane needs the four values of the
+// S rows 16t + 4g + i it holds: the output wave stages the row in LDS two chunks ahead and the
+// chain wave reads it back as broadcast vector loads.
+template <int K>
+__device__ __forceinline__ void stage_eg(const float (&eg)[K / 64], Handoff32<K> &ho, int par,
                                          int lane)
 {
 #pragma unroll
-    for (int e = 0; e < ChainFrag32<K, V>::EGPL; ++e)
-        ho.eg[par][lane * ChainFrag32<K, V>::EGPL + e] = f.eg[e];
+    for (int e = 0; e < K / 64; ++e) ho.eg[par][lane * (K / 64) + e] = eg[e];
 }
 
-// Chain wave, one 32-token chunk: delta = U - W S, hand (S, delta) to the output wave, then
-// S <- diag(e^{gam}) S + KR^T delta. The W S products start from -U, so delta is just the
-// negated accumulator. The fp16 copy of the next S tiles and the decay of the tiles already
-// copied are interleaved between the W S MFMAs. Operand groups of `f` are refilled from `nxt`
-// (two chunks ahead, clamped to the last chunk) right after their last use; `fn` is the buffer
-// of the next chunk, whose exp(gam) (loaded with its W rows a step and a half ago) is staged
-// for the next step.
+// Chain wave, one 32-token chunk with S at the chunk start.
+//   1. exp(gam) of the chunk is read from LDS (latency covered by the products below);
+//   2. the fp16 copy of S goes to the hand-off and into the W S products, which start from -U
+//      so that delta is the negated accumulator; delta goes to the hand-off;
+//   3. S is decayed tile by tile, each tile followed by its update MFMA (KR^T delta); the
+//      update is issued before the hand-off barrier, so the barrier wait overlaps it.
+// The W and -U groups of `f` are refilled from `nxt` (two chunks ahead, clamped to the last
+// chunk) once the products are issued, the KR^T group once the update is issued.
 template <int K, int V>
-__device__ __forceinline__ void chain_step32(ChainFrag32<K, V> &f, const ChainFrag32<K, V> &fn,
-                                             const Chunk32<K, V> &nxt, f32x4 (&S)[K / 16],
-                                             Handoff32<K> &ho, int par, int lane, int grp)
+__device__ __forceinline__ void chain_step32(ChainFrag32<K, V> &f, const Chunk32<K, V> &nxt,
+                                             f32x4 (&S)[K / 16], Handoff32<K> &ho, int par,
+                                             int lane, int grp)
 {
     constexpr int NS = K / 32, NK = K / 16;
-    f16x8 Sh[NS];
+    f32x4 e4[NK];
+#pragma unroll
+    for (int t = 0; t < NK; ++t) e4[t] = *(const f32x4 *)&ho.eg[par][16 * t + 4 * grp];
     f32x4 X0 = f.nu[0], X1 = f.nu[1];
-    Sh[0] = cat(to_f16x4(S[0]), to_f16x4(S[1]));
-    ho.sh[par][0][lane] = Sh[0];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-        X0 = mfma32(f.w[0][st], Sh[st], X0);
-        X1 = mfma32(f.w[1][st], Sh[st], X1);
-        if (st + 1 < NS) {
-            Sh[st + 1] = cat(to_f16x4(S[2 * st + 2]), to_f16x4(S[2 * st + 3]));
-            ho.sh[par][st + 1][lane] = Sh[st + 1];
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = 2 * st + u;
-            const f32x4 e4 = *(const f32x4 *)&ho.eg[par][16 * t + 4 * grp];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[t][i] *= e4[i];
-        }
+        const f16x8 Sh = cat(to_f16x4(S[2 * st]), to_f16x4(S[2 * st + 1]));
+        ho.sh[par][st][lane] = Sh;
+        X0 = mfma32(f.w[0][st], Sh, X0);
+        X1 = mfma32(f.w[1][st], Sh, X1);
     }
     nxt.load_w(f);
     f16x4 dh0, dh1;
@@ -174,29 +163,37 @@ __device__ __forceinline__ void chain_step32(ChainFrag32<K, V> &f, const ChainFr
     }
     ho.dh[par][0][lane] = dh0;
     ho.dh[par][1][lane] = dh1;
-    nxt.load_nu(f);
-    stage_eg(fn, ho, par ^ 1, lane);
-    release_lds();
-    __builtin_amdgcn_s_barrier();
     const f16x8 d32 = cat(dh0, dh1);
 #pragma unroll
-    for (int t = 0; t < NK; ++t) S[t] = mfma32(f.kr[t], d32, S[t]);
+    for (int t = 0; t < NK; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= e4[t][i];
+        S[t] = mfma32(f.kr[t], d32, S[t]);
+    }
+    release_lds();
+    __builtin_amdgcn_s_barrier();
+    acquire_lds();
     nxt.load_kreg(f);
 }
 
-// Output wave, one 32-token chunk: o = QD S + Mqk delta from the hand-off, stored as bf16.
+// Output wave, one 32-token chunk: o = QD S + Mqk delta from the hand-off, stored as bf16;
+// exp(gam) of the chunk two ahead is staged for the chain wave. `nxt` is the record two
+// chunks ahead (output operands) and `nxt2` the one four ahead (its exp(gam)).
 template <int K, int V>
 __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V> &nxt,
-                                           const Handoff32<K> &ho, int par, int lane,
-                                           __amdgpu_buffer_rsrc_t orows, const int (&ooff)[8])
+                                           const Chunk32<K, V> &nxt2, Handoff32<K> &ho, int par,
+                                           int lane, __amdgpu_buffer_rsrc_t orows,
+                                           const int (&ooff)[8])
 {
     constexpr int NS = K / 32;
+    release_lds();
     __builtin_amdgcn_s_barrier();
     acquire_lds();
     f16x8 Sh[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) Sh[st] = ho.sh[par][st][lane];
     const f16x4 dh0 = ho.dh[par][0][lane], dh1 = ho.dh[par][1][lane];
+    stage_eg<K>(f.eg, ho, par, lane);
     f32x4 Y0 = zero4(), Y1 = zero4();
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -205,7 +202,7 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
     }
     const f32x4 O0 = mfma16(f.mqa, dh0, Y0);
     const f32x4 O1 = mfma32(f.mqb, cat(dh0, dh1), Y1);
-    nxt.load_out(f);
+    nxt.load_out(f, nxt2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const __bf16 b0 = (__bf16)O0[i], b1 = (__bf16)O1[i];
@@ -218,6 +215,11 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
 
 }  // namespace
 
+// Barrier schedule (nc chunks, both waves pass nc + 1 barriers): an initial one after the
+// output wave has staged exp(gam) of chunks 0 and 1, then one per chunk c after the chain wave
+// has written the hand-off of chunk c. Between barriers c and c+1 the output wave reads the
+// hand-off slot c % 2 and overwrites the exp(gam) slot c % 2 with chunk c+2, while the chain
+// wave reads exp(gam) slot (c+1) % 2 and writes the hand-off slot (c+1) % 2.
 template <int K, int V>
 __global__ __launch_bounds__(128) void state32_bf16_kernel(FwdParams p)
 {
@@ -255,21 +257,22 @@ __global__ __launch_bounds__(128) void state32_bf16_kernel(FwdParams p)
         }
         if (nc > 0) {
             ChainFrag32<K, V> fa, fb;
-            at(0).load_w(fa); at(0).load_nu(fa); at(0).load_kreg(fa);
-            at(1).load_w(fb); at(1).load_nu(fb); at(1).load_kreg(fb);
+            at(0).load_w(fa); at(0).load_kreg(fa);
+            at(1).load_w(fb); at(1).load_kreg(fb);
             // drain the prologue loads: the loop header then carries only the loop's own
             // pending loads, and the waits inside the loop count back to the right group
             vm_drain();
-            stage_eg(fa, ho, 0, lane);
-            // the loop body has no exit between its two steps: an exit there would merge a
+            __builtin_amdgcn_s_barrier();     // exp(gam) of chunks 0 and 1 staged
+            acquire_lds();
+            // no exit between the loop body's two steps: an exit there would merge a
             // half-step state into the loop header and make every iteration wait for the
             // loads just issued
             int c = 0;
             for (; c + 2 <= nc; c += 2) {
-                chain_step32<K, V>(fa, fb, at(c + 2), S, ho, 0, lane, grp);
-                chain_step32<K, V>(fb, fa, at(c + 3), S, ho, 1, lane, grp);
+                chain_step32<K, V>(fa, at(c + 2), S, ho, 0, lane, grp);
+                chain_step32<K, V>(fb, at(c + 3), S, ho, 1, lane, grp);
             }
-            if (c < nc) chain_step32<K, V>(fa, fb, at(c + 2), S, ho, 0, lane, grp);
+            if (c < nc) chain_step32<K, V>(fa, at(c + 2), S, ho, 0, lane, grp);
         }
         if (p.ht) {
             float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
@@ -292,15 +295,22 @@ __global__ __launch_bounds__(128) void state32_bf16_kernel(FwdParams p)
             return rows_rsrc(p.o, r0, (int)(nv < CT ? nv : CT), row_bytes, head_bytes);
         };
         OutFrag32<K, V> fa, fb;
-        at(0).load_out(fa);
-        at(1).load_out(fb);
+        float eg0[K / 64], eg1[K / 64];
+        at(0).load_eg(eg0);
+        at(1).load_eg(eg1);
+        at(0).load_out(fa, at(2));
+        at(1).load_out(fb, at(3));
         vm_drain();
+        stage_eg<K>(eg0, ho, 0, lane);
+        stage_eg<K>(eg1, ho, 1, lane);
+        release_lds();
+        __builtin_amdgcn_s_barrier();         // initial barrier: exp(gam) of chunks 0 and 1
         int c = 0;
         for (; c + 2 <= nc; c += 2) {
-            out_step32<K, V>(fa, at(c + 2), ho, 0, lane, rows(c), ooff);
-            out_step32<K, V>(fb, at(c + 3), ho, 1, lane, rows(c + 1), ooff);
+            out_step32<K, V>(fa, at(c + 2), at(c + 4), ho, 0, lane, rows(c), ooff);
+            out_step32<K, V>(fb, at(c + 3), at(c + 5), ho, 1, lane, rows(c + 1), ooff);
         }
-        if (c < nc) out_step32<K, V>(fa, at(c + 2), ho, 0, lane, rows(c), ooff);
+        if (c < nc) out_step32<K, V>(fa, at(c + 2), at(c + 4), ho, 0, lane, rows(c), ooff);
     }
 }
 
