@@ -30,9 +30,18 @@ struct Prep32Share {
     bf16x8 kih[K / 32][64];      // block a: k e^{ref - Gam}, hi part, 16x16x32 B operand
     bf16x8 kil[K / 32][64];      //          lo part
     f32x4 xaa[64];               // C(X_aa)
-    bf16x4 kdc[K / 16][64];      // C(KD_a tile c): column-per-lane k e^{Gam} of block a
-    bf16x4 vc[V / 16][64];       // C(V_a tile c)
     float beta_a[16];
+    f32x4 g2b[K / 16][64];       // block b: Gam in TPL, one tile per entry
+    union {                      // block a: its Gam tiles, then (once both of its factor
+        f32x4 g2a[K / 16][64];   // phases are done) its column-per-lane KD and V tiles
+        struct {
+            bf16x4 kdc[K / 16][64];
+            bf16x4 vc[V / 16][64];
+        } cols;
+    } a;
+    __device__ __forceinline__ f32x4 &g2(int wave, int c, int lane) {
+        return wave == 0 ? a.g2a[c][lane] : g2b[c][lane];
+    }
 };
 
 template <int K, int V>
@@ -57,46 +66,47 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
     const int row = 16 * wave + r;
     const bool live = row < nvalid;
     const int64_t tok = bos + row;
+    uint8_t *ws = p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES;
 
-    // ---------------------------------------------------------------- loads (TPL)
-    float qf[NK][4], kf[NK][4], gl[NK][4];
-    uint2 vraw[NV];
+    // ---------------------------------------------------------------- loads (TPL, kept packed)
+    // q, k and v stay as packed bf16 pairs until each use: every phase below rebuilds the fp32
+    // values it needs from them, which keeps the live register set small enough for two waves
+    // per SIMD.
+    uint2 qr[NK], kr[NK], vraw[NV];
+    float G2[NK][4];
     float beta_r = 0.f;
 #pragma unroll
-    for (int c = 0; c < NK; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { qf[c][i] = 0.f; kf[c][i] = 0.f; gl[c][i] = 0.f; }
+    for (int c = 0; c < NK; ++c) { qr[c] = make_uint2(0u, 0u); kr[c] = make_uint2(0u, 0u); }
 #pragma unroll
     for (int c = 0; c < NV; ++c) vraw[c] = make_uint2(0u, 0u);
-    if (live) {
-        const uint16_t *qp = (const uint16_t *)p.q + ((tok * p.H + h) * K + 4 * grp);
-        const uint16_t *kp = (const uint16_t *)p.k + ((tok * p.H + h) * K + 4 * grp);
-        const uint16_t *gp = (const uint16_t *)p.g + ((tok * p.HV + j) * K + 4 * grp);
-        const uint16_t *vp = (const uint16_t *)p.v + ((tok * p.HV + j) * V + 4 * grp);
-        uint2 qr[NK], kr[NK], gr[NK];
+    {
+        uint2 gr[NK];
 #pragma unroll
-        for (int c = 0; c < NK; ++c) {
-            qr[c] = *(const uint2 *)(qp + 16 * c);
-            kr[c] = *(const uint2 *)(kp + 16 * c);
-            gr[c] = *(const uint2 *)(gp + 16 * c);
+        for (int c = 0; c < NK; ++c) gr[c] = make_uint2(0u, 0u);
+        if (live) {
+            const uint16_t *qp = (const uint16_t *)p.q + ((tok * p.H + h) * K + 4 * grp);
+            const uint16_t *kp = (const uint16_t *)p.k + ((tok * p.H + h) * K + 4 * grp);
+            const uint16_t *gp = (const uint16_t *)p.g + ((tok * p.HV + j) * K + 4 * grp);
+            const uint16_t *vp = (const uint16_t *)p.v + ((tok * p.HV + j) * V + 4 * grp);
+#pragma unroll
+            for (int c = 0; c < NK; ++c) {
+                gr[c] = *(const uint2 *)(gp + 16 * c);
+                kr[c] = *(const uint2 *)(kp + 16 * c);
+                qr[c] = *(const uint2 *)(qp + 16 * c);
+            }
+#pragma unroll
+            for (int c = 0; c < NV; ++c) vraw[c] = *(const uint2 *)(vp + 16 * c);
+            beta_r = bf16_bits_to_f32(((const uint16_t *)p.beta)[tok * p.HV + j]);
         }
-#pragma unroll
-        for (int c = 0; c < NV; ++c) vraw[c] = *(const uint2 *)(vp + 16 * c);
-        beta_r = bf16_bits_to_f32(((const uint16_t *)p.beta)[tok * p.HV + j]);
+        // ------------------------------------------------------------ cumsum over 32 tokens
 #pragma unroll
         for (int c = 0; c < NK; ++c) {
-            unpack_bf16x4(qr[c], qf[c]);
-            unpack_bf16x4(kr[c], kf[c]);
-            unpack_bf16x4(gr[c], gl[c]);
+            float gl[4];
+            unpack_bf16x4(gr[c], gl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[i] * LOG2E);
         }
     }
-
-    // ---------------------------------------------------------------- cumsum over 32 tokens
-    float G2[NK][4];
-#pragma unroll
-    for (int c = 0; c < NK; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[c][i] * LOG2E);
     if (wave == 0) {
         if (r == 15) {
 #pragma unroll
@@ -120,131 +130,189 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
                 for (int i = 0; i < 4; ++i) sh.tot_ab[16 * c + 4 * grp + i] = G2[c][i];
         }
     }
+    // Gam goes to LDS and is read back one tile at a time by both factor phases
+#pragma unroll
+    for (int c = 0; c < NK; ++c)
+        sh.g2(wave, c, lane) = f32x4{G2[c][0], G2[c][1], G2[c][2], G2[c][3]};
     __syncthreads();
 
-    // ---------------------------------------------------------------- decay factors
-    // reference point: the cumsum at the block boundary (token 15), the middle of the chunk
-    const float sc = p.scale;
-    float KD[NK][4], QD[NK][4], KRv[NK][4];
-    bf16x8 kdh[NS], kdl[NS], kih[NS], kil[NS], qdh[NS], qdl[NS];
-#pragma unroll
-    for (int c = 0; c < NK; ++c) {
-        const float4 rf = *(const float4 *)&sh.tot_a[16 * c + 4 * grp];
-        const float4 gm = *(const float4 *)&sh.tot_ab[16 * c + 4 * grp];
-        const float ref[4] = {rf.x, rf.y, rf.z, rf.w};
-        const float gam[4] = {gm.x, gm.y, gm.z, gm.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float d1 = G2[c][i] - ref[i];
-            const float e1 = __builtin_amdgcn_exp2f(d1);
-            const float e2 = __builtin_amdgcn_exp2f(-d1);
-            const float eA = __builtin_amdgcn_exp2f(G2[c][i]);
-            const float eR = __builtin_amdgcn_exp2f(gam[i] - G2[c][i]);
-            const float kk = kf[c][i], qq = sc * qf[c][i];
-            KD[c][i] = kk * eA;
-            QD[c][i] = qq * eA;
-            KRv[c][i] = kk * eR;
-            const float xd = kk * e1, xi = kk * e2, xq = qq * e1;
-            const int st = c >> 1, e = (c & 1) * 4 + i;
-            const __bf16 hd = (__bf16)xd, hi_ = (__bf16)xi, hq = (__bf16)xq;
-            kdh[st][e] = hd; kdl[st][e] = (__bf16)(xd - (float)hd);
-            kih[st][e] = hi_; kil[st][e] = (__bf16)(xi - (float)hi_);
-            qdh[st][e] = hq; qdl[st][e] = (__bf16)(xq - (float)hq);
-        }
-    }
-    if (wave == 0) {
-#pragma unroll
-        for (int st = 0; st < NS; ++st) { sh.kih[st][lane] = kih[st]; sh.kil[st][lane] = kil[st]; }
-    }
-
-    // ---------------------------------------------------------------- diagonal blocks
-    f32x4 Lacc = zero4(), Macc = zero4();
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        Lacc = mfma32(kdh[st], kih[st], Lacc);
-        Macc = mfma32(qdh[st], kih[st], Macc);
-        Lacc = mfma32(kdh[st], kil[st], Lacc);
-        Macc = mfma32(qdh[st], kil[st], Macc);
-        Lacc = mfma32(kdl[st], kih[st], Lacc);
-        Macc = mfma32(qdl[st], kih[st], Macc);
-    }
-    float b4[4], Mq[4];
-    f32x4 L, eye;
+    float b4[4], eye[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * grp + i;
-        b4[i] = lane_read(beta_r, rr);                   // beta of row rr of this block
-        L[i] = rr > r ? b4[i] * Lacc[i] : 0.f;
-        Mq[i] = rr >= r ? Macc[i] : 0.f;
-        eye[i] = rr == r ? 1.f : 0.f;
+        b4[i] = lane_read(beta_r, 4 * grp + i);        // beta of row 4g + i of this block
+        eye[i] = 4 * grp + i == r ? 1.f : 0.f;
     }
     const bf16x4 Ib = to_bf16x4(eye);
     const f16x4 Ih = to_f16x4(eye);
 
+    // The two factor phases below are independent except that block b's off-diagonal Gram
+    // products need block a's KI factors. Block a therefore forms its Gram products first and
+    // block b its QD / KR phase; after the hand-over each does the other phase, and block b
+    // builds its diagonal and off-diagonal products slab by slab without keeping any factors.
+    const float sc = p.scale;
+    bf16x4 kdC[NK];
+    f32x4 Lacc = zero4(), Macc = zero4(), Lba = zero4(), Mba = zero4();
+
+    // QD, KR, e^{gam}, KD: factors relative to the chunk start, stored as soon as they are
+    // formed; KD is kept in column-per-lane form (identity MFMA) for W
+    auto qd_kr_phase = [&]() {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            float QD[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int c = 2 * st + u;
+                const float4 gm = *(const float4 *)&sh.tot_ab[16 * c + 4 * grp];
+                const float gam[4] = {gm.x, gm.y, gm.z, gm.w};
+                const f32x4 gc = sh.g2(wave, c, lane);
+                float kk[4], qq[4], KD[4], KRv[4];
+                unpack_bf16x4(kr[c], kk);
+                unpack_bf16x4(qr[c], qq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float eA = __builtin_amdgcn_exp2f(gc[i]);
+                    const float eR = __builtin_amdgcn_exp2f(gam[i] - gc[i]);
+                    KD[i] = kk[i] * eA;
+                    QD[u][i] = sc * qq[i] * eA;
+                    KRv[i] = kk[i] * eR;
+                }
+                kdC[c] = to_bf16x4(mfma16(to_bf16x4(KD), Ib, zero4()));
+                *(f16x4 *)(ws + WS::KR + (c * 64 + lane) * 16 + wave * 8) =
+                    to_f16x4(mfma16(to_f16x4(KRv), Ih, zero4()));
+            }
+            *(f16x8 *)(ws + WS::QD + ((wave * NS + st) * 64 + lane) * 16) =
+                cat(to_f16x4(QD[0]), to_f16x4(QD[1]));
+        }
+        if (wave == 1 && r == 15) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c) {
+                const f32x4 gc = sh.g2b[c][lane];
+                float4 e;
+                e.x = __builtin_amdgcn_exp2f(gc[0]);
+                e.y = __builtin_amdgcn_exp2f(gc[1]);
+                e.z = __builtin_amdgcn_exp2f(gc[2]);
+                e.w = __builtin_amdgcn_exp2f(gc[3]);
+                *(float4 *)(ws + WS::EG + (16 * c + 4 * grp) * 4) = e;
+            }
+        }
+    };
+
+    // Gram products L = KD KI^T and Mqk = QD KI^T with factors centred on the block boundary
+    // (token 15, the middle of the chunk), each as hi + lo bf16 in three passes (hi hi, hi lo,
+    // lo hi), one 32-column slab at a time. Block a publishes its KI factors; block b also
+    // contracts its rows against them (the off-diagonal blocks L_ba, Mqk_ba).
+    auto gram_phase = [&]() {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            bf16x8 kdh, kdl, kih, kil, qdh, qdl;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int c = 2 * st + u;
+                const float4 rf = *(const float4 *)&sh.tot_a[16 * c + 4 * grp];
+                const float ref[4] = {rf.x, rf.y, rf.z, rf.w};
+                const f32x4 gc = sh.g2(wave, c, lane);
+                float kk[4], qq[4];
+                unpack_bf16x4(kr[c], kk);
+                unpack_bf16x4(qr[c], qq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d1 = gc[i] - ref[i];
+                    const float e1 = __builtin_amdgcn_exp2f(d1);
+                    const float e2 = __builtin_amdgcn_exp2f(-d1);
+                    const float xd = kk[i] * e1, xi = kk[i] * e2, xq = sc * qq[i] * e1;
+                    const int e = u * 4 + i;
+                    const __bf16 hd = (__bf16)xd, hi_ = (__bf16)xi, hq = (__bf16)xq;
+                    kdh[e] = hd; kdl[e] = (__bf16)(xd - (float)hd);
+                    kih[e] = hi_; kil[e] = (__bf16)(xi - (float)hi_);
+                    qdh[e] = hq; qdl[e] = (__bf16)(xq - (float)hq);
+                }
+            }
+            Lacc = mfma32(kdh, kih, Lacc);
+            Macc = mfma32(qdh, kih, Macc);
+            Lacc = mfma32(kdh, kil, Lacc);
+            Macc = mfma32(qdh, kil, Macc);
+            Lacc = mfma32(kdl, kih, Lacc);
+            Macc = mfma32(qdl, kih, Macc);
+            if (wave == 0) {
+                sh.kih[st][lane] = kih;
+                sh.kil[st][lane] = kil;
+            } else {
+                const bf16x8 ah = sh.kih[st][lane], al = sh.kil[st][lane];
+                Lba = mfma32(kdh, ah, Lba);
+                Mba = mfma32(qdh, ah, Mba);
+                Lba = mfma32(kdh, al, Lba);
+                Mba = mfma32(qdh, al, Mba);
+                Lba = mfma32(kdl, ah, Lba);
+                Mba = mfma32(qdl, ah, Mba);
+            }
+        }
+    };
+
+    if (wave == 0) gram_phase(); else qd_kr_phase();
+    __syncthreads();
+    if (wave == 0) qd_kr_phase(); else gram_phase();
+
+    float Mq[4];
+    f32x4 L;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * grp + i;
+        L[i] = rr > r ? b4[i] * Lacc[i] : 0.f;
+        Mq[i] = rr >= r ? Macc[i] : 0.f;
+    }
+    const f32x4 eyev = {eye[0], eye[1], eye[2], eye[3]};
+
     // Neumann product of the diagonal block on the fp32 matrix core (see kda_prepare.hip):
     // INV = C(X^T); block a also forms C(X) for block b's off-diagonal solve
-    const f32x4 Mf = mm16_f32(L, eye, zero4());
+    const f32x4 Mf = mm16_f32(L, eyev, zero4());
     const f32x4 P2 = mm16_f32(L, Mf, zero4());
     const f32x4 Q2 = mm16_f32(Mf, L, zero4());
     const f32x4 P4 = mm16_f32(Q2, P2, zero4());
     const f32x4 Q4 = mm16_f32(P2, Q2, zero4());
     const f32x4 Q8 = mm16_f32(P4, Q4, zero4());
-    f32x4 INV = eye - Mf;
+    f32x4 INV = eyev - Mf;
     INV = mm16_f32(Q2, INV, INV);
     INV = mm16_f32(Q4, INV, INV);
     INV = mm16_f32(Q8, INV, INV);
     if (wave == 0) {
         const f32x4 P8 = mm16_f32(Q4, P4, zero4());       // C(M^8) == A16 of L^8
-        f32x4 XN = eye - L;                                // C(I - L)
+        f32x4 XN = eyev - L;                               // C(I - L)
         XN = mm16_f32(P2, XN, XN);                         // (I + L^2)(I - L)
         XN = mm16_f32(P4, XN, XN);
         XN = mm16_f32(P8, XN, XN);                         // C(X_aa)
         sh.xaa[lane] = XN;
     }
 
-    uint8_t *ws = p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES;
-
-    // column-per-lane KD and V tiles of this block (identity MFMAs)
-    bf16x4 kdC[NK], vC[NV];
-#pragma unroll
-    for (int c = 0; c < NK; ++c) kdC[c] = to_bf16x4(mfma16(to_bf16x4(KD[c]), Ib, zero4()));
+    // column-per-lane KD and V tiles of block a for block b's W and U rows
+    bf16x4 vC[NV];
 #pragma unroll
     for (int c = 0; c < NV; ++c)
         vC[c] = to_bf16x4(mfma16(__builtin_bit_cast(bf16x4, vraw[c]), Ib, zero4()));
     if (wave == 0) {
 #pragma unroll
-        for (int c = 0; c < NK; ++c) sh.kdc[c][lane] = kdC[c];
+        for (int c = 0; c < NK; ++c) sh.a.cols.kdc[c][lane] = kdC[c];
 #pragma unroll
-        for (int c = 0; c < NV; ++c) sh.vc[c][lane] = vC[c];
+        for (int c = 0; c < NV; ++c) sh.a.cols.vc[c][lane] = vC[c];
     }
     __syncthreads();
 
-    // ---------------------------------------------------------------- W, U
+    // ---------------------------------------------------------------- W, U, Mqk
     float AT[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) AT[i] = INV[i] * b4[i];     // C(A_xx^T) = diag(beta) X_xx^T
     const bf16x4 ATb = to_bf16x4(AT);
-    f16x4 wT[NK];
-    f32x4 uT[NV];
-    f16x4 MqbaT = to_f16x4(zero4());
+    const f16x4 MqT = to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4()));   // C(Mqk_xx^T)
     if (wave == 0) {
 #pragma unroll
-        for (int c = 0; c < NK; ++c) wT[c] = to_f16x4(mfma16(kdC[c], ATb, zero4()));
+        for (int st = 0; st < NS; ++st)
+            *(f16x8 *)(ws + WS::W + (st * 64 + lane) * 16) =
+                cat(to_f16x4(mfma16(kdC[2 * st], ATb, zero4())),
+                    to_f16x4(mfma16(kdC[2 * st + 1], ATb, zero4())));
 #pragma unroll
-        for (int c = 0; c < NV; ++c) uT[c] = mfma16(ATb, vC[c], zero4());
+        for (int c = 0; c < NV; ++c)
+            *(f32x4 *)(ws + WS::NU + (c * 64 + lane) * 16) = -mfma16(ATb, vC[c], zero4());
+        *(f16x4 *)(ws + WS::MQKA + lane * 8) = MqT;
     } else {
-        // off-diagonal blocks of L and Mqk: block b rows against block a columns
-        f32x4 Lba = zero4(), Mba = zero4();
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            const bf16x8 ah = sh.kih[st][lane], al = sh.kil[st][lane];
-            Lba = mfma32(kdh[st], ah, Lba);
-            Mba = mfma32(qdh[st], ah, Mba);
-            Lba = mfma32(kdh[st], al, Lba);
-            Mba = mfma32(qdh[st], al, Mba);
-            Lba = mfma32(kdl[st], ah, Lba);
-            Mba = mfma32(qdl[st], ah, Mba);
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Lba[i] *= b4[i];
         // X_ba^T = -X_aa^T L_ba^T X_bb^T
@@ -256,45 +324,17 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
         const bf16x4 ABTb = to_bf16x4(ABT);                  // C(A_ba^T)
         const bf16x8 Arow = cat(ABTb, ATb);                  // [A_ba | A_bb] as A (16 x 32)
 #pragma unroll
-        for (int c = 0; c < NK; ++c)
-            wT[c] = to_f16x4(mfma32(cat(sh.kdc[c][lane], kdC[c]), Arow, zero4()));
+        for (int st = 0; st < NS; ++st)
+            *(f16x8 *)(ws + WS::W + ((NS + st) * 64 + lane) * 16) =
+                cat(to_f16x4(mfma32(cat(sh.a.cols.kdc[2 * st][lane], kdC[2 * st]), Arow, zero4())),
+                    to_f16x4(mfma32(cat(sh.a.cols.kdc[2 * st + 1][lane], kdC[2 * st + 1]), Arow,
+                                    zero4())));
 #pragma unroll
-        for (int c = 0; c < NV; ++c) uT[c] = mfma32(Arow, cat(sh.vc[c][lane], vC[c]), zero4());
-        MqbaT = to_f16x4(mfma16(to_f16x4(Mba), Ih, zero4()));  // C(Mqk_ba^T)
-    }
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-        *(f16x8 *)(ws + WS::W + ((wave * NS + st) * 64 + lane) * 16) =
-            cat(wT[2 * st], wT[2 * st + 1]);
-#pragma unroll
-    for (int c = 0; c < NV; ++c)
-        *(f32x4 *)(ws + WS::NU + ((wave * NV + c) * 64 + lane) * 16) = -uT[c];
-
-    // ---------------------------------------------------------------- QD, KR, Mqk, e^{gam}
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-        *(f16x8 *)(ws + WS::QD + ((wave * NS + st) * 64 + lane) * 16) =
-            cat(to_f16x4(QD[2 * st]), to_f16x4(QD[2 * st + 1]));
-#pragma unroll
-    for (int c = 0; c < NK; ++c)
-        *(f16x4 *)(ws + WS::KR + (c * 64 + lane) * 16 + wave * 8) =
-            to_f16x4(mfma16(to_f16x4(KRv[c]), Ih, zero4()));
-    const f16x4 MqT = to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4()));   // C(Mqk_xx^T)
-    if (wave == 0) {
-        *(f16x4 *)(ws + WS::MQKA + lane * 8) = MqT;
-    } else {
+        for (int c = 0; c < NV; ++c)
+            *(f32x4 *)(ws + WS::NU + ((NV + c) * 64 + lane) * 16) =
+                -mfma32(Arow, cat(sh.a.cols.vc[c][lane], vC[c]), zero4());
+        const f16x4 MqbaT = to_f16x4(mfma16(to_f16x4(Mba), Ih, zero4()));  // C(Mqk_ba^T)
         *(f16x8 *)(ws + WS::MQKB + lane * 16) = cat(MqbaT, MqT);
-        if (r == 15) {
-#pragma unroll
-            for (int c = 0; c < NK; ++c) {
-                float4 e;
-                e.x = __builtin_amdgcn_exp2f(G2[c][0]);
-                e.y = __builtin_amdgcn_exp2f(G2[c][1]);
-                e.z = __builtin_amdgcn_exp2f(G2[c][2]);
-                e.w = __builtin_amdgcn_exp2f(G2[c][3]);
-                *(float4 *)(ws + WS::EG + (16 * c + 4 * grp) * 4) = e;
-            }
-        }
     }
 }
 
