@@ -7,14 +7,19 @@
 //     o     = QD S + Mqk delta             (32 x V), rows past the sequence end not stored
 //     S    <- diag(e^{gam}) S + KR^T delta
 //
-// Same structure as the 16-token kernel (kda_state.hip): one workgroup = a chain wave and an
-// output wave on two SIMDs for one (sequence, value head, 16-column slice), S in fp32 registers,
-// fp16 operands, a double-buffered LDS hand-off and one barrier per chunk. Chunk operands are
-// read through buffer resources (scalar addressing). The 32-token step is
-// what makes the chain cheaper per token: W S is two independent 16-row products (8 MFMAs), the
-// state update contracts all 32 tokens in one full-rate 16x16x32 MFMA per 16-row tile of S
-// (8 MFMAs, against 8 half-rate 16x16x16 MFMAs per 16 tokens), and the per-step VALU work
-// (fp16 copy of S, decay, hand-off, barrier) is paid once per 32 tokens.
+// One workgroup per (sequence, value head, 16-column slice of V), three waves on three SIMDs:
+// two chain waves that each own half of the key rows of S (fp32 registers) and one output wave.
+// A chain step is split where the contraction over the key dimension allows it: each chain
+// wave forms its half of W S from its fp16 rows and hands the 32 x 16 fp32 partial to the
+// other through LDS; after the step's barrier both add the two partials (in the same order of
+// operands, so both hold the same delta), and each updates its own rows. The per-step VMEM,
+// VALU and MFMA work of one chain wave is half of a single-wave chain's, which is what bounds
+// the step: the serial path per 32 tokens is one LDS exchange, four update MFMAs and four W S
+// MFMAs. The output wave computes o for chunk c one barrier later, from the fp16 copy of S
+// the chain waves wrote and delta.
+//
+// Fragments are loaded two chunks ahead through buffer resources (scalar base = the chunk
+// record, clamped to the last chunk), in the lane order the prepare kernel wrote them.
 #include "kda_internal.h"
 
 namespace kda {
@@ -45,60 +50,66 @@ __device__ __forceinline__ void release_lds() {
 __device__ __forceinline__ void acquire_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+__device__ __forceinline__ void lds_barrier() {
+    release_lds();
+    __builtin_amdgcn_s_barrier();
+    acquire_lds();
+}
 
+// Operands of one chunk for the chain wave that owns key rows [K/2 h, K/2 (h + 1)).
 template <int K, int V>
-struct ChainFrag32 {
-    f16x8 w[2][K / 32];                      // W rows of blocks a and b
-    f16x8 kr[K / 16];                        // KR^T tiles over the 32 tokens
-    f32x4 nu[2];                             // -U of blocks a and b, this lane's slice (fp32)
+struct HalfFrag {
+    static constexpr int NSH = K / 64, NKH = K / 32;   // 32-row slabs and 16-row tiles owned
+    f16x8 w[2][NSH];          // W rows of blocks a and b, this half's columns
+    f16x8 kr[NKH];            // KR^T tiles of this half over the 32 tokens
+    f32x4 eg[NKH];            // exp(gam) of the four rows 16t + 4g + i each lane holds
+    f32x4 nu[2];              // -U of blocks a and b (half 0 only)
 };
 
 template <int K, int V>
 struct OutFrag32 {
-    static constexpr int EGPL = K / 64;      // exp(gam) values loaded per lane
     f16x8 qd[2][K / 32];
     f16x4 mqa;
     f16x8 mqb;
-    float eg[EGPL];                          // exp(gam) of the chunk two ahead of this one
 };
 
-// One chunk record seen through a buffer resource (scalar base = the record); every field
-// offset is a scalar constant and the per-lane part is lane * size, so no load needs vector
-// address arithmetic.
+// One chunk record seen through a buffer resource (scalar base = the record); field offsets
+// are scalar constants and the per-lane part is lane * size.
 template <int K, int V>
 struct Chunk32 {
     using WS = WsBf16x32<K, V>;
-    static constexpr int NS = K / 32, NV = V / 16, EGPL = K / 64;
+    static constexpr int NS = K / 32, NV = V / 16;
+    static constexpr int NSH = HalfFrag<K, V>::NSH, NKH = HalfFrag<K, V>::NKH;
     __amdgpu_buffer_rsrc_t rs;
     int lane, slice;
-    __device__ __forceinline__ void load_w(ChainFrag32<K, V> &f) const {
+    template <int h>
+    __device__ __forceinline__ void load_w(HalfFrag<K, V> &f) const {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
-                f.w[b][st] = __builtin_bit_cast(f16x8, bload16(rs, lane * 16,
-                                                               WS::W + (b * NS + st) * 1024));
+            for (int j = 0; j < NSH; ++j)
+                f.w[b][j] = __builtin_bit_cast(
+                    f16x8, bload16(rs, lane * 16, WS::W + (b * NS + h * NSH + j) * 1024));
+        const int grp = lane >> 4;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-            f.nu[b] = __builtin_bit_cast(f32x4, bload16(rs, lane * 16,
-                                                        WS::NU + (b * NV + slice) * 1024));
-    }
-    __device__ __forceinline__ void load_kreg(ChainFrag32<K, V> &f) const {
+        for (int t = 0; t < NKH; ++t)
+            f.eg[t] = __builtin_bit_cast(
+                f32x4, bload16(rs, grp * 16, WS::EG + (h * NKH + t) * 64));
+        if constexpr (h == 0) {
 #pragma unroll
-        for (int t = 0; t < K / 16; ++t)
-            f.kr[t] = __builtin_bit_cast(f16x8, bload16(rs, lane * 16, WS::KR + t * 1024));
-    }
-    __device__ __forceinline__ void load_eg(float (&eg)[EGPL]) const {
-        if constexpr (EGPL == 2) {
-            const u32x2 e = bload8(rs, lane * 8, WS::EG);
-            eg[0] = __uint_as_float(e[0]);
-            eg[1] = __uint_as_float(e[1]);
-        } else {
-            eg[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, WS::EG, 0));
+            for (int b = 0; b < 2; ++b)
+                f.nu[b] = __builtin_bit_cast(f32x4, bload16(rs, lane * 16,
+                                                            WS::NU + (b * NV + slice) * 1024));
         }
     }
-    // output operands of this chunk and exp(gam) of chunk `ahead` (two chunks later)
-    __device__ __forceinline__ void load_out(OutFrag32<K, V> &f, const Chunk32 &ahead) const {
+    template <int h>
+    __device__ __forceinline__ void load_kreg(HalfFrag<K, V> &f) const {
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+            f.kr[t] = __builtin_bit_cast(f16x8,
+                                         bload16(rs, lane * 16, WS::KR + (h * NKH + t) * 1024));
+    }
+    __device__ __forceinline__ void load_out(OutFrag32<K, V> &f) const {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -107,93 +118,154 @@ struct Chunk32 {
                                                                 WS::QD + (b * NS + st) * 1024));
         f.mqa = __builtin_bit_cast(f16x4, bload8(rs, lane * 8, WS::MQKA));
         f.mqb = __builtin_bit_cast(f16x8, bload16(rs, lane * 16, WS::MQKB));
-        ahead.load_eg(f.eg);
     }
 };
 
 template <int K>
 struct Handoff32 {
-    f16x8 sh[2][K / 32][64];     // S (fp16) by chunk parity
-    f16x4 dh[2][2][64];          // delta of blocks a and b by chunk parity
-    float eg[2][K];              // exp(gam) by chunk parity, staged by the output wave
+    f16x8 sh[3][K / 32][64];     // S (fp16) of chunk c in slot c % 3
+    f32x4 xp[2][2][2][64];       // [chunk parity][half][block] partial W S (half 0: + (-U))
+    f16x4 dh[2][2][64];          // [chunk parity][block] delta
 };
 
-// exp(gam) arrives as K/64 values per lane, but every chain lane needs the four values of the
-// S rows 16t + 4g + i it holds: the output wave stages the row in LDS two chunks ahead and the
-// chain wave reads it back as broadcast vector loads.
-template <int K>
-__device__ __forceinline__ void stage_eg(const float (&eg)[K / 64], Handoff32<K> &ho, int par,
-                                         int lane)
+// Chain wave h, one 32-token chunk c (S = its rows of the state at the chunk start), up to
+// and including barrier c: fp16 rows to the hand-off, the partial of W S to the other half,
+// then the decay of its rows; the W / exp(gam) / -U group of `f` is refilled from `nxt` (two
+// chunks ahead).
+template <int K, int V, int h>
+__device__ __forceinline__ void chain_half_a(HalfFrag<K, V> &f, const Chunk32<K, V> &nxt,
+                                             f32x4 (&S)[K / 32], f32x4 &Xa, f32x4 &Xb,
+                                             Handoff32<K> &ho, int slot, int par, int lane)
 {
+    constexpr int NSH = K / 64, NKH = K / 32;
+    if constexpr (h == 0) {
+        Xa = f.nu[0];
+        Xb = f.nu[1];
+    } else {
+        Xa = zero4();
+        Xb = zero4();
+    }
 #pragma unroll
-    for (int e = 0; e < K / 64; ++e) ho.eg[par][lane * (K / 64) + e] = eg[e];
+    for (int j = 0; j < NSH; ++j) {
+        const f16x8 Sh = cat(to_f16x4(S[2 * j]), to_f16x4(S[2 * j + 1]));
+        ho.sh[slot][h * NSH + j][lane] = Sh;
+        Xa = mfma32(f.w[0][j], Sh, Xa);
+        Xb = mfma32(f.w[1][j], Sh, Xb);
+    }
+    ho.xp[par][h][0][lane] = Xa;
+    ho.xp[par][h][1][lane] = Xb;
+#pragma unroll
+    for (int t = 0; t < NKH; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
+    nxt.template load_w<h>(f);
+    lds_barrier();
 }
 
-// Chain wave, one 32-token chunk with S at the chunk start.
-//   1. exp(gam) of the chunk is read from LDS (latency covered by the products below);
-//   2. the fp16 copy of S goes to the hand-off and into the W S products, which start from -U
-//      so that delta is the negated accumulator; delta goes to the hand-off;
-//   3. S is decayed tile by tile, each tile followed by its update MFMA (KR^T delta); the
-//      update is issued before the hand-off barrier, so the barrier wait overlaps it.
-// The W and -U groups of `f` are refilled from `nxt` (two chunks ahead, clamped to the last
-// chunk) once the products are issued, the KR^T group once the update is issued.
-template <int K, int V>
-__device__ __forceinline__ void chain_step32(ChainFrag32<K, V> &f, const Chunk32<K, V> &nxt,
-                                             f32x4 (&S)[K / 16], Handoff32<K> &ho, int par,
-                                             int lane, int grp)
+// Chain wave h after barrier c: delta = -(own partial + other partial) (half 0 hands it to the
+// output wave), then the update of its rows; the KR^T group is refilled from `nxt`.
+template <int K, int V, int h>
+__device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, const Chunk32<K, V> &nxt,
+                                             f32x4 (&S)[K / 32], f32x4 Xa, f32x4 Xb,
+                                             Handoff32<K> &ho, int par, int lane)
 {
-    constexpr int NS = K / 32, NK = K / 16;
-    f32x4 e4[NK];
-#pragma unroll
-    for (int t = 0; t < NK; ++t) e4[t] = *(const f32x4 *)&ho.eg[par][16 * t + 4 * grp];
-    f32x4 X0 = f.nu[0], X1 = f.nu[1];
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        const f16x8 Sh = cat(to_f16x4(S[2 * st]), to_f16x4(S[2 * st + 1]));
-        ho.sh[par][st][lane] = Sh;
-        X0 = mfma32(f.w[0][st], Sh, X0);
-        X1 = mfma32(f.w[1][st], Sh, X1);
-    }
-    nxt.load_w(f);
+    constexpr int NKH = K / 32;
+    const f32x4 Pa = ho.xp[par][1 - h][0][lane], Pb = ho.xp[par][1 - h][1][lane];
     f16x4 dh0, dh1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        dh0[i] = (_Float16)(-X0[i]);
-        dh1[i] = (_Float16)(-X1[i]);
+        // half 0 adds (own + other) and half 1 (other + own): the same two fp32 operands, so
+        // both halves round to the same delta
+        dh0[i] = (_Float16)(-(Xa[i] + Pa[i]));
+        dh1[i] = (_Float16)(-(Xb[i] + Pb[i]));
     }
-    ho.dh[par][0][lane] = dh0;
-    ho.dh[par][1][lane] = dh1;
+    if constexpr (h == 0) {
+        ho.dh[par][0][lane] = dh0;
+        ho.dh[par][1][lane] = dh1;
+    }
     const f16x8 d32 = cat(dh0, dh1);
 #pragma unroll
-    for (int t = 0; t < NK; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] *= e4[t][i];
-        S[t] = mfma32(f.kr[t], d32, S[t]);
-    }
-    release_lds();
-    __builtin_amdgcn_s_barrier();
-    acquire_lds();
-    nxt.load_kreg(f);
+    for (int t = 0; t < NKH; ++t) S[t] = mfma32(f.kr[t], d32, S[t]);
+    nxt.template load_kreg<h>(f);
 }
 
-// Output wave, one 32-token chunk: o = QD S + Mqk delta from the hand-off, stored as bf16;
-// exp(gam) of the chunk two ahead is staged for the chain wave. `nxt` is the record two
-// chunks ahead (output operands) and `nxt2` the one four ahead (its exp(gam)).
+template <int K, int V, int h>
+__device__ __forceinline__ void chain_step(HalfFrag<K, V> &f, const Chunk32<K, V> &nxt,
+                                           f32x4 (&S)[K / 32], Handoff32<K> &ho, int c,
+                                           int par, int lane)
+{
+    f32x4 Xa, Xb;
+    chain_half_a<K, V, h>(f, nxt, S, Xa, Xb, ho, c % 3, par, lane);
+    chain_half_b<K, V, h>(f, nxt, S, Xa, Xb, ho, par, lane);
+}
+
+// Chain wave h over the whole sequence: S rows [K/2 h, K/2 (h + 1)) from initial_state (or 0),
+// the chunk loop, barrier nc, and the final state.
+template <int K, int V, int h>
+__device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
+                                           const uint8_t *base, int nc, int s, int j, int col,
+                                           int slice, int lane)
+{
+    constexpr int NKH = K / 32;
+    using WS = WsBf16x32<K, V>;
+    const int grp = lane >> 4;
+    const int row0 = h * (K / 2);
+    auto at = [&](int c) {
+        return Chunk32<K, V>{buffer_rsrc(base + (size_t)min(c, nc - 1) * WS::BYTES, WS::BYTES),
+                             lane, slice};
+    };
+    f32x4 S[NKH];
+    if (p.h0) {
+        const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[t][i] = h0[(size_t)(row0 + 16 * t + 4 * grp + i) * V];
+    } else {
+#pragma unroll
+        for (int t = 0; t < NKH; ++t) S[t] = zero4();
+    }
+    if (nc > 0) {
+        HalfFrag<K, V> fa, fb;
+        at(0).template load_w<h>(fa); at(0).template load_kreg<h>(fa);
+        at(1).template load_w<h>(fb); at(1).template load_kreg<h>(fb);
+        // drain the prologue loads: the loop header then carries only the loop's own pending
+        // loads, and the waits inside the loop count back to the right group
+        vm_drain();
+        // no exit between the loop body's two steps: an exit there would merge a half-step
+        // state into the loop header and make every iteration wait for the loads just issued
+        int c = 0;
+        for (; c + 2 <= nc; c += 2) {
+            chain_step<K, V, h>(fa, at(c + 2), S, ho, c, 0, lane);
+            chain_step<K, V, h>(fb, at(c + 3), S, ho, c + 1, 1, lane);
+        }
+        if (c < nc) chain_step<K, V, h>(fa, at(c + 2), S, ho, c, 0, lane);
+        lds_barrier();    // barrier nc: delta of the last chunk is in the hand-off
+    }
+    if (p.ht) {
+        float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ht[(size_t)(row0 + 16 * t + 4 * grp + i) * V] = S[t][i];
+    }
+}
+
+// Output wave, chunk c, after barrier c + 1: o = QD S + Mqk delta, stored as bf16. `nxt` is
+// the record two chunks ahead.
 template <int K, int V>
 __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V> &nxt,
-                                           const Chunk32<K, V> &nxt2, Handoff32<K> &ho, int par,
-                                           int lane, __amdgpu_buffer_rsrc_t orows,
-                                           const int (&ooff)[8])
+                                           const Handoff32<K> &ho, int slot, int par, int lane,
+                                           __amdgpu_buffer_rsrc_t orows, const int (&ooff)[8])
 {
     constexpr int NS = K / 32;
-    release_lds();
-    __builtin_amdgcn_s_barrier();
-    acquire_lds();
+    lds_barrier();
     f16x8 Sh[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) Sh[st] = ho.sh[par][st][lane];
+    for (int st = 0; st < NS; ++st) Sh[st] = ho.sh[slot][st][lane];
     const f16x4 dh0 = ho.dh[par][0][lane], dh1 = ho.dh[par][1][lane];
-    stage_eg<K>(f.eg, ho, par, lane);
     f32x4 Y0 = zero4(), Y1 = zero4();
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -202,7 +274,7 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
     }
     const f32x4 O0 = mfma16(f.mqa, dh0, Y0);
     const f32x4 O1 = mfma32(f.mqb, cat(dh0, dh1), Y1);
-    nxt.load_out(f, nxt2);
+    nxt.load_out(f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const __bf16 b0 = (__bf16)O0[i], b1 = (__bf16)O1[i];
@@ -215,18 +287,24 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
 
 }  // namespace
 
-// Barrier schedule (nc chunks, both waves pass nc + 1 barriers): an initial one after the
-// output wave has staged exp(gam) of chunks 0 and 1, then one per chunk c after the chain wave
-// has written the hand-off of chunk c. Between barriers c and c+1 the output wave reads the
-// hand-off slot c % 2 and overwrites the exp(gam) slot c % 2 with chunk c+2, while the chain
-// wave reads exp(gam) slot (c+1) % 2 and writes the hand-off slot (c+1) % 2.
+// Barrier schedule for nc chunks: every wave passes nc + 1 barriers. Barrier c (c < nc)
+// follows the chain waves' hand-off of chunk c (fp16 rows of S in slot c % 3, the W S
+// partials in slot c % 2); between barriers c and c+1 the chain waves form delta_c (half 0
+// writes it to slot c % 2) and update S, then write chunk c+1's hand-off; the output wave,
+// after barrier c+1, reads the fp16 rows and delta_c. The fp16 rows are rewritten three
+// chunks later (after barrier c+2), the partials and delta two chunks later (after barrier
+// c+1 and c+2 respectively), each after its readers are done. The chain waves pass barrier nc
+// after their last update.
 template <int K, int V>
-__global__ __launch_bounds__(128) void state32_bf16_kernel(FwdParams p)
+__global__ __launch_bounds__(192) void state32_bf16_kernel(FwdParams p)
 {
-    constexpr int NK = K / 16, NV = V / 16, CT = 32;
+    constexpr int NV = V / 16, CT = 32;
     using WS = WsBf16x32<K, V>;
     __shared__ Handoff32<K> ho;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform per wave; readfirstlane makes that visible to the compiler,
+    // so field offsets derived from it stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, n = lane & 15;
     int unit, slice;
     if (!state_unit32(blockIdx.x, NV, p.seq.N * p.HV, &unit, &slice)) return;
@@ -244,43 +322,9 @@ __global__ __launch_bounds__(128) void state32_bf16_kernel(FwdParams p)
     };
 
     if (wave == 0) {
-        f32x4 S[NK];
-        if (p.h0) {
-            const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + col;
-#pragma unroll
-            for (int t = 0; t < NK; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][i] = h0[(size_t)(16 * t + 4 * grp + i) * V];
-        } else {
-#pragma unroll
-            for (int t = 0; t < NK; ++t) S[t] = zero4();
-        }
-        if (nc > 0) {
-            ChainFrag32<K, V> fa, fb;
-            at(0).load_w(fa); at(0).load_kreg(fa);
-            at(1).load_w(fb); at(1).load_kreg(fb);
-            // drain the prologue loads: the loop header then carries only the loop's own
-            // pending loads, and the waits inside the loop count back to the right group
-            vm_drain();
-            __builtin_amdgcn_s_barrier();     // exp(gam) of chunks 0 and 1 staged
-            acquire_lds();
-            // no exit between the loop body's two steps: an exit there would merge a
-            // half-step state into the loop header and make every iteration wait for the
-            // loads just issued
-            int c = 0;
-            for (; c + 2 <= nc; c += 2) {
-                chain_step32<K, V>(fa, at(c + 2), S, ho, 0, lane, grp);
-                chain_step32<K, V>(fb, at(c + 3), S, ho, 1, lane, grp);
-            }
-            if (c < nc) chain_step32<K, V>(fa, at(c + 2), S, ho, 0, lane, grp);
-        }
-        if (p.ht) {
-            float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
-#pragma unroll
-            for (int t = 0; t < NK; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ht[(size_t)(16 * t + 4 * grp + i) * V] = S[t][i];
-        }
+        chain_wave<K, V, 0>(p, ho, base, nc, s, j, col, slice, lane);
+    } else if (wave == 1) {
+        chain_wave<K, V, 1>(p, ho, base, nc, s, j, col, slice, lane);
     } else if (nc > 0) {
         const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)j * V * 2;
         int ooff[8];
@@ -295,22 +339,16 @@ __global__ __launch_bounds__(128) void state32_bf16_kernel(FwdParams p)
             return rows_rsrc(p.o, r0, (int)(nv < CT ? nv : CT), row_bytes, head_bytes);
         };
         OutFrag32<K, V> fa, fb;
-        float eg0[K / 64], eg1[K / 64];
-        at(0).load_eg(eg0);
-        at(1).load_eg(eg1);
-        at(0).load_out(fa, at(2));
-        at(1).load_out(fb, at(3));
+        at(0).load_out(fa);
+        at(1).load_out(fb);
         vm_drain();
-        stage_eg<K>(eg0, ho, 0, lane);
-        stage_eg<K>(eg1, ho, 1, lane);
-        release_lds();
-        __builtin_amdgcn_s_barrier();         // initial barrier: exp(gam) of chunks 0 and 1
+        lds_barrier();        // barrier 0
         int c = 0;
         for (; c + 2 <= nc; c += 2) {
-            out_step32<K, V>(fa, at(c + 2), at(c + 4), ho, 0, lane, rows(c), ooff);
-            out_step32<K, V>(fb, at(c + 3), at(c + 5), ho, 1, lane, rows(c + 1), ooff);
+            out_step32<K, V>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff);
+            out_step32<K, V>(fb, at(c + 3), ho, (c + 1) % 3, 1, lane, rows(c + 1), ooff);
         }
-        if (c < nc) out_step32<K, V>(fa, at(c + 2), at(c + 4), ho, 0, lane, rows(c), ooff);
+        if (c < nc) out_step32<K, V>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff);
     }
 }
 
@@ -320,7 +358,7 @@ hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st)
     const int64_t units = (int64_t)p.seq.N * p.HV;
     const int64_t nblk = (units + 7) / 8 * 8 * (V / 16);
     if (nblk == 0) return hipSuccess;
-    state32_bf16_kernel<K, V><<<dim3((unsigned)nblk), dim3(128), 0, st>>>(p);
+    state32_bf16_kernel<K, V><<<dim3((unsigned)nblk), dim3(192), 0, st>>>(p);
     return hipGetLastError();
 }
 
