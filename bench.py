@@ -17,6 +17,7 @@ Extra fields beyond the driver contract:
 from __future__ import annotations
 
 import argparse
+import re
 import hashlib
 import glob
 import json
@@ -115,12 +116,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
             raise SystemExit(f"no calibration copy kernel in {d}")
         scale = copy_bytes / statistics.mean(copy[0])
         for k, v in vals.items():
-            for short in ("prepare", "state"):
-                if f"kda::{short}_" in k:
-                    e = res.setdefault(f"kda_{short}", {})
-                    e[counter.lower() + "_raw_bytes"] = statistics.mean(v)
-                    e[counter.lower() + "_scale"] = round(scale, 4)
-                    e[counter.lower() + "_bytes"] = statistics.mean(v) * scale
+            m = re.search(r"kda::(prepare|state)(?:32)?_", k)
+            if m:
+                e = res.setdefault(f"kda_{m.group(1)}", {})
+                e[counter.lower() + "_raw_bytes"] = statistics.mean(v)
+                e[counter.lower() + "_scale"] = round(scale, 4)
+                e[counter.lower() + "_bytes"] = statistics.mean(v) * scale
+                e["kernel_name"] = k
     for k, e in res.items():
         e["hbm_bytes_per_launch"] = e["fetch_size_bytes"] + e["write_size_bytes"]
         e.update(kernel=k, workload=workload, source_digest=source_digest(), command=command)

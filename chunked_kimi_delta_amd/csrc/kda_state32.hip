@@ -129,15 +129,14 @@ struct Handoff32 {
 };
 
 // Chain wave h, one 32-token chunk c (S = its rows of the state at the chunk start), up to
-// and including barrier c: fp16 rows to the hand-off, the partial of W S to the other half,
-// then the decay of its rows; the W / exp(gam) / -U group of `f` is refilled from `nxt` (two
-// chunks ahead).
+// and including barrier c: fp16 rows to the hand-off and the partial of W S to the other half.
+// Nothing else precedes the barrier, so both halves reach it as early as their products allow.
 template <int K, int V, int h>
-__device__ __forceinline__ void chain_half_a(HalfFrag<K, V> &f, const Chunk32<K, V> &nxt,
-                                             f32x4 (&S)[K / 32], f32x4 &Xa, f32x4 &Xb,
-                                             Handoff32<K> &ho, int slot, int par, int lane)
+__device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, const f32x4 (&S)[K / 32],
+                                             f32x4 &Xa, f32x4 &Xb, Handoff32<K> &ho, int slot,
+                                             int par, int lane)
 {
-    constexpr int NSH = K / 64, NKH = K / 32;
+    constexpr int NSH = K / 64;
     if constexpr (h == 0) {
         Xa = f.nu[0];
         Xb = f.nu[1];
@@ -154,16 +153,13 @@ __device__ __forceinline__ void chain_half_a(HalfFrag<K, V> &f, const Chunk32<K,
     }
     ho.xp[par][h][0][lane] = Xa;
     ho.xp[par][h][1][lane] = Xb;
-#pragma unroll
-    for (int t = 0; t < NKH; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
-    nxt.template load_w<h>(f);
     lds_barrier();
 }
 
-// Chain wave h after barrier c: delta = -(own partial + other partial) (half 0 hands it to the
-// output wave), then the update of its rows; the KR^T group is refilled from `nxt`.
+// Chain wave h after barrier c: the other half's partial is read first, and its LDS latency
+// is covered by the decay of this half's rows and the refill of the W / exp(gam) / -U group
+// from `nxt` (two chunks ahead); then delta = -(own partial + other partial) (half 0 hands it
+// to the output wave) and the update of its rows; the KR^T group is refilled last.
 template <int K, int V, int h>
 __device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, const Chunk32<K, V> &nxt,
                                              f32x4 (&S)[K / 32], f32x4 Xa, f32x4 Xb,
@@ -171,6 +167,11 @@ __device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, const Chunk32<K,
 {
     constexpr int NKH = K / 32;
     const f32x4 Pa = ho.xp[par][1 - h][0][lane], Pb = ho.xp[par][1 - h][1][lane];
+#pragma unroll
+    for (int t = 0; t < NKH; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
+    nxt.template load_w<h>(f);
     f16x4 dh0, dh1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -195,7 +196,7 @@ __device__ __forceinline__ void chain_step(HalfFrag<K, V> &f, const Chunk32<K, V
                                            int par, int lane)
 {
     f32x4 Xa, Xb;
-    chain_half_a<K, V, h>(f, nxt, S, Xa, Xb, ho, c % 3, par, lane);
+    chain_half_a<K, V, h>(f, S, Xa, Xb, ho, c % 3, par, lane);
     chain_half_b<K, V, h>(f, nxt, S, Xa, Xb, ho, par, lane);
 }
 
@@ -258,7 +259,8 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
 template <int K, int V>
 __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V> &nxt,
                                            const Handoff32<K> &ho, int slot, int par, int lane,
-                                           __amdgpu_buffer_rsrc_t orows, const int (&ooff)[8])
+                                           __amdgpu_buffer_rsrc_t orows, const int (&ooff)[2],
+                                           bf16x4 Ib)
 {
     constexpr int NS = K / 32;
     lds_barrier();
@@ -275,14 +277,13 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
     const f32x4 O0 = mfma16(f.mqa, dh0, Y0);
     const f32x4 O1 = mfma32(f.mqb, cat(dh0, dh1), Y1);
     nxt.load_out(f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 b0 = (__bf16)O0[i], b1 = (__bf16)O1[i];
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b0), orows, ooff[i],
-                                              0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b1), orows,
-                                              ooff[4 + i], 0, 0);
-    }
+    // C(O) holds four rows of one column per lane; the identity product C(O^T) holds four
+    // consecutive columns of one row, so each block goes out as one 8-byte store per lane (the
+    // values are bf16 already, so the product changes none of them)
+    const bf16x4 T0 = to_bf16x4(mfma16(to_bf16x4(O0), Ib, zero4()));
+    const bf16x4 T1 = to_bf16x4(mfma16(to_bf16x4(O1), Ib, zero4()));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T0), orows, ooff[0], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T1), orows, ooff[1], 0, 0);
 }
 
 }  // namespace
@@ -327,12 +328,15 @@ __global__ __launch_bounds__(192) void state32_bf16_kernel(FwdParams p)
         chain_wave<K, V, 1>(p, ho, base, nc, s, j, col, slice, lane);
     } else if (nc > 0) {
         const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)j * V * 2;
-        int ooff[8];
+        // after the transposing product lane (g, n) holds row n (block a) / 16 + n (block b),
+        // columns 16 slice + 4g .. + 3
+        const int ocol = 16 * slice + 4 * grp;
+        const int ooff[2] = {(int)(n * row_bytes + ocol * 2),
+                             (int)((16 + n) * row_bytes + ocol * 2)};
+        float eye[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ooff[i] = (int)((4 * grp + i) * row_bytes + col * 2);
-            ooff[4 + i] = (int)((16 + 4 * grp + i) * row_bytes + col * 2);
-        }
+        for (int i = 0; i < 4; ++i) eye[i] = 4 * grp + i == n ? 1.f : 0.f;
+        const bf16x4 Ib = to_bf16x4(eye);
         auto rows = [&](int c) {
             const int64_t r0 = bos + CT * c;
             const int64_t nv = eos - r0;
@@ -345,10 +349,10 @@ __global__ __launch_bounds__(192) void state32_bf16_kernel(FwdParams p)
         lds_barrier();        // barrier 0
         int c = 0;
         for (; c + 2 <= nc; c += 2) {
-            out_step32<K, V>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff);
-            out_step32<K, V>(fb, at(c + 3), ho, (c + 1) % 3, 1, lane, rows(c + 1), ooff);
+            out_step32<K, V>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff, Ib);
+            out_step32<K, V>(fb, at(c + 3), ho, (c + 1) % 3, 1, lane, rows(c + 1), ooff, Ib);
         }
-        if (c < nc) out_step32<K, V>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff);
+        if (c < nc) out_step32<K, V>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff, Ib);
     }
 }
 
