@@ -21,6 +21,17 @@ def pytest_runtest_logstart(nodeid, location):
         sys.__stderr__.flush()
 
 
+def pytest_runtest_logreport(report):
+    # errors a GPU test measured (tests/errlog.py), after its call phase
+    if report.when != "call":
+        return
+    import errlog
+    for line in errlog.PENDING:
+        sys.__stderr__.write(line + "\n")
+    sys.__stderr__.flush()
+    errlog.PENDING.clear()
+
+
 def pytest_collection_modifyitems(config, items):
     gpu_items = [it for it in items if it.get_closest_marker("gpu")]
     if not gpu_items:

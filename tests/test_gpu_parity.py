@@ -16,6 +16,7 @@ import torch
 import workloads as W
 from oracle.chunked import chunk_prepare
 from oracle.native import kda_oracle_c
+from errlog import report
 from ws_decode import chunk_bytes, chunk_bytes32, decode_chunk, decode_chunk32
 
 import chunked_kimi_delta_amd as kda
@@ -68,6 +69,7 @@ def o_flat(o, inp):
 def check_all(inp, o, fin, o_ref, f_ref, tol):
     assert np.isfinite(o).all() and np.isfinite(fin).all()
     eo, ef = rel_l2(o, o_ref), rel_l2(fin, f_ref)
+    report(eo, ef)
     assert eo <= tol and ef <= tol, f"rel L2 o={eo:.3e} final={ef:.3e} > {tol}"
     return eo, ef
 
@@ -246,4 +248,5 @@ def test_full_size_sampled_parity(name, chunk):
         got_f.append(fin[s, j]); ref_f.append(f_ref[s, j])
     eo = rel_l2(np.concatenate(got_o), np.concatenate(ref_o))
     ef = rel_l2(np.stack(got_f), np.stack(ref_f))
+    report(eo, ef)
     assert eo <= TOL[w.dtype] and ef <= TOL[w.dtype], f"rel L2 o={eo:.3e} final={ef:.3e}"
