@@ -87,10 +87,11 @@ struct WsBf16 {
 //   W    [2 blocks][K/32][64][8] fp16   W rows of each block in TPL (as WsBf16::W)
 //   QD   [2][K/32][64][8]        fp16
 //   KR   [K/16][64][8]           fp16   KR^T tile t as a 16x16x32 A operand over the 32 tokens
-//   NU   [2][V/16][64][4]        fp32   -U rows of each block, C-layout per 16-column slice
-//                                       (negated and fp32: it is the accumulator the state
-//                                       kernel starts W S from, so delta = -(W S - U) costs no
-//                                       VALU work)
+//   NU   [V/16][64][8]           fp16   -U in C-layout per 16-column slice, block a in
+//                                       elements 0..3 and block b in 4..7 of each lane's 16
+//                                       bytes (negated: the state kernel starts its W S
+//                                       accumulator from it, so delta = -(W S - U) needs no
+//                                       subtraction)
 //   MQKA [64][4]                 fp16   Mqk_aa in A16-layout
 //   MQKB [64][8]                 fp16   [Mqk_ba | Mqk_bb] as a 16x16x32 A operand
 //   EG   [K]                     fp32   exp(gamma) of the whole 32-token chunk
@@ -100,7 +101,7 @@ struct WsBf16x32 {
     static constexpr int QD = W + 64 * K;
     static constexpr int KR = QD + 64 * K;
     static constexpr int NU = KR + 64 * K;
-    static constexpr int MQKA = NU + 128 * V;
+    static constexpr int MQKA = NU + 64 * V;
     static constexpr int MQKB = MQKA + 512;
     static constexpr int EG = MQKB + 1024;
     static constexpr int END = EG + 4 * K;

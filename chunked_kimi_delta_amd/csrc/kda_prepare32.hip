@@ -12,7 +12,7 @@
 //           substitution; every factor stays as bounded as the inverse itself)
 //     A   = X diag(beta),  W = A (k e^{Gam}),  U = A v,  QD = scale q e^{Gam},
 //     KR  = k e^{gam - Gam},  Mqk = tril(QD' . KI'^T) (32 x 32),  e^{gam}
-// (U is stored negated in fp32, see WsBf16x32)
+// (U is stored negated, see WsBf16x32)
 // which is the chunk half of naive_chunk_kda ("手撕KDA" section 1) for a 32-token chunk.
 //
 // The per-block work is the 16-token kernel of kda_prepare.hip (same layouts, same numerics:
@@ -310,7 +310,8 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
                     to_f16x4(mfma16(kdC[2 * st + 1], ATb, zero4())));
 #pragma unroll
         for (int c = 0; c < NV; ++c)
-            *(f32x4 *)(ws + WS::NU + (c * 64 + lane) * 16) = -mfma16(ATb, vC[c], zero4());
+            *(f16x4 *)(ws + WS::NU + (c * 64 + lane) * 16) =
+                to_f16x4(-mfma16(ATb, vC[c], zero4()));
         *(f16x4 *)(ws + WS::MQKA + lane * 8) = MqT;
     } else {
 #pragma unroll
@@ -331,8 +332,8 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
                                     zero4())));
 #pragma unroll
         for (int c = 0; c < NV; ++c)
-            *(f32x4 *)(ws + WS::NU + ((NV + c) * 64 + lane) * 16) =
-                -mfma32(Arow, cat(sh.a.cols.vc[c][lane], vC[c]), zero4());
+            *(f16x4 *)(ws + WS::NU + (c * 64 + lane) * 16 + 8) =
+                to_f16x4(-mfma32(Arow, cat(sh.a.cols.vc[c][lane], vC[c]), zero4()));
         const f16x4 MqbaT = to_f16x4(mfma16(to_f16x4(Mba), Ih, zero4()));  // C(Mqk_ba^T)
         *(f16x8 *)(ws + WS::MQKB + lane * 16) = cat(MqbaT, MqT);
     }

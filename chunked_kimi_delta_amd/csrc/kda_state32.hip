@@ -63,7 +63,7 @@ struct HalfFrag {
     f16x8 w[2][NSH];          // W rows of blocks a and b, this half's columns
     f16x8 kr[NKH];            // KR^T tiles of this half over the 32 tokens
     f32x4 eg[NKH];            // exp(gam) of the four rows 16t + 4g + i each lane holds
-    f32x4 nu[2];              // -U of blocks a and b (half 0 only)
+    f16x8 nu;                 // -U of blocks a (0..3) and b (4..7), this slice (half 0 only)
 };
 
 template <int K, int V>
@@ -95,12 +95,8 @@ struct Chunk32 {
         for (int t = 0; t < NKH; ++t)
             f.eg[t] = __builtin_bit_cast(
                 f32x4, bload16(rs, grp * 16, WS::EG + (h * NKH + t) * 64));
-        if constexpr (h == 0) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                f.nu[b] = __builtin_bit_cast(f32x4, bload16(rs, lane * 16,
-                                                            WS::NU + (b * NV + slice) * 1024));
-        }
+        if constexpr (h == 0)
+            f.nu = __builtin_bit_cast(f16x8, bload16(rs, lane * 16, WS::NU + slice * 1024));
     }
     template <int h>
     __device__ __forceinline__ void load_kreg(HalfFrag<K, V> &f) const {
@@ -138,8 +134,11 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, const f32x
 {
     constexpr int NSH = K / 64;
     if constexpr (h == 0) {
-        Xa = f.nu[0];
-        Xb = f.nu[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Xa[i] = (float)f.nu[i];
+            Xb[i] = (float)f.nu[4 + i];
+        }
     } else {
         Xa = zero4();
         Xb = zero4();

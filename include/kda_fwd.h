@@ -87,7 +87,7 @@ typedef struct {
 /* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
    Returns 0 for arguments kda_fwd would reject. The workspace holds the prepare kernel's
    per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma)) for ceil-bounded chunk slots of every
-   value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16) or 43,008 B (chunk 32) at
+   value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16) or 34,816 B (chunk 32) at
    bf16 io and K = V = 128. */
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
 

@@ -59,10 +59,10 @@ def test_workspace_bytes(lib):
     assert f(args(io=1)) == (4096 // 16 + 1) * 16 * 34304
     assert f(args(B=4, T=8192, N=4, H=16, HV=32)) == (4 * 8192 // 16 + 4) * 32 * 17408
     assert f(args(T=45, N=1)) == (45 // 16 + 1) * 16 * 17408
-    assert f(args(chunk=32)) == (4096 // 32 + 1) * 16 * 43008
+    assert f(args(chunk=32)) == (4096 // 32 + 1) * 16 * 34816
     assert f(args(chunk=0)) == f(args(chunk=32))          # bf16 default: 32-token chunks
     assert f(args(io=1, chunk=0)) == f(args(io=1, chunk=16))
-    assert f(args(chunk=32, T=45)) == (45 // 32 + 1) * 16 * 43008
+    assert f(args(chunk=32, T=45)) == (45 // 32 + 1) * 16 * 34816
     assert f(args(io=1, chunk=32)) == 0                   # fp32 io: 16-token chunks only
     assert f(args(chunk=64)) == 0
     assert f(args(K=96)) == 0          # unsupported head dim

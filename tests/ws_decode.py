@@ -58,7 +58,7 @@ def decode_chunk(raw: np.ndarray, K: int, V: int):
 
 
 def chunk_bytes32(K, V):
-    end = 64 * K * 3 + 128 * V + 512 + 1024 + 4 * K
+    end = 64 * K * 3 + 64 * V + 512 + 1024 + 4 * K
     return (end + 255) // 256 * 256
 
 
@@ -88,14 +88,14 @@ def decode_chunk32(raw: np.ndarray, K: int, V: int):
             X[tokv, 16 * t + m] = frag[t, :, e]
     out["kr"] = X
     off += 64 * K
-    frag = -raw[off:off + 128 * V].view(np.float32).astype(np.float64).reshape(2, NV, 64, 4)
+    frag = -h16(off, off + 64 * V).reshape(NV, 64, 8)
     X = np.full((32, V), np.nan)
     for b in range(2):
         for c in range(NV):
             for i in range(4):
-                X[16 * b + 4 * g + i, 16 * c + m] = frag[b, c, :, i]
-    out["u"] = X                       # stored negated, fp32
-    off += 128 * V
+                X[16 * b + 4 * g + i, 16 * c + m] = frag[c, :, 4 * b + i]
+    out["u"] = X                       # stored negated
+    off += 64 * V
     M = np.zeros((32, 32))
     fa = h16(off, off + 512).reshape(64, 4)
     for i in range(4):
