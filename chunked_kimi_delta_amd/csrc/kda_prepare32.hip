@@ -25,87 +25,122 @@ namespace kda {
 
 template <int K, int V>
 struct Prep32Share {
+    static constexpr int MAXKV = K > V ? K : V;
+    static constexpr int STAGE = 16 * (2 * MAXKV + 16);   // one block's 16 rows, padded
     float tot_a[K];              // Gam (log2 units) at the last token of block a
     float tot_ab[K];             // Gam at the last token of the chunk
     bf16x8 kih[K / 32][64];      // block a: k e^{ref - Gam}, hi part, 16x16x32 B operand
     bf16x8 kil[K / 32][64];      //          lo part
     f32x4 xaa[64];               // C(X_aa)
     float beta_a[16];
-    f32x4 g2b[K / 16][64];       // block b: Gam in TPL, one tile per entry
-    union {                      // block a: its Gam tiles, then (once both of its factor
-        f32x4 g2a[K / 16][64];   // phases are done) its column-per-lane KD and V tiles
+    union {
         struct {
-            bf16x4 kdc[K / 16][64];
-            bf16x4 vc[V / 16][64];
-        } cols;
-    } a;
+            f32x4 g2b[K / 16][64];       // block b: Gam in TPL, one tile per entry
+            union {                      // block a: its Gam tiles, then (once both of its
+                f32x4 g2a[K / 16][64];   // factor phases are done) its column-per-lane KD
+                struct {                 // and V tiles
+                    bf16x4 kdc[K / 16][64];
+                    bf16x4 vc[V / 16][64];
+                } cols;
+            } a;
+        } ph;
+        uint8_t stage[2][STAGE];         // per block: input rows on their way to TPL (first)
+    } u;
     __device__ __forceinline__ f32x4 &g2(int wave, int c, int lane) {
-        return wave == 0 ? a.g2a[c][lane] : g2b[c][lane];
+        return wave == 0 ? u.ph.a.g2a[c][lane] : u.ph.g2b[c][lane];
     }
 };
 
+// Inputs of one 32-token chunk as each lane loads them: the 16 rows of its block (wave)
+// row-contiguously, 16 bytes per lane (row RPI u + lane / CPR, 8 columns from 8 (lane % CPR)),
+// so that every quarter-wave reads one or two whole cache lines.
 template <int K, int V>
-__global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
+struct Prep32In {
+    u32x4 q[K / 32], k[K / 32], g[K / 32], v[V / 32];
+    float beta;
+};
+
+template <int RL>
+__device__ __forceinline__ void load_rows(const uint16_t *base, int64_t row_elems, int nrows,
+                                          int lane, u32x4 (&x)[RL / 32])
+{
+    constexpr int CPR = RL / 8, RPI = 64 / CPR;     // 16-byte chunks per row, rows per load
+#pragma unroll
+    for (int u = 0; u < RL / 32; ++u) {
+        const int row = RPI * u + lane / CPR, chunk = lane % CPR;
+        x[u] = row < nrows ? *(const u32x4 *)(base + row * row_elems + 8 * chunk)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int K, int V>
+__device__ __forceinline__ void prep32_load(const FwdParams &p, int64_t bos, int nvalid, int j,
+                                            int wave, int lane, Prep32In<K, V> &in)
+{
+    const int r = lane & 15;
+    const int64_t tok0 = bos + 16 * wave;
+    const int nrows = nvalid - 16 * wave;           // valid rows of this block (may be <= 0)
+    const int h = j / p.G;
+    load_rows<K>((const uint16_t *)p.g + (tok0 * p.HV + j) * K, (int64_t)p.HV * K, nrows, lane,
+                 in.g);
+    load_rows<K>((const uint16_t *)p.k + (tok0 * p.H + h) * K, (int64_t)p.H * K, nrows, lane,
+                 in.k);
+    load_rows<K>((const uint16_t *)p.q + (tok0 * p.H + h) * K, (int64_t)p.H * K, nrows, lane,
+                 in.q);
+    load_rows<V>((const uint16_t *)p.v + (tok0 * p.HV + j) * V, (int64_t)p.HV * V, nrows, lane,
+                 in.v);
+    in.beta = r < nrows ? bf16_bits_to_f32(((const uint16_t *)p.beta)[(tok0 + r) * p.HV + j])
+                        : 0.f;
+}
+
+// Row-contiguous input rows -> TPL (lane (g, r): row r, columns 16c + 4g .. + 3) through this
+// wave's LDS stage. The row stride is padded by 16 bytes, so the 16 rows read by a quarter-wave
+// fall in distinct banks. Only this wave touches its stage, and one wave's LDS accesses are
+// performed in order.
+template <int RL>
+__device__ __forceinline__ void rows_to_tpl(const u32x4 (&x)[RL / 32], uint2 (&out)[RL / 16],
+                                            uint8_t *stage, int lane)
+{
+    constexpr int CPR = RL / 8, RPI = 64 / CPR, STRIDE = 2 * RL + 16;
+#pragma unroll
+    for (int u = 0; u < RL / 32; ++u)
+        *(u32x4 *)(stage + (RPI * u + lane / CPR) * STRIDE + 16 * (lane % CPR)) = x[u];
+    const int grp = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int c = 0; c < RL / 16; ++c)
+        out[c] = *(const uint2 *)(stage + r * STRIDE + 32 * c + 8 * grp);
+}
+
+// One 32-token chunk of one value head from its loaded inputs; both waves of the workgroup
+// call it together (it synchronises the workgroup).
+template <int K, int V>
+__device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, V> &sh,
+                                             const Prep32In<K, V> &in, uint8_t *ws, int wave,
+                                             int lane)
 {
     constexpr int NK = K / 16, NV = V / 16, NS = K / 32;
     using WS = WsBf16x32<K, V>;
-    __shared__ Prep32Share<K, V> sh;
-
-    const int wave = threadIdx.x >> 6;      // row block: 0 = a, 1 = b
-    const int lane = threadIdx.x & 63;
     const int grp = lane >> 4;
     const int r = lane & 15;                 // TPL: token row in the block; C-layout: column
-    const int slot = blockIdx.x;
-    const int j = blockIdx.y;
-    const int h = j / p.G;
-
-    int s;
-    int64_t bos;
-    int nvalid;
-    if (!locate_slot<32>(p.seq, slot, &s, &bos, &nvalid)) return;   // whole workgroup
-    const int row = 16 * wave + r;
-    const bool live = row < nvalid;
-    const int64_t tok = bos + row;
-    uint8_t *ws = p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES;
-
-    // ---------------------------------------------------------------- loads (TPL, kept packed)
     // q, k and v stay as packed bf16 pairs until each use: every phase below rebuilds the fp32
-    // values it needs from them, which keeps the live register set small enough for two waves
-    // per SIMD.
-    uint2 qr[NK], kr[NK], vraw[NV];
+    // values it needs from them, which keeps the live register set small enough for several
+    // waves per SIMD.
+    uint2 qr[NK], kr[NK], gr[NK], vraw[NV];
+    uint8_t *stage = sh.u.stage[wave];
+    rows_to_tpl<K>(in.g, gr, stage, lane);
+    rows_to_tpl<K>(in.k, kr, stage, lane);
+    rows_to_tpl<K>(in.q, qr, stage, lane);
+    rows_to_tpl<V>(in.v, vraw, stage, lane);
+    const float beta_r = in.beta;
+
+    // ---------------------------------------------------------------- cumsum over 32 tokens
     float G2[NK][4];
-    float beta_r = 0.f;
 #pragma unroll
-    for (int c = 0; c < NK; ++c) { qr[c] = make_uint2(0u, 0u); kr[c] = make_uint2(0u, 0u); }
+    for (int c = 0; c < NK; ++c) {
+        float gl[4];
+        unpack_bf16x4(gr[c], gl);
 #pragma unroll
-    for (int c = 0; c < NV; ++c) vraw[c] = make_uint2(0u, 0u);
-    {
-        uint2 gr[NK];
-#pragma unroll
-        for (int c = 0; c < NK; ++c) gr[c] = make_uint2(0u, 0u);
-        if (live) {
-            const uint16_t *qp = (const uint16_t *)p.q + ((tok * p.H + h) * K + 4 * grp);
-            const uint16_t *kp = (const uint16_t *)p.k + ((tok * p.H + h) * K + 4 * grp);
-            const uint16_t *gp = (const uint16_t *)p.g + ((tok * p.HV + j) * K + 4 * grp);
-            const uint16_t *vp = (const uint16_t *)p.v + ((tok * p.HV + j) * V + 4 * grp);
-#pragma unroll
-            for (int c = 0; c < NK; ++c) {
-                gr[c] = *(const uint2 *)(gp + 16 * c);
-                kr[c] = *(const uint2 *)(kp + 16 * c);
-                qr[c] = *(const uint2 *)(qp + 16 * c);
-            }
-#pragma unroll
-            for (int c = 0; c < NV; ++c) vraw[c] = *(const uint2 *)(vp + 16 * c);
-            beta_r = bf16_bits_to_f32(((const uint16_t *)p.beta)[tok * p.HV + j]);
-        }
-        // ------------------------------------------------------------ cumsum over 32 tokens
-#pragma unroll
-        for (int c = 0; c < NK; ++c) {
-            float gl[4];
-            unpack_bf16x4(gr[c], gl);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[i] * LOG2E);
-        }
+        for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[i] * LOG2E);
     }
     if (wave == 0) {
         if (r == 15) {
@@ -186,7 +221,7 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
         if (wave == 1 && r == 15) {
 #pragma unroll
             for (int c = 0; c < NK; ++c) {
-                const f32x4 gc = sh.g2b[c][lane];
+                const f32x4 gc = sh.u.ph.g2b[c][lane];
                 float4 e;
                 e.x = __builtin_amdgcn_exp2f(gc[0]);
                 e.y = __builtin_amdgcn_exp2f(gc[1]);
@@ -290,9 +325,9 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
         vC[c] = to_bf16x4(mfma16(__builtin_bit_cast(bf16x4, vraw[c]), Ib, zero4()));
     if (wave == 0) {
 #pragma unroll
-        for (int c = 0; c < NK; ++c) sh.a.cols.kdc[c][lane] = kdC[c];
+        for (int c = 0; c < NK; ++c) sh.u.ph.a.cols.kdc[c][lane] = kdC[c];
 #pragma unroll
-        for (int c = 0; c < NV; ++c) sh.a.cols.vc[c][lane] = vC[c];
+        for (int c = 0; c < NV; ++c) sh.u.ph.a.cols.vc[c][lane] = vC[c];
     }
     __syncthreads();
 
@@ -327,22 +362,47 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
 #pragma unroll
         for (int st = 0; st < NS; ++st)
             *(f16x8 *)(ws + WS::W + ((NS + st) * 64 + lane) * 16) =
-                cat(to_f16x4(mfma32(cat(sh.a.cols.kdc[2 * st][lane], kdC[2 * st]), Arow, zero4())),
-                    to_f16x4(mfma32(cat(sh.a.cols.kdc[2 * st + 1][lane], kdC[2 * st + 1]), Arow,
+                cat(to_f16x4(mfma32(cat(sh.u.ph.a.cols.kdc[2 * st][lane], kdC[2 * st]), Arow, zero4())),
+                    to_f16x4(mfma32(cat(sh.u.ph.a.cols.kdc[2 * st + 1][lane], kdC[2 * st + 1]), Arow,
                                     zero4())));
 #pragma unroll
         for (int c = 0; c < NV; ++c)
             *(f16x4 *)(ws + WS::NU + (c * 64 + lane) * 16 + 8) =
-                to_f16x4(-mfma32(Arow, cat(sh.a.cols.vc[c][lane], vC[c]), zero4()));
+                to_f16x4(-mfma32(Arow, cat(sh.u.ph.a.cols.vc[c][lane], vC[c]), zero4()));
         const f16x4 MqbaT = to_f16x4(mfma16(to_f16x4(Mba), Ih, zero4()));  // C(Mqk_ba^T)
         *(f16x8 *)(ws + WS::MQKB + lane * 16) = cat(MqbaT, MqT);
     }
 }
 
+// Two chunk slots per workgroup: the second slot's inputs are loaded before the first slot is
+// processed, so their memory latency is covered by the first slot's work.
+template <int K, int V>
+__global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
+{
+    using WS = WsBf16x32<K, V>;
+    __shared__ Prep32Share<K, V> sh;
+    const int wave = threadIdx.x >> 6;      // row block: 0 = a, 1 = b
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.y;
+    const int slot0 = 2 * blockIdx.x, slot1 = slot0 + 1;
+    int s0 = 0, s1 = 0, nv0 = 0, nv1 = 0;
+    int64_t bos0 = 0, bos1 = 0;
+    // workgroup-uniform: every wave takes the same branches and barriers
+    const bool ok0 = slot0 < p.seq.n_slots && locate_slot<32>(p.seq, slot0, &s0, &bos0, &nv0);
+    const bool ok1 = slot1 < p.seq.n_slots && locate_slot<32>(p.seq, slot1, &s1, &bos1, &nv1);
+    Prep32In<K, V> in0, in1;
+    if (ok0) prep32_load<K, V>(p, bos0, nv0, j, wave, lane, in0);
+    if (ok1) prep32_load<K, V>(p, bos1, nv1, j, wave, lane, in1);
+    uint8_t *ws = p.ws + (size_t)j * p.seq.n_slots * (size_t)WS::BYTES;
+    if (ok0) prep32_chunk<K, V>(p, sh, in0, ws + (size_t)slot0 * WS::BYTES, wave, lane);
+    if (ok0 && ok1) __syncthreads();         // the shared block is reused by the second slot
+    if (ok1) prep32_chunk<K, V>(p, sh, in1, ws + (size_t)slot1 * WS::BYTES, wave, lane);
+}
+
 template <int K, int V>
 hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st)
 {
-    dim3 grid(p.seq.n_slots, p.HV);
+    dim3 grid((p.seq.n_slots + 1) / 2, p.HV);
     prepare32_bf16_kernel<K, V><<<grid, dim3(128), 0, st>>>(p);
     return hipGetLastError();
 }
