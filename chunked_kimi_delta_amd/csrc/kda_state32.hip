@@ -295,19 +295,27 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
 // chunks later (after barrier c+2), the partials and delta two chunks later (after barrier
 // c+1 and c+2 respectively), each after its readers are done. The chain waves pass barrier nc
 // after their last update.
-template <int K, int V>
-__global__ __launch_bounds__(192) void state32_bf16_kernel(FwdParams p)
+// SPW V-slices of one (sequence, value head) per workgroup, three waves each (two chain halves
+// and the output wave). With several slices per workgroup the slices pass their barriers
+// together and read each chunk record at the same time, so a record is fetched once per
+// workgroup instead of once per slice; with one slice per workgroup small launches spread over
+// more CUs.
+template <int K, int V, int SPW>
+__global__ __launch_bounds__(192 * SPW) void state32_bf16_kernel(FwdParams p)
 {
-    constexpr int NV = V / 16, CT = 32;
+    constexpr int NV = V / 16, NG = NV / SPW, CT = 32;
     using WS = WsBf16x32<K, V>;
-    __shared__ Handoff32<K> ho;
+    __shared__ Handoff32<K> hos[SPW];
     // the wave index is uniform per wave; readfirstlane makes that visible to the compiler,
     // so field offsets derived from it stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sw = wave / 3, role = wave % 3;
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, n = lane & 15;
-    int unit, slice;
-    if (!state_unit32(blockIdx.x, NV, p.seq.N * p.HV, &unit, &slice)) return;
+    int unit, group;
+    if (!state_unit32(blockIdx.x, NG, p.seq.N * p.HV, &unit, &group)) return;
+    const int slice = group * SPW + sw;
+    Handoff32<K> &ho = hos[sw];
     const int j = unit % p.HV;
     const int s = unit / p.HV;
     const int64_t bos = seq_bos(p.seq, s);
@@ -321,9 +329,9 @@ __global__ __launch_bounds__(192) void state32_bf16_kernel(FwdParams p)
                              lane, slice};
     };
 
-    if (wave == 0) {
+    if (role == 0) {
         chain_wave<K, V, 0>(p, ho, base, nc, s, j, col, slice, lane);
-    } else if (wave == 1) {
+    } else if (role == 1) {
         chain_wave<K, V, 1>(p, ho, base, nc, s, j, col, slice, lane);
     } else if (nc > 0) {
         const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)j * V * 2;
@@ -355,14 +363,28 @@ __global__ __launch_bounds__(192) void state32_bf16_kernel(FwdParams p)
     }
 }
 
+template <int K, int V, int SPW>
+static hipError_t launch_state32_spw(const FwdParams &p, hipStream_t st)
+{
+    const int64_t units = (int64_t)p.seq.N * p.HV;
+    const int64_t nblk = (units + 7) / 8 * 8 * (V / 16 / SPW);
+    if (nblk == 0) return hipSuccess;
+    state32_bf16_kernel<K, V, SPW><<<dim3((unsigned)nblk), dim3(192 * SPW), 0, st>>>(p);
+    return hipGetLastError();
+}
+
+// Slices per workgroup: 4 (2) once there are at least 4 (2) slice workgroups per CU to fill,
+// else 1.
 template <int K, int V>
 hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st)
 {
-    const int64_t units = (int64_t)p.seq.N * p.HV;
-    const int64_t nblk = (units + 7) / 8 * 8 * (V / 16);
-    if (nblk == 0) return hipSuccess;
-    state32_bf16_kernel<K, V><<<dim3((unsigned)nblk), dim3(192), 0, st>>>(p);
-    return hipGetLastError();
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t slice_wgs = (int64_t)p.seq.N * p.HV * (V / 16);
+    if (slice_wgs >= 4LL * cus) return launch_state32_spw<K, V, 4>(p, st);
+    if (slice_wgs >= 2LL * cus) return launch_state32_spw<K, V, 2>(p, st);
+    return launch_state32_spw<K, V, 1>(p, st);
 }
 
 #define KDA_INST(K, V) \

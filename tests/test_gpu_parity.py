@@ -88,6 +88,11 @@ SMALL = {
     "fp32_varlen_gva": W.custom(H=2, HV=4, K=128, V=128, dtype="fp32", h0_std=0.1,
                                 lengths=(5, 40, 0, 16)),
     "fp32_k64v128_t70": W.custom(B=2, T=70, H=1, HV=1, K=64, V=128, dtype="fp32"),
+    # enough (sequence, head, 16-column slice) units that the 32-token state kernel groups 2
+    # and 4 slices per workgroup (512 and 1024 slice units on a 256-CU part)
+    "bf16_b4_h16_t70_slices2": W.custom(B=4, T=70, H=8, HV=16, K=128, V=128, h0_std=0.1),
+    "bf16_b8_h16_t45_slices4": W.custom(B=8, T=45, H=16, HV=16, K=128, V=128),
+    "bf16_b16_h16_k64v64_slices4": W.custom(B=16, T=40, H=16, HV=16, K=64, V=64, h0_std=0.1),
 }
 
 
