@@ -55,7 +55,7 @@ def algorithmic_work(inp, C):
     prep_bytes = T_total * (H * 2 * K * es + HV * (V * es + K * es + es))
     state_bytes = T_total * HV * V * es + N * HV * K * V * 4 * (1 + (inp.h0 is not None))
     state_flops = n_chunk_heads * (6 * C * K * V + 2 * C * C * V + K * V)
-    inv_flops = (C // 16) * 6 * 2 * 16 ** 3 + (C // 16 - 1) * 2 * 2 * 16 ** 3
+    inv_flops = ((C // 16) * 6 * 2 * 16 ** 3 + (C // 16 - 1) * 2 * 2 * 16 ** 3) if C >= 16 else 0
     prep_flops = n_chunk_heads * (2 * C * C * (3 * K + V) + inv_flops)
     return dict(prep_bytes=prep_bytes, state_bytes=state_bytes, prep_flops=prep_flops,
                 state_flops=state_flops, n_chunk_heads=n_chunk_heads)
@@ -116,7 +116,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
             raise SystemExit(f"no calibration copy kernel in {d}")
         scale = copy_bytes / statistics.mean(copy[0])
         for k, v in vals.items():
-            m = re.search(r"kda::(prepare|state)(?:32)?_", k)
+            m = re.search(r"kda::(prepare|state|recurrent)(?:32)?_", k)
             if m:
                 e = res.setdefault(f"kda_{m.group(1)}", {})
                 e[counter.lower() + "_raw_bytes"] = statistics.mean(v)
@@ -267,7 +267,18 @@ def main():
                       "alg_bytes": work["state_bytes"], "alg_flops": work["state_flops"],
                       "achieved_TFLOPs": round(work["state_flops"] / (state_ms * 1e-3) / 1e12, 2)},
     }
-    if state_ms >= prep_ms:
+    if chunk == 1:
+        # the token recurrence is one kernel (the prepare launch is empty): everything it reads
+        # and writes (inputs, o, the states) is its algorithmic traffic
+        rb = work["prep_bytes"] + work["state_bytes"]
+        kernels = {"kda_recurrent": {"avg_ms": round(state_ms, 5), "bound": "hbm",
+                                     "alg_bytes": rb,
+                                     "achieved_GBs": round(rb / (state_ms * 1e-3) / 1e9, 1)}}
+        ach = rb / (state_ms * 1e-3) / 1e9
+        roof = {"kernel": "kda_recurrent", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 5),
+                "traffic": committed_traffic("kda_recurrent", w.name)}
+    elif state_ms >= prep_ms:
         ach = work["state_flops"] / (state_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[es]
         roof = {"kernel": "kda_state", "bound": "mfma", "achieved": round(ach, 3),
@@ -297,7 +308,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
                    "K": w.K, "V": w.V, "chunk": chunk, "tokens_per_step": inp.T_total,
                    "parallelism": "single-gpu",
-                   "arithmetic": "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse"},
+                   "arithmetic": ("fp32 VALU token recurrence" if chunk == 1 else
+                                  "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse")},
         "roofline": roof, "roofline_path": roof_path, "kernels": kernels,
         "cold_cache": cold, "cpu_baseline": cpu,
     }

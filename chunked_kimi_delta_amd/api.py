@@ -79,9 +79,11 @@ class KdaFwdPlan:
         self.args = a
         self._keep = (q, k, v, g, beta, cu_seqlens, initial_state)
         need = int(self.lib.kda_fwd_workspace_bytes(ctypes.byref(a)))
-        if need == 0 and B * T > 0:
+        # 0 means "rejected", except for chunk 1, which needs no workspace (its shape errors
+        # surface as the call's status)
+        if need == 0 and B * T > 0 and int(chunk) != 1:
             raise ValueError("unsupported shapes or chunk (K, V in {64, 128}; HV % H == 0; "
-                             "chunk 16, or 32 with bf16 io)")
+                             "chunk 1, 16, or 32 with bf16 io)")
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         elif workspace.numel() < need:

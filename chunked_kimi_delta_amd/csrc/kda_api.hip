@@ -41,12 +41,14 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_UNSUPPORTED;
     int ct = a->chunk;
     if (ct == 0) ct = a->io == KDA_BF16 ? 32 : 16;
-    if (ct != 16 && !(ct == 32 && a->io == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if (ct != 1 && ct != 16 && !(ct == 32 && a->io == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
     const int64_t tt = (int64_t)a->B * a->T;
     const int64_t ns = tt / ct + a->N;
     if (ns > INT32_MAX || (int64_t)a->HV > 65535) return KDA_ERR_UNSUPPORTED;
     size_t cb;
-    if (a->io == KDA_BF16)
+    if (ct == 1)
+        cb = 0;                      // the token-recurrent kernel needs no workspace
+    else if (a->io == KDA_BF16)
         cb = ct == 32 ? record_bytes<WsBf16x32>(a->K, a->V) : record_bytes<WsBf16>(a->K, a->V);
     else
         cb = record_bytes<WsF32>(a->K, a->V);
@@ -63,6 +65,8 @@ template <int K, int V>
 hipError_t dispatch(const FwdParams &p, int io, int chunk, int stages, hipStream_t st)
 {
     hipError_t e;
+    if (chunk == 1)     // token-recurrent: no prepare stage
+        return (stages & STAGE_STATE) ? launch_recurrent<K, V>(p, io, st) : hipSuccess;
     const bool prep = (stages & STAGE_PREPARE) && p.seq.T_total > 0;
     if (io == KDA_BF16 && chunk == 32) {
         if (prep && (e = launch_prepare32_bf16<K, V>(p, st)) != hipSuccess) return e;
@@ -93,7 +97,7 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     if (a->final_state && !aligned16(a->final_state)) return KDA_ERR_INVALID_ARG;
     if (a->cu_seqlens && !aligned16(a->cu_seqlens)) return KDA_ERR_INVALID_ARG;
     const size_t need = (size_t)ns * (size_t)a->HV * cb;
-    if (tt > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
+    if (tt > 0 && need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
         return KDA_ERR_WORKSPACE;
     if (a->N == 0) return KDA_OK;
 
@@ -163,13 +167,13 @@ const char *kda_strerror(int status)
     case KDA_OK: return "ok";
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED:
-        return "unsupported configuration (K, V in {64, 128}; chunk 16, or 32 with bf16 io)";
+        return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 with bf16 io)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
     }
 }
 
-int kda_version(void) { return 101; }
+int kda_version(void) { return 102; }
 
 }  // extern "C"

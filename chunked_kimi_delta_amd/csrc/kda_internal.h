@@ -287,4 +287,5 @@ template <int K, int V> hipError_t launch_prepare_f32(const FwdParams &p, hipStr
 template <int K, int V> hipError_t launch_state_f32(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_recurrent(const FwdParams &p, int io, hipStream_t st);
 }  // namespace kda

@@ -65,9 +65,10 @@ typedef struct {
     const void *v;            /* [B, T, HV, V]  io dtype                                    */
     const void *g;            /* [B, T, HV, K]  io dtype; per-key-dim decay in natural-log
                                  units (exp(g) multiplies the state). The chunked
-                                 factorisation needs every 16-token in-chunk sum of g to stay
-                                 above about -170 per key dim (fp32 exponent range); g <= 0 is
-                                 expected but not enforced.                                 */
+                                 factorisation needs the sum of g over any 8 (chunk 16) or 16
+                                 (chunk 32) consecutive tokens of a chunk to stay above about
+                                 -88 per key dim (fp32 exponent range); chunk 1 and fp32 io have
+                                 no such limit. g <= 0 is expected but not enforced.         */
     const void *beta;         /* [B, T, HV]     io dtype; used as given (no sigmoid)        */
     float scale;              /* output scale; <= 0 or NaN selects K^-0.5                   */
     const int64_t *cu_seqlens;/* device [N + 1] token offsets (cu[0] = 0, nondecreasing,
@@ -79,16 +80,18 @@ typedef struct {
     float *final_state;       /* [N, HV, K, V] fp32, or NULL to skip                        */
     int32_t chunk;            /* tokens per serial step of the state kernel: 16 (the FlashKDA
                                  tile of "KDA源码剖析之FlashKDA（上）"), 32 (two 16-token blocks
-                                 joined by block forward substitution; bf16 io only), or 0 for
-                                 the default (32 for bf16 io, 16 for fp32 io). Results agree to
-                                 rounding; 32 is faster.                                     */
+                                 joined by block forward substitution; bf16 io only), 1 (the
+                                 token recurrence itself, fp32 arithmetic, no workspace: for
+                                 decoding and other short sequences, where a chunk's fixed cost
+                                 dominates), or 0 for the default (32 for bf16 io, 16 for fp32
+                                 io). Results agree to rounding.                             */
 } kda_fwd_args;
 
 /* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
    Returns 0 for arguments kda_fwd would reject. The workspace holds the prepare kernel's
    per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma)) for ceil-bounded chunk slots of every
    value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16) or 34,816 B (chunk 32) at
-   bf16 io and K = V = 128. */
+   bf16 io and K = V = 128. Chunk 1 needs none (0; kda_fwd then accepts a NULL workspace). */
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
 
 /* Enqueue the forward: prepare kernel, then state kernel, on `stream` (hipStream_t or NULL).

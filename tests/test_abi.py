@@ -64,6 +64,7 @@ def test_workspace_bytes(lib):
     assert f(args(io=1, chunk=0)) == f(args(io=1, chunk=16))
     assert f(args(chunk=32, T=45)) == (45 // 32 + 1) * 16 * 34816
     assert f(args(io=1, chunk=32)) == 0                   # fp32 io: 16-token chunks only
+    assert f(args(chunk=1)) == 0 and f(args(io=1, chunk=1)) == 0   # recurrent: no workspace
     assert f(args(chunk=64)) == 0
     assert f(args(K=96)) == 0          # unsupported head dim
     assert f(args(HV=24, H=16)) == 0   # HV % H != 0
@@ -77,6 +78,9 @@ def test_workspace_bytes(lib):
     (dict(io=7), _lib.KDA_ERR_UNSUPPORTED),
     (dict(chunk=8), _lib.KDA_ERR_UNSUPPORTED),
     (dict(io=1, chunk=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=1, K=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=1, HV=24), _lib.KDA_ERR_INVALID_ARG),
+    (dict(chunk=1), _lib.KDA_ERR_INVALID_ARG),     # null tensor pointers, no workspace needed
     (dict(HV=24), _lib.KDA_ERR_INVALID_ARG),
     (dict(N=3), _lib.KDA_ERR_INVALID_ARG),
     (dict(T=-1), _lib.KDA_ERR_INVALID_ARG),
@@ -112,7 +116,7 @@ def test_strerror_and_version(lib):
     for st in range(5):
         assert kda._lib.strerror(st)
     assert "unknown" in kda._lib.strerror(99)
-    assert lib.kda_version() == 101
+    assert lib.kda_version() == 102
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):

@@ -97,7 +97,7 @@ SMALL = {
 
 
 # chunk lengths the library offers per io dtype (0 = its default)
-CHUNKS = {"bf16": [16, 32], "fp32": [16]}
+CHUNKS = {"bf16": [1, 16, 32], "fp32": [1, 16]}
 SMALL_CASES = [(n, c) for n in SMALL for c in CHUNKS[SMALL[n].dtype]]
 
 
@@ -110,7 +110,8 @@ def test_small_parity(name, chunk):
     check_all(inp, o, fin, o_ref, f_ref, TOL[w.dtype])
 
 
-@pytest.mark.parametrize("io,chunk", [("bf16", 16), ("bf16", 32), ("fp32", 16)])
+@pytest.mark.parametrize("io,chunk", [("bf16", 1), ("bf16", 16), ("bf16", 32), ("fp32", 1),
+                                      ("fp32", 16)])
 def test_empty_sequences_carry_initial_state(io, chunk):
     w = W.custom(B=2, T=0, H=1, HV=2, K=128, V=64, dtype=io, h0_std=1.0)
     inp = W.make_inputs(w, seed=3)
@@ -119,7 +120,7 @@ def test_empty_sequences_carry_initial_state(io, chunk):
     assert np.array_equal(fin, inp.h0.numpy().astype(np.float64))
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32])
 @pytest.mark.parametrize("case", ["beta0", "g0"])
 def test_degenerate_gates(case, chunk):
     w = W.custom(B=1, T=90, H=2, HV=2, K=128, V=128, h0_std=0.5)
@@ -134,7 +135,7 @@ def test_degenerate_gates(case, chunk):
         assert rel_l2(fin[0], np.exp(cum)[:, :, None] * S0[0]) <= 1e-3
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32])
 def test_deltanet_retrieval_property(chunk):
     # g = 0, beta = 1 and one fixed unit key shared by all tokens with q = k: each output
     # returns scale * v_t (the plain delta rule overwrites the memory slot every token)
@@ -156,7 +157,7 @@ def test_deltanet_retrieval_property(chunk):
     assert rel_l2(o[0, :, 0], 0.5 * nk2 * inp.v.float().numpy()[0, :, 0]) <= 2e-2
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32])
 def test_no_final_state_and_explicit_scale(chunk):
     w = W.custom(B=1, T=64, H=1, HV=2, K=128, V=128)
     inp = W.make_inputs(w, seed=2)
@@ -166,7 +167,7 @@ def test_no_final_state_and_explicit_scale(chunk):
     assert rel_l2(o, o_ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32])
 def test_deterministic_and_repeatable(chunk):
     w = W.custom(B=1, T=300, H=2, HV=2, K=128, V=128, h0_std=0.1)
     inp = W.make_inputs(w, seed=4)
@@ -231,7 +232,7 @@ FULL = {
 }
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32])
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled_parity(name, chunk):
     w = W.WORKLOADS[name]

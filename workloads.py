@@ -64,6 +64,9 @@ WORKLOADS = {
                              dtype="bf16"),
     "long_t131072": Workload("long_t131072", B=1, T=131072, H=32, HV=32, K=128, V=128,
                              dtype="bf16", g_lo=0.5, g_hi=0.9999, beta_std=2.0),
+    # one decoding step of a batch: 64 sequences, one new token each, carried state
+    "decode_b64_h32": Workload("decode_b64_h32", B=64, T=1, H=32, HV=32, K=128, V=128,
+                               dtype="bf16", h0_std=0.1),
 }
 
 
