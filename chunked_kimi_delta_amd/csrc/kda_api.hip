@@ -40,7 +40,8 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     if (!k_ok || !v_ok) return KDA_ERR_UNSUPPORTED;
     if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_UNSUPPORTED;
     int ct = a->chunk;
-    if (ct == 0) ct = a->io == KDA_BF16 ? 32 : 16;
+    if (ct == 0)            // default: the token recurrence for short dense batches (decode)
+        ct = (!a->cu_seqlens && a->T <= 16) ? 1 : (a->io == KDA_BF16 ? 32 : 16);
     if (ct != 1 && ct != 16 && !(ct == 32 && a->io == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
     const int64_t tt = (int64_t)a->B * a->T;
     const int64_t ns = tt / ct + a->N;

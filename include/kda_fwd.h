@@ -83,8 +83,9 @@ typedef struct {
                                  joined by block forward substitution; bf16 io only), 1 (the
                                  token recurrence itself, fp32 arithmetic, no workspace: for
                                  decoding and other short sequences, where a chunk's fixed cost
-                                 dominates), or 0 for the default (32 for bf16 io, 16 for fp32
-                                 io). Results agree to rounding.                             */
+                                 dominates), or 0 for the default: 1 for a dense batch with
+                                 T <= 16, else 32 for bf16 io and 16 for fp32 io. Results agree
+                                 to rounding.                                                */
 } kda_fwd_args;
 
 /* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
