@@ -111,10 +111,12 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
             if r["Counter_Name"] != counter:
                 continue
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024)
-        copy = [v for k, v in vals.items() if "copyBuffer" in k]
+        # the calibration copy is the largest copy dispatch (inputs uploaded to the device
+        # show up as smaller ones)
+        copy = [x for k, v in vals.items() if "copyBuffer" in k for x in v]
         if not copy:
             raise SystemExit(f"no calibration copy kernel in {d}")
-        scale = copy_bytes / statistics.mean(copy[0])
+        scale = copy_bytes / max(copy)
         for k, v in vals.items():
             m = re.search(r"kda::(prepare|state|recurrent)(?:32)?_", k)
             if m:
