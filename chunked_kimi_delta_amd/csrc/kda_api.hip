@@ -24,9 +24,10 @@ size_t record_bytes(int K, int V)
                    : (V == 64 ? WS<128, 64>::BYTES : WS<128, 128>::BYTES);
 }
 
-// Returns KDA_OK and fills the derived sizes, or the status kda_fwd must return.
+// Returns KDA_OK and fills the derived sizes (`need`: workspace bytes), or the status kda_fwd
+// must return.
 kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots,
-                        size_t *chunk_bytes, int *chunk)
+                        size_t *need, int *chunk)
 {
     if (!a) return KDA_ERR_INVALID_ARG;
     if (a->B < 1 || a->T < 0 || a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H)
@@ -55,7 +56,7 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
         cb = record_bytes<WsF32>(a->K, a->V);
     *T_total = tt;
     *n_slots = ns;
-    *chunk_bytes = cb;
+    *need = (size_t)ns * (size_t)a->HV * cb;
     *chunk = ct;
     return KDA_OK;
 }
@@ -85,9 +86,9 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
                       int stages)
 {
     int64_t tt, ns;
-    size_t cb;
+    size_t need;
     int ct;
-    const kda_status st = check_shapes(a, &tt, &ns, &cb, &ct);
+    const kda_status st = check_shapes(a, &tt, &ns, &need, &ct);
     if (st != KDA_OK) return st;
     if (a->N > 0 || tt > 0) {
         const void *ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
@@ -97,7 +98,6 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     if (a->initial_state && !aligned16(a->initial_state)) return KDA_ERR_INVALID_ARG;
     if (a->final_state && !aligned16(a->final_state)) return KDA_ERR_INVALID_ARG;
     if (a->cu_seqlens && !aligned16(a->cu_seqlens)) return KDA_ERR_INVALID_ARG;
-    const size_t need = (size_t)ns * (size_t)a->HV * cb;
     if (tt > 0 && need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
         return KDA_ERR_WORKSPACE;
     if (a->N == 0) return KDA_OK;
@@ -140,10 +140,10 @@ extern "C" {
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *a)
 {
     int64_t tt, ns;
-    size_t cb;
+    size_t need;
     int ct;
-    if (check_shapes(a, &tt, &ns, &cb, &ct) != KDA_OK) return 0;
-    return (size_t)ns * (size_t)a->HV * cb;
+    if (check_shapes(a, &tt, &ns, &need, &ct) != KDA_OK) return 0;
+    return need;
 }
 
 kda_status kda_fwd(const kda_fwd_args *a, void *workspace, size_t ws_bytes, void *stream)

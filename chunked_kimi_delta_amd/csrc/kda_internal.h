@@ -235,11 +235,29 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
+template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
 }
+template <int AUX = 0>
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+}
+// Stores through a buffer resource with cache policy AUX; stores past the resource's size are
+// dropped. A 16-byte store goes out as two 8-byte stores: behind a store with 128-bit data the
+// compiler has scheduled a VALU write of one of its data registers, and the store then wrote
+// the new value for some lanes (stores of at most 64 bits of data have shown no such loss).
+template <int AUX, class T>
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int voff, int soff, T v) {
+    static_assert(sizeof(T) == 16, "16-byte store");
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, r, voff, soff, AUX);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, r, voff, soff + 8, AUX);
+}
+template <int AUX, class T>
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int voff, int soff, T v) {
+    static_assert(sizeof(T) == 8, "8-byte store");
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, AUX);
 }
 
 // 16x16x16 product on the fp32 matrix core: D = A B + C with A in A16-layout and B in

@@ -169,7 +169,9 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
     for (int i = 0; i < 4; ++i) AT[i] = INV[i] * b4[i];  // A^T = diag(beta) (I + L)^{-T}
     const bf16x4 ATb = to_bf16x4(AT);                    // B-layout of A^T == A-layout of A
 
-    uint8_t *ws = p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES;
+    // the record, through a buffer resource: every store below is at most 8 bytes wide
+    const __amdgpu_buffer_rsrc_t wr =
+        buffer_rsrc(p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES, WS::BYTES);
 
     // ---------------------------------------------------------------- w = A KD  (TPL out)
     f16x4 wT[NK];
@@ -180,42 +182,40 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-        *(f16x8 *)(ws + WS::W + (st * 64 + lane) * 16) = cat(wT[2 * st], wT[2 * st + 1]);
+        bstore16<0>(wr, lane * 16, WS::W + st * 1024, cat(wT[2 * st], wT[2 * st + 1]));
 
     // ---------------------------------------------------------------- u = A V  (C-layout)
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
         const bf16x4 vA = __builtin_bit_cast(bf16x4, vraw[c]);
         const f32x4 vC = mfma16(vA, Ib, zero4());                    // C(V_c)
-        *(f16x4 *)(ws + WS::U + (c * 64 + lane) * 8) =
-            to_f16x4(mfma16(ATb, to_bf16x4(vC), zero4()));           // C(A V_c)
+        bstore8<0>(wr, lane * 8, WS::U + c * 512,
+                   to_f16x4(mfma16(ATb, to_bf16x4(vC), zero4())));   // C(A V_c)
     }
 
     // ---------------------------------------------------------------- qd (TPL), kr (C)
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-        *(f16x8 *)(ws + WS::QD + (st * 64 + lane) * 16) =
-            cat(to_f16x4(QD[2 * st]), to_f16x4(QD[2 * st + 1]));
+        bstore16<0>(wr, lane * 16, WS::QD + st * 1024,
+                    cat(to_f16x4(QD[2 * st]), to_f16x4(QD[2 * st + 1])));
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
         const f32x4 a = mfma16(to_f16x4(KRv[2 * st]), Ih, zero4());
         const f32x4 b = mfma16(to_f16x4(KRv[2 * st + 1]), Ih, zero4());
-        *(f16x8 *)(ws + WS::KR + (st * 64 + lane) * 16) = cat(to_f16x4(a), to_f16x4(b));
+        bstore16<0>(wr, lane * 16, WS::KR + st * 1024, cat(to_f16x4(a), to_f16x4(b)));
     }
 
     // ---------------------------------------------------------------- Mqk (A-layout)
-    *(f16x4 *)(ws + WS::MQK + lane * 8) = to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4()));
+    bstore8<0>(wr, lane * 8, WS::MQK, to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4())));
 
     // ---------------------------------------------------------------- exp(gam)
     if (r == 15) {
 #pragma unroll
         for (int c = 0; c < NK; ++c) {
-            float4 e;
-            e.x = __builtin_amdgcn_exp2f(G2[c][0]);
-            e.y = __builtin_amdgcn_exp2f(G2[c][1]);
-            e.z = __builtin_amdgcn_exp2f(G2[c][2]);
-            e.w = __builtin_amdgcn_exp2f(G2[c][3]);
-            *(float4 *)(ws + WS::EG + (16 * c + 4 * grp) * 4) = e;
+            f32x4 e;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(G2[c][i]);
+            bstore16<0>(wr, grp * 16, WS::EG + 64 * c, e);
         }
     }
 }

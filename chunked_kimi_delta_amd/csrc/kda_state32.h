@@ -1,0 +1,359 @@
+// kda_state32.h -- stage 2 with 32-token chunks: the chunk-sequential state pass, one serial
+// step per 32 tokens.
+//
+// Per chunk, with S the K x V state at the chunk start ("手撕KDA" section 1, chunk loop of
+// naive_chunk_kda, here with chunk 32):
+//     delta = U - W S                      (32 x V)
+//     o     = QD S + Mqk delta             (32 x V), rows past the sequence end not stored
+//     S    <- diag(e^{gam}) S + KR^T delta
+//
+// One workgroup per (sequence, value head, 16-column slice of V), three waves on three SIMDs:
+// two chain waves that each own half of the key rows of S (fp32 registers) and one output wave.
+// A chain step is split where the contraction over the key dimension allows it: each chain
+// wave forms its half of W S from its fp16 rows and hands the 32 x 16 fp32 partial to the
+// other through LDS; after the step's barrier both add the two partials (in the same order of
+// operands, so both hold the same delta), and each updates its own rows. The per-step VMEM,
+// VALU and MFMA work of one chain wave is half of a single-wave chain's, which is what bounds
+// the step: the serial path per 32 tokens is one LDS exchange, four update MFMAs and four W S
+// MFMAs. The output wave computes o for chunk c one barrier later, from the fp16 copy of S
+// the chain waves wrote and delta.
+//
+// Fragments are loaded two chunks ahead through buffer resources (scalar base = the chunk
+// record, clamped to the last chunk), in the lane order the prepare kernel wrote them.
+#pragma once
+
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+__device__ __forceinline__ bool state_unit32(int wg, int NV, int units, int *unit, int *slice) {
+    // all V/16 slices of one (sequence, value head) on one XCD (dispatch is round-robin over
+    // the 8 XCDs, each with its own L2), so they share the chunk operands in L2
+    const int xcd = wg & 7, idx = wg >> 3;
+    *unit = (idx / NV) * 8 + xcd;
+    *slice = idx % NV;
+    return *unit < units;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *o, int64_t row0, int nvalid,
+                                                            int64_t row_bytes,
+                                                            int64_t head_bytes) {
+    // range ends after the last valid token: stores to later rows are dropped by the hardware
+    uint8_t *base = (uint8_t *)o + row0 * row_bytes + head_bytes;
+    const int num = (int)(nvalid * row_bytes - head_bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, num, 0x00020000);
+}
+
+__device__ __forceinline__ void release_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+__device__ __forceinline__ void acquire_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_barrier() {
+    release_lds();
+    __builtin_amdgcn_s_barrier();
+    acquire_lds();
+}
+
+// Operands of one chunk for the chain wave that owns key rows [K/2 h, K/2 (h + 1)).
+template <int K, int V>
+struct HalfFrag {
+    static constexpr int NSH = K / 64, NKH = K / 32;   // 32-row slabs and 16-row tiles owned
+    f16x8 w[2][NSH];          // W rows of blocks a and b, this half's columns
+    f16x8 kr[NKH];            // KR^T tiles of this half over the 32 tokens
+    f32x4 eg[NKH];            // exp(gam) of the four rows 16t + 4g + i each lane holds
+    f16x8 nu;                 // -U of blocks a (0..3) and b (4..7), this slice (half 0 only)
+};
+
+template <int K, int V>
+struct OutFrag32 {
+    f16x8 qd[2][K / 32];
+    f16x4 mqa;
+    f16x8 mqb;
+};
+
+// One chunk record seen through a buffer resource (scalar base = the record); field offsets
+// are scalar constants and the per-lane part is lane * size.
+// AUX is the cache policy of the loads.
+template <int K, int V, int AUX = 0>
+struct Chunk32 {
+    using WS = WsBf16x32<K, V>;
+    static constexpr int NS = K / 32, NV = V / 16;
+    static constexpr int NSH = HalfFrag<K, V>::NSH, NKH = HalfFrag<K, V>::NKH;
+    __amdgpu_buffer_rsrc_t rs;
+    int lane, slice;
+    template <int h>
+    __device__ __forceinline__ void load_w(HalfFrag<K, V> &f) const {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < NSH; ++j)
+                f.w[b][j] = __builtin_bit_cast(
+                    f16x8, bload16<AUX>(rs, lane * 16, WS::W + (b * NS + h * NSH + j) * 1024));
+        const int grp = lane >> 4;
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+            f.eg[t] = __builtin_bit_cast(
+                f32x4, bload16<AUX>(rs, grp * 16, WS::EG + (h * NKH + t) * 64));
+        if constexpr (h == 0)
+            f.nu = __builtin_bit_cast(f16x8, bload16<AUX>(rs, lane * 16, WS::NU + slice * 1024));
+    }
+    template <int h>
+    __device__ __forceinline__ void load_kreg(HalfFrag<K, V> &f) const {
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+            f.kr[t] = __builtin_bit_cast(f16x8,
+                                         bload16<AUX>(rs, lane * 16, WS::KR + (h * NKH + t) * 1024));
+    }
+    __device__ __forceinline__ void load_out(OutFrag32<K, V> &f) const {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+                f.qd[b][st] = __builtin_bit_cast(f16x8, bload16<AUX>(rs, lane * 16,
+                                                                WS::QD + (b * NS + st) * 1024));
+        f.mqa = __builtin_bit_cast(f16x4, bload8<AUX>(rs, lane * 8, WS::MQKA));
+        f.mqb = __builtin_bit_cast(f16x8, bload16<AUX>(rs, lane * 16, WS::MQKB));
+    }
+};
+
+template <int K>
+struct Handoff32 {
+    f16x8 sh[3][K / 32][64];     // S (fp16) of chunk c in slot c % 3
+    f32x4 xp[2][2][2][64];       // [chunk parity][half][block] partial W S (half 0: + (-U))
+    f16x4 dh[2][2][64];          // [chunk parity][block] delta
+};
+
+// Chain wave h, one 32-token chunk c (S = its rows of the state at the chunk start), up to
+// and including barrier c: fp16 rows to the hand-off and the partial of W S to the other half.
+// Nothing else precedes the barrier, so both halves reach it as early as their products allow.
+template <int K, int V, int h>
+__device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, const f32x4 (&S)[K / 32],
+                                             f32x4 &Xa, f32x4 &Xb, Handoff32<K> &ho, int slot,
+                                             int par, int lane)
+{
+    constexpr int NSH = K / 64;
+    if constexpr (h == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Xa[i] = (float)f.nu[i];
+            Xb[i] = (float)f.nu[4 + i];
+        }
+    } else {
+        Xa = zero4();
+        Xb = zero4();
+    }
+#pragma unroll
+    for (int j = 0; j < NSH; ++j) {
+        const f16x8 Sh = cat(to_f16x4(S[2 * j]), to_f16x4(S[2 * j + 1]));
+        ho.sh[slot][h * NSH + j][lane] = Sh;
+        Xa = mfma32(f.w[0][j], Sh, Xa);
+        Xb = mfma32(f.w[1][j], Sh, Xb);
+    }
+    ho.xp[par][h][0][lane] = Xa;
+    ho.xp[par][h][1][lane] = Xb;
+    lds_barrier();
+}
+
+// Chain wave h after barrier c: the other half's partial is read first, and its LDS latency
+// is covered by the decay of this half's rows and the refill of the W / exp(gam) / -U group
+// from `nxt` (two chunks ahead); then delta = -(own partial + other partial) (half 0 hands it
+// to the output wave) and the update of its rows; the KR^T group is refilled last.
+template <int K, int V, int h, int AUX>
+__device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, const Chunk32<K, V, AUX> &nxt,
+                                             f32x4 (&S)[K / 32], f32x4 Xa, f32x4 Xb,
+                                             Handoff32<K> &ho, int par, int lane)
+{
+    constexpr int NKH = K / 32;
+    const f32x4 Pa = ho.xp[par][1 - h][0][lane], Pb = ho.xp[par][1 - h][1][lane];
+#pragma unroll
+    for (int t = 0; t < NKH; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
+    nxt.template load_w<h>(f);
+    f16x4 dh0, dh1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // half 0 adds (own + other) and half 1 (other + own): the same two fp32 operands, so
+        // both halves round to the same delta
+        dh0[i] = (_Float16)(-(Xa[i] + Pa[i]));
+        dh1[i] = (_Float16)(-(Xb[i] + Pb[i]));
+    }
+    if constexpr (h == 0) {
+        ho.dh[par][0][lane] = dh0;
+        ho.dh[par][1][lane] = dh1;
+    }
+    const f16x8 d32 = cat(dh0, dh1);
+#pragma unroll
+    for (int t = 0; t < NKH; ++t) S[t] = mfma32(f.kr[t], d32, S[t]);
+    nxt.template load_kreg<h>(f);
+}
+
+template <int K, int V, int h, int AUX>
+__device__ __forceinline__ void chain_step(HalfFrag<K, V> &f, const Chunk32<K, V, AUX> &nxt,
+                                           f32x4 (&S)[K / 32], Handoff32<K> &ho, int c,
+                                           int par, int lane)
+{
+    f32x4 Xa, Xb;
+    chain_half_a<K, V, h>(f, S, Xa, Xb, ho, c % 3, par, lane);
+    chain_half_b<K, V, h, AUX>(f, nxt, S, Xa, Xb, ho, par, lane);
+}
+
+// Chain wave h over the whole sequence: S rows [K/2 h, K/2 (h + 1)) from initial_state (or 0),
+// the chunk loop, barrier nc, and the final state.
+template <int K, int V, int h, int AUX>
+__device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
+                                           const uint8_t *base, int nc, int s, int j, int col,
+                                           int slice, int lane)
+{
+    constexpr int NKH = K / 32;
+    using WS = WsBf16x32<K, V>;
+    const int grp = lane >> 4;
+    const int row0 = h * (K / 2);
+    auto at = [&](int c) {
+        return Chunk32<K, V, AUX>{
+            buffer_rsrc(base + (size_t)min(c, nc - 1) * WS::BYTES, WS::BYTES), lane, slice};
+    };
+    f32x4 S[NKH];
+    if (p.h0) {
+        const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[t][i] = h0[(size_t)(row0 + 16 * t + 4 * grp + i) * V];
+    } else {
+#pragma unroll
+        for (int t = 0; t < NKH; ++t) S[t] = zero4();
+    }
+    if (nc > 0) {
+        HalfFrag<K, V> fa, fb;
+        at(0).template load_w<h>(fa); at(0).template load_kreg<h>(fa);
+        at(1).template load_w<h>(fb); at(1).template load_kreg<h>(fb);
+        // drain the prologue loads: the loop header then carries only the loop's own pending
+        // loads, and the waits inside the loop count back to the right group
+        vm_drain();
+        // no exit between the loop body's two steps: an exit there would merge a half-step
+        // state into the loop header and make every iteration wait for the loads just issued
+        int c = 0;
+        for (; c + 2 <= nc; c += 2) {
+            chain_step<K, V, h, AUX>(fa, at(c + 2), S, ho, c, 0, lane);
+            chain_step<K, V, h, AUX>(fb, at(c + 3), S, ho, c + 1, 1, lane);
+        }
+        if (c < nc) chain_step<K, V, h, AUX>(fa, at(c + 2), S, ho, c, 0, lane);
+        lds_barrier();    // barrier nc: delta of the last chunk is in the hand-off
+    }
+    if (p.ht) {
+        float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+#pragma unroll
+        for (int t = 0; t < NKH; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ht[(size_t)(row0 + 16 * t + 4 * grp + i) * V] = S[t][i];
+    }
+}
+
+// Output wave, chunk c, after barrier c + 1: o = QD S + Mqk delta, stored as bf16. `nxt` is
+// the record two chunks ahead.
+template <int K, int V, int AUX>
+__device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V, AUX> &nxt,
+                                           const Handoff32<K> &ho, int slot, int par, int lane,
+                                           __amdgpu_buffer_rsrc_t orows, const int (&ooff)[2],
+                                           bf16x4 Ib)
+{
+    constexpr int NS = K / 32;
+    lds_barrier();
+    f16x8 Sh[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) Sh[st] = ho.sh[slot][st][lane];
+    const f16x4 dh0 = ho.dh[par][0][lane], dh1 = ho.dh[par][1][lane];
+    f32x4 Y0 = zero4(), Y1 = zero4();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        Y0 = mfma32(f.qd[0][st], Sh[st], Y0);
+        Y1 = mfma32(f.qd[1][st], Sh[st], Y1);
+    }
+    const f32x4 O0 = mfma16(f.mqa, dh0, Y0);
+    const f32x4 O1 = mfma32(f.mqb, cat(dh0, dh1), Y1);
+    nxt.load_out(f);
+    // C(O) holds four rows of one column per lane; the identity product C(O^T) holds four
+    // consecutive columns of one row, so each block goes out as one 8-byte store per lane (the
+    // values are bf16 already, so the product changes none of them)
+    const bf16x4 T0 = to_bf16x4(mfma16(to_bf16x4(O0), Ib, zero4()));
+    const bf16x4 T1 = to_bf16x4(mfma16(to_bf16x4(O1), Ib, zero4()));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T0), orows, ooff[0], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T1), orows, ooff[1], 0, 0);
+}
+
+// Barrier schedule for nc chunks: every wave passes nc + 1 barriers. Barrier c (c < nc)
+// follows the chain waves' hand-off of chunk c (fp16 rows of S in slot c % 3, the W S
+// partials in slot c % 2); between barriers c and c+1 the chain waves form delta_c (half 0
+// writes it to slot c % 2) and update S, then write chunk c+1's hand-off; the output wave,
+// after barrier c+1, reads the fp16 rows and delta_c. The fp16 rows are rewritten three
+// chunks later (after barrier c+2), the partials and delta two chunks later (after barrier
+// c+1 and c+2 respectively), each after its readers are done. The chain waves pass barrier nc
+// after their last update.
+
+// One V-slice (16 columns of S and o) of one (sequence, value head) unit, as three waves: role
+// 0 and 1 are the chain halves, role 2 the output wave; every role passes the same barriers.
+// AUX is the cache policy of the workspace loads.
+template <int K, int V, int AUX>
+__device__ __forceinline__ void state32_slice(const FwdParams &p, Handoff32<K> &ho, int unit,
+                                              int slice, int role, int lane)
+{
+    constexpr int CT = 32;
+    using WS = WsBf16x32<K, V>;
+    const int grp = lane >> 4, n = lane & 15;
+    const int j = unit % p.HV;
+    const int s = unit / p.HV;
+    const int64_t bos = seq_bos(p.seq, s);
+    const int64_t eos = seq_eos(p.seq, s, bos);
+    const int nc = (int)((eos - bos + CT - 1) / CT);
+    const int col = 16 * slice + n;
+    const uint8_t *base =
+        p.ws + ((size_t)j * p.seq.n_slots + (size_t)(bos / CT + s)) * (size_t)WS::BYTES;
+    auto at = [&](int c) {
+        return Chunk32<K, V, AUX>{
+            buffer_rsrc(base + (size_t)min(c, nc - 1) * WS::BYTES, WS::BYTES), lane, slice};
+    };
+
+    if (role == 0) {
+        chain_wave<K, V, 0, AUX>(p, ho, base, nc, s, j, col, slice, lane);
+    } else if (role == 1) {
+        chain_wave<K, V, 1, AUX>(p, ho, base, nc, s, j, col, slice, lane);
+    } else if (nc > 0) {
+        const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)j * V * 2;
+        // after the transposing product lane (g, n) holds row n (block a) / 16 + n (block b),
+        // columns 16 slice + 4g .. + 3
+        const int ocol = 16 * slice + 4 * grp;
+        const int ooff[2] = {(int)(n * row_bytes + ocol * 2),
+                             (int)((16 + n) * row_bytes + ocol * 2)};
+        float eye[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eye[i] = 4 * grp + i == n ? 1.f : 0.f;
+        const bf16x4 Ib = to_bf16x4(eye);
+        auto rows = [&](int c) {
+            const int64_t r0 = bos + CT * c;
+            const int64_t nv = eos - r0;
+            return rows_rsrc(p.o, r0, (int)(nv < CT ? nv : CT), row_bytes, head_bytes);
+        };
+        OutFrag32<K, V> fa, fb;
+        at(0).load_out(fa);
+        at(1).load_out(fb);
+        vm_drain();
+        lds_barrier();        // barrier 0
+        int c = 0;
+        for (; c + 2 <= nc; c += 2) {
+            out_step32<K, V, AUX>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff, Ib);
+            out_step32<K, V, AUX>(fb, at(c + 3), ho, (c + 1) % 3, 1, lane, rows(c + 1), ooff, Ib);
+        }
+        if (c < nc) out_step32<K, V, AUX>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff, Ib);
+    }
+}
+
+}  // namespace
+
+}  // namespace kda

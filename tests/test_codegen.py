@@ -1,0 +1,91 @@
+"""Code generation checks on the gfx950 assembly of every kernel source (CPU only: hipcc -S).
+
+A VMEM store with more than 64 bits of data reads its data registers after issue; a VALU
+instruction that overwrites one of them right behind the store made the store write the new
+value for some lanes (seen as torn chunk records). The kernels therefore store at most 8 bytes
+per instruction where a record is written, and this test keeps any wide store followed closely
+by a write of its data registers out of the library.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "chunked_kimi_delta_amd", "csrc")
+
+WIDE_STORE = re.compile(r"^(global_store_dwordx[34]|buffer_store_dwordx[34]|flat_store_dwordx[34])\s+(.*)")
+
+
+def vregs(tok: str) -> set:
+    out = set()
+    for m in re.finditer(r"\bv(\d+)\b|\bv\[(\d+):(\d+)\]", tok):
+        if m.group(1):
+            out.add(int(m.group(1)))
+        else:
+            out.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    return out
+
+
+def wide_store_overwrites(asm: str, window: int = 3):
+    """(line, store, writer) for every wide store whose data registers a VALU instruction among
+    the next `window` instructions writes."""
+    lines = [l.split(";")[0].strip() for l in asm.splitlines()]
+    instr = [(i, l) for i, l in enumerate(lines)
+             if l and not l.endswith(":") and not l.startswith(".")]
+    hits = []
+    for k, (i, l) in enumerate(instr):
+        m = WIDE_STORE.match(l)
+        if not m:
+            continue
+        ops = [x.strip() for x in m.group(2).split(",")]
+        data = vregs(ops[0]) if m.group(1).startswith("buffer") else vregs(ops[1])
+        for _, nxt in instr[k + 1:k + 1 + window]:
+            if nxt.startswith("v_") and not nxt.startswith(("v_cmp", "v_readfirstlane",
+                                                            "v_readlane")):
+                parts = nxt.split(None, 1)
+                if len(parts) == 2 and vregs(parts[1].split(",")[0]) & data:
+                    hits.append((i, l, nxt))
+                    break
+    return hits
+
+
+def test_detector_finds_the_pattern():
+    asm = """
+    buffer_store_dwordx4 v[52:55], v101, s[20:23], s6 offen
+    v_mov_b32_e32 v52, 0
+    global_store_dwordx4 v[2:3], v[8:11], off
+    v_add_f32_e32 v1, v2, v3
+    buffer_store_dwordx2 v[4:5], v1, s[0:3], 0 offen
+    v_mov_b32_e32 v4, 0
+    """
+    hits = wide_store_overwrites(asm)
+    assert [h[2] for h in hits] == ["v_mov_b32_e32 v52, 0"]
+
+
+def _asm(src: str, out_dir: str) -> str:
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "chunked_kimi_delta_amd"))
+    from build import HIPCC_FLAGS, hipcc
+    out = os.path.join(out_dir, os.path.basename(src) + ".s")
+    subprocess.run([hipcc()] + HIPCC_FLAGS + ["--cuda-device-only", "-S", src, "-o", out],
+                   check=True, capture_output=True)
+    return open(out).read()
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_no_wide_store_data_overwrite_in_kernels():
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with tempfile.TemporaryDirectory() as d, cf.ThreadPoolExecutor(4) as ex:
+        asms = dict(zip(srcs, ex.map(lambda s: _asm(s, d), srcs)))
+    bad = {os.path.basename(s): wide_store_overwrites(a)[:3] for s, a in asms.items()}
+    bad = {k: v for k, v in bad.items() if v}
+    assert not bad, bad

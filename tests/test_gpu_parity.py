@@ -256,3 +256,20 @@ def test_full_size_sampled_parity(name, chunk):
     ef = rel_l2(np.stack(got_f), np.stack(ref_f))
     report(eo, ef)
     assert eo <= TOL[w.dtype] and ef <= TOL[w.dtype], f"rel L2 o={eo:.3e} final={ef:.3e}"
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_prepare_records_repeat_bitwise_full_size(chunk):
+    # every chunk record of the h16_t4096 workload, written twice into a zeroed workspace, is
+    # the same bits both times (a lost or torn record store shows up as a difference)
+    w = W.WORKLOADS["h16_t4096"]
+    inp = W.make_inputs(w, seed=0)
+    plan = gpu_plan(inp, chunk=chunk)
+    runs = []
+    for _ in range(3):
+        plan.workspace.zero_()
+        plan.prepare()
+        torch.cuda.synchronize()
+        runs.append(plan.workspace.clone())
+    for r in runs[1:]:
+        assert torch.equal(runs[0], r)
