@@ -211,7 +211,10 @@ def main():
     d = lambda x: None if x is None else x.to(dev).contiguous()
     plan = kda.KdaFwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta),
                           cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0), chunk=a.chunk)
-    chunk = a.chunk or (32 if w.dtype == "bf16" else 16)
+    # the chunk the library picks for chunk 0 (include/kda_fwd.h): the token recurrence for a
+    # dense batch of at most 16 tokens per sequence, else 32 (bf16 io) or 16 (fp32 io)
+    chunk = a.chunk or (1 if inp.cu_seqlens is None and inp.q.shape[1] <= 16 else
+                        32 if w.dtype == "bf16" else 16)
     stream = torch.cuda.current_stream(dev)
 
     if a.copy_calibration:
@@ -268,14 +271,17 @@ def main():
 
     work = algorithmic_work(inp, chunk)
     es = "bf16" if w.dtype == "bf16" else "fp32"
-    kernels = {
-        "kda_prepare": {"avg_ms": round(prep_ms, 5), "bound": "hbm",
-                        "alg_bytes": work["prep_bytes"], "alg_flops": work["prep_flops"],
-                        "achieved_GBs": round(work["prep_bytes"] / (prep_ms * 1e-3) / 1e9, 1)},
-        "kda_state": {"avg_ms": round(state_ms, 5), "bound": "mfma",
-                      "alg_bytes": work["state_bytes"], "alg_flops": work["state_flops"],
-                      "achieved_TFLOPs": round(work["state_flops"] / (state_ms * 1e-3) / 1e12, 2)},
-    }
+    if chunk != 1:
+        kernels = {
+            "kda_prepare": {"avg_ms": round(prep_ms, 5), "bound": "hbm",
+                            "alg_bytes": work["prep_bytes"], "alg_flops": work["prep_flops"],
+                            "achieved_GBs": round(work["prep_bytes"] / (prep_ms * 1e-3) / 1e9,
+                                                  1)},
+            "kda_state": {"avg_ms": round(state_ms, 5), "bound": "mfma",
+                          "alg_bytes": work["state_bytes"], "alg_flops": work["state_flops"],
+                          "achieved_TFLOPs": round(work["state_flops"] / (state_ms * 1e-3) / 1e12,
+                                                   2)},
+        }
     if chunk == 1:
         # the token recurrence is one kernel (the prepare launch is empty): everything it reads
         # and writes (inputs, o, the states) is its algorithmic traffic

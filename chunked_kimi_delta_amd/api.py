@@ -79,9 +79,11 @@ class KdaFwdPlan:
         self.args = a
         self._keep = (q, k, v, g, beta, cu_seqlens, initial_state)
         need = int(self.lib.kda_fwd_workspace_bytes(ctypes.byref(a)))
-        # 0 means "rejected", except for chunk 1, which needs no workspace (its shape errors
-        # surface as the call's status)
-        if need == 0 and B * T > 0 and int(chunk) != 1:
+        # 0 means "rejected", except for the token recurrence (chunk 1, which chunk 0 selects
+        # for a dense batch of at most 16 tokens per sequence): it needs no workspace, and its
+        # shape errors surface as the call's status
+        recurrent = int(chunk) == 1 or (int(chunk) == 0 and cu_seqlens is None and T <= 16)
+        if need == 0 and B * T > 0 and not recurrent:
             raise ValueError("unsupported shapes or chunk (K, V in {64, 128}; HV % H == 0; "
                              "chunk 1, 16, or 32 with bf16 io)")
         if workspace is None:

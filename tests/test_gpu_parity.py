@@ -273,3 +273,13 @@ def test_prepare_records_repeat_bitwise_full_size(chunk):
         runs.append(plan.workspace.clone())
     for r in runs[1:]:
         assert torch.equal(runs[0], r)
+
+
+@pytest.mark.parametrize("T", [1, 16, 17])
+def test_default_chunk_short_dense_batches(T):
+    # chunk 0: the token recurrence for T <= 16 (decode steps), 32-token chunks above
+    w = W.custom(B=4, T=T, H=2, HV=4, K=128, V=128, h0_std=0.1)
+    inp = W.make_inputs(w, seed=13)
+    o, fin = gpu_run(inp, chunk=0)
+    o_ref, f_ref = oracle_run(inp)
+    check_all(inp, o, fin, o_ref, f_ref, TOL["bf16"])
