@@ -15,6 +15,9 @@ Contents
                   inputs with rational decays.
   kda_oracle.c    the fp64 token recurrence in plain C, threaded over independent
                   (sequence, value head) units; the fast oracle for large workloads.
+  prestage.py     fp64 pre-stage: q/k L2 normalisation, beta sigmoid and the two gate
+                  activations (softplus and bounded sigmoid) that produce the recurrence's
+                  q, k, g, beta from raw projections.
   native.py       ctypes loader for the C oracle.
   build.py        compiles kda_oracle.c with gcc.
 
