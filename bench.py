@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h16_t4096")
+    ap.add_argument("--prestage", choices=["none", "softplus", "bounded"], default="none",
+                    help="raw inputs with the fused pre-stage (q/k L2 norm, beta sigmoid and "
+                         "this gate activation) inside the kernels")
     ap.add_argument("--chunk", type=int, default=0,
                     help="tokens per serial state step (16, 32; 0 = library default)")
     ap.add_argument("--cold-steps", type=int, default=20,
@@ -206,11 +209,19 @@ def main():
     import chunked_kimi_delta_amd as kda
 
     w = W.WORKLOADS[a.workload]
-    inp = W.make_inputs(w, seed=0)
+    pre = {}
+    if a.prestage != "none":
+        raw = W.make_raw_inputs(w, seed=0)
+        inp = raw.inp
+        pre = dict(use_qk_l2norm=True, use_beta_sigmoid=True, gate=a.prestage,
+                   A_log=raw.A_log.to("cuda:0"), dt_bias=raw.dt_bias.to("cuda:0"))
+    else:
+        inp = W.make_inputs(w, seed=0)
     dev = torch.device("cuda:0")
     d = lambda x: None if x is None else x.to(dev).contiguous()
     plan = kda.KdaFwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta),
-                          cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0), chunk=a.chunk)
+                          cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0), chunk=a.chunk,
+                          **pre)
     # the chunk the library picks for chunk 0 (include/kda_fwd.h): the token recurrence for a
     # dense batch of at most 16 tokens per sequence, else 32 (bf16 io) or 16 (fp32 io)
     chunk = a.chunk or (1 if inp.cu_seqlens is None and inp.q.shape[1] <= 16 else
@@ -311,7 +322,7 @@ def main():
                  "alg_bytes_per_step": path_bytes}
 
     cpu = None
-    if a.cpu_seconds > 0:
+    if a.cpu_seconds > 0 and not pre:
         cpu = cpu_baseline(inp, a.cpu_seconds)
 
     value = inp.T_total / (ms_per_step * 1e-3)
@@ -322,7 +333,7 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
                    "K": w.K, "V": w.V, "chunk": chunk, "tokens_per_step": inp.T_total,
-                   "parallelism": "single-gpu",
+                   "parallelism": "single-gpu", "prestage": a.prestage,
                    "arithmetic": ("fp32 VALU token recurrence" if chunk == 1 else
                                   "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse")},
         "roofline": roof, "roofline_path": roof_path, "kernels": kernels,

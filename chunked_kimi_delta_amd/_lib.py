@@ -9,6 +9,7 @@ LIB_NAME = "libkda_fwd.so"
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_BF16, KDA_FP32 = 0, 1
+KDA_GATE_NONE, KDA_GATE_SOFTPLUS, KDA_GATE_BOUNDED = 0, 1, 2
 
 
 class KdaFwdArgs(ctypes.Structure):
@@ -23,6 +24,9 @@ class KdaFwdArgs(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
         ("chunk", ctypes.c_int32),
+        ("qk_l2norm", ctypes.c_int32), ("beta_sigmoid", ctypes.c_int32),
+        ("gate", ctypes.c_int32), ("gate_lower_bound", ctypes.c_float),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
     ]
 
 

@@ -6,7 +6,10 @@ from typing import Optional
 
 import torch
 
-from ._lib import KDA_BF16, KDA_FP32, KdaFwdArgs, load, strerror
+from ._lib import (KDA_BF16, KDA_FP32, KDA_GATE_BOUNDED, KDA_GATE_NONE, KDA_GATE_SOFTPLUS,
+                   KdaFwdArgs, load, strerror)
+
+_GATES = {None: KDA_GATE_NONE, "softplus": KDA_GATE_SOFTPLUS, "bounded": KDA_GATE_BOUNDED}
 
 _IO = {torch.bfloat16: KDA_BF16, torch.float32: KDA_FP32}
 
@@ -33,10 +36,18 @@ class KdaFwdPlan:
     HIP device); cu_seqlens int64 [N+1] on the device (then B == 1) or None; initial_state fp32
     [N,HV,K,V] or None. Outputs o (io dtype, like v) and final_state (fp32, or None) and the
     workspace are allocated once through torch and reused by every call().
+
+    Pre-stage, done inside the kernels: use_qk_l2norm divides each token's q and k by
+    sqrt(sum of squares + 1e-6); use_beta_sigmoid takes beta as logits; gate "softplus"
+    (g <- -exp(A_log) softplus(g + dt_bias)) or "bounded" (g <- gate_lower_bound *
+    sigmoid(exp(A_log) (g + dt_bias))) takes g as the raw gate input, with A_log fp32 [HV] and
+    dt_bias fp32 [HV, K] or None.
     """
 
     def __init__(self, q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
-                 output_final_state=True, workspace=None, o=None, final_state=None, chunk=0):
+                 output_final_state=True, workspace=None, o=None, final_state=None, chunk=0,
+                 use_qk_l2norm=False, use_beta_sigmoid=False, gate=None, A_log=None,
+                 dt_bias=None, gate_lower_bound=-5.0):
         self.lib = load()
         if q.dtype not in _IO:
             raise TypeError(f"unsupported io dtype {q.dtype} (bf16 or fp32)")
@@ -76,8 +87,21 @@ class KdaFwdPlan:
         a.o = _ptr(self.o)
         a.final_state = _ptr(self.final_state)
         a.chunk = int(chunk)
+        if gate not in _GATES:
+            raise ValueError(f"gate must be None, 'softplus' or 'bounded' (got {gate!r})")
+        a.qk_l2norm = int(bool(use_qk_l2norm))
+        a.beta_sigmoid = int(bool(use_beta_sigmoid))
+        a.gate = _GATES[gate]
+        a.gate_lower_bound = float(gate_lower_bound)
+        if gate is not None:
+            if A_log is None:
+                raise ValueError("a gate needs A_log")
+            _check(A_log, "A_log", torch.float32, (HV,), dev)
+            if dt_bias is not None:
+                _check(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+            a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
         self.args = a
-        self._keep = (q, k, v, g, beta, cu_seqlens, initial_state)
+        self._keep = (q, k, v, g, beta, cu_seqlens, initial_state, A_log, dt_bias)
         need = int(self.lib.kda_fwd_workspace_bytes(ctypes.byref(a)))
         # 0 means "rejected", except for the token recurrence (chunk 1, which chunk 0 selects
         # for a dense batch of at most 16 tokens per sequence): it needs no workspace, and its
@@ -118,10 +142,12 @@ class KdaFwdPlan:
 
 
 def kda_fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
-            output_final_state=True, workspace=None, chunk=0):
-    """KDA forward. Returns (o, final_state or None); see KdaFwdPlan for shapes."""
+            output_final_state=True, workspace=None, chunk=0, **prestage):
+    """KDA forward. Returns (o, final_state or None); see KdaFwdPlan for shapes and the
+    pre-stage keywords (use_qk_l2norm, use_beta_sigmoid, gate, A_log, dt_bias,
+    gate_lower_bound)."""
     plan = KdaFwdPlan(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_final_state,
-                      workspace, chunk=chunk)
+                      workspace, chunk=chunk, **prestage)
     return plan()
 
 

@@ -98,6 +98,15 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     if (a->initial_state && !aligned16(a->initial_state)) return KDA_ERR_INVALID_ARG;
     if (a->final_state && !aligned16(a->final_state)) return KDA_ERR_INVALID_ARG;
     if (a->cu_seqlens && !aligned16(a->cu_seqlens)) return KDA_ERR_INVALID_ARG;
+    if (a->gate != KDA_GATE_NONE && a->gate != KDA_GATE_SOFTPLUS && a->gate != KDA_GATE_BOUNDED)
+        return KDA_ERR_UNSUPPORTED;
+    if (a->gate != KDA_GATE_NONE) {
+        if (!a->A_log || ((uintptr_t)a->A_log & 3u)) return KDA_ERR_INVALID_ARG;
+        if (a->dt_bias && !aligned16(a->dt_bias)) return KDA_ERR_INVALID_ARG;
+        if (a->gate == KDA_GATE_BOUNDED &&
+            !(a->gate_lower_bound < 0.f && a->gate_lower_bound > -INFINITY))
+            return KDA_ERR_INVALID_ARG;
+    }
     if (tt > 0 && need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
         return KDA_ERR_WORKSPACE;
     if (a->N == 0) return KDA_OK;
@@ -121,6 +130,12 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     p.o = a->o;
     p.ht = a->final_state;
     p.ws = (uint8_t *)workspace;
+    p.pre.qk_l2norm = a->qk_l2norm != 0;
+    p.pre.beta_sigmoid = a->beta_sigmoid != 0;
+    p.pre.gate = a->gate;
+    p.pre.lower_bound = a->gate_lower_bound;
+    p.pre.A_log = a->A_log;
+    p.pre.dt_bias = a->dt_bias;
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -168,13 +183,14 @@ const char *kda_strerror(int status)
     case KDA_OK: return "ok";
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED:
-        return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 with bf16 io)";
+        return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 with bf16 io; "
+               "gate 0, 1 or 2)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
     }
 }
 
-int kda_version(void) { return 102; }
+int kda_version(void) { return 103; }
 
 }  // extern "C"

@@ -47,6 +47,15 @@ struct SeqGeom {
     int32_t n_slots;     // T_total / CT + N
 };
 
+// Pre-stage of the raw inputs (q/k L2 norm, beta sigmoid, gate activation), applied by every
+// kernel that reads q, k, g or beta.
+struct Prestage {
+    int32_t qk_l2norm, beta_sigmoid, gate;   // gate: 0 none, 1 softplus, 2 bounded sigmoid
+    float lower_bound;
+    const float *A_log;                      // [HV]
+    const float *dt_bias;                    // [HV, K] or nullptr
+};
+
 struct FwdParams {
     SeqGeom seq;
     int32_t H, HV, G;
@@ -56,6 +65,7 @@ struct FwdParams {
     void *o;
     float *ht;
     uint8_t *ws;
+    Prestage pre;
 };
 
 // Workspace of one (value head, slot) chunk, bf16 io. All fragments are stored in the exact
@@ -284,9 +294,43 @@ __device__ __forceinline__ float row_inclusive_scan(float x) {
     return x;
 }
 
+// Sum of x over the four lanes of a wave that share lane % 16 (the four lane groups).
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
 // value of x held by lane `src` (0..63)
 __device__ __forceinline__ float lane_read(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// ----------------------------------------------------------------------------- pre-stage
+
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float L2NORM_EPS = 1e-6f;
+
+// 1 / (1 + e^-x) from the base-2 exponential; 0 and 1 at the extremes, never NaN.
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * LOG2E));
+}
+
+// log(1 + e^x) as max(x, 0) + log(1 + e^-|x|): no overflow; absolute error about 1e-7, which
+// is what a log decay needs (exp(g) then has relative error about 1e-7).
+__device__ __forceinline__ float softplus_f(float x) {
+    return fmaxf(x, 0.f) +
+           LN2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E));
+}
+
+// The gate activation on x = g + dt_bias with a = exp(A_log) of the value head (pre.gate != 0).
+__device__ __forceinline__ float gate_activation(const Prestage &pre, float x, float a) {
+    return pre.gate == 1 ? -a * softplus_f(x) : pre.lower_bound * sigmoid_f(a * x);
+}
+
+// 1 / sqrt(sum of squares + eps): the L2-norm factor of a q or k row.
+__device__ __forceinline__ float l2norm_factor(float sumsq) {
+    return __builtin_amdgcn_rsqf(sumsq + L2NORM_EPS);
 }
 
 // Wait for every outstanding vector memory load of this wave (vmcnt 0; the LDS/scalar and

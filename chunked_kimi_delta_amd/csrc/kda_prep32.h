@@ -60,6 +60,7 @@ template <int K, int V>
 struct Prep32In {
     u32x4 q[K / 32], k[K / 32], g[K / 32], v[V / 32];
     float beta;
+    int nrows;                   // valid rows of the block (the rest are zero padding)
 };
 
 template <int RL>
@@ -93,6 +94,8 @@ __device__ __forceinline__ void prep32_load(const FwdParams &p, int64_t bos, int
                  in.v);
     in.beta = r < nrows ? bf16_bits_to_f32(((const uint16_t *)p.beta)[(tok0 + r) * p.HV + j])
                         : 0.f;
+    if (p.pre.beta_sigmoid && r < nrows) in.beta = sigmoid_f(in.beta);   // pre-stage
+    in.nrows = nrows;
 }
 
 // Row-contiguous input rows -> TPL (lane (g, r): row r, columns 16c + 4g .. + 3) through this
@@ -117,11 +120,15 @@ __device__ __forceinline__ void rows_to_tpl(const u32x4 (&x)[RL / 32], uint2 (&o
 // call it together (it synchronises the workgroup).
 //
 // `wr` is a buffer resource over the chunk's workspace record (a zero-sized one drops every
-// store); AUX is the cache policy of the stores.
-template <int K, int V, int AUX = 0>
+// store) of value head j; AUX is the cache policy of the stores. NORM: q and k are divided by
+// their L2 norms (pre-stage); the factor of each token's row is applied in fp32 wherever q or
+// k is unpacked, so the bf16 inputs are not rounded again. A gate activation (pre-stage) is
+// applied to g before the cumsum, to valid rows only (padding rows keep g = 0).
+template <int K, int V, bool NORM = false, int AUX = 0>
 __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, V> &sh,
                                              const Prep32In<K, V> &in,
-                                             __amdgpu_buffer_rsrc_t wr, int wave, int lane)
+                                             __amdgpu_buffer_rsrc_t wr, int j, int wave,
+                                             int lane)
 {
     constexpr int NK = K / 16, NV = V / 16, NS = K / 32;
     using WS = WsBf16x32<K, V>;
@@ -130,6 +137,20 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     // q, k and v stay as packed bf16 pairs until each use: every phase below rebuilds the fp32
     // values it needs from them, which keeps the live register set small enough for several
     // waves per SIMD.
+    // gate parameters of this value head, loaded first so their latency is covered
+    const bool gated = p.pre.gate != 0;
+    float aexp = 0.f;
+    f32x4 dtv[NK];
+#pragma unroll
+    for (int c = 0; c < NK; ++c) dtv[c] = zero4();
+    if (gated) {
+        aexp = __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E);
+        if (p.pre.dt_bias) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c)
+                dtv[c] = *(const f32x4 *)(p.pre.dt_bias + (size_t)j * K + 16 * c + 4 * grp);
+        }
+    }
     uint2 qr[NK], kr[NK], gr[NK], vraw[NV];
     uint8_t *stage = sh.u.stage[wave];
     rows_to_tpl<K>(in.g, gr, stage, lane);
@@ -137,6 +158,25 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     rows_to_tpl<K>(in.q, qr, stage, lane);
     rows_to_tpl<V>(in.v, vraw, stage, lane);
     const float beta_r = in.beta;
+    // L2-norm factors of this lane's token row (its other columns are in the three other lane
+    // groups); padding rows are zero and stay zero
+    float rk = 1.f, rq = 1.f;
+    if constexpr (NORM) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            float kk[4], qq[4];
+            unpack_bf16x4(kr[c], kk);
+            unpack_bf16x4(qr[c], qq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sk += kk[i] * kk[i];
+                sq += qq[i] * qq[i];
+            }
+        }
+        rk = l2norm_factor(sum_lane_groups(sk));
+        rq = l2norm_factor(sum_lane_groups(sq));
+    }
 
     // ---------------------------------------------------------------- cumsum over 32 tokens
     float G2[NK][4];
@@ -144,6 +184,11 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     for (int c = 0; c < NK; ++c) {
         float gl[4];
         unpack_bf16x4(gr[c], gl);
+        if (gated) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                gl[i] = r < in.nrows ? gate_activation(p.pre, gl[i] + dtv[c][i], aexp) : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[i] * LOG2E);
     }
@@ -189,7 +234,7 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     // products need block a's KI factors. Block a therefore forms its Gram products first and
     // block b its QD / KR phase; after the hand-over each does the other phase, and block b
     // builds its diagonal and off-diagonal products slab by slab without keeping any factors.
-    const float sc = p.scale;
+    const float sc = p.scale * rq;            // the output scale and q's norm factor
     bf16x4 kdC[NK];
     f32x4 Lacc = zero4(), Macc = zero4(), Lba = zero4(), Mba = zero4();
 
@@ -208,6 +253,10 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
                 float kk[4], qq[4], KD[4], KRv[4];
                 unpack_bf16x4(kr[c], kk);
                 unpack_bf16x4(qr[c], qq);
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kk[i] *= rk;
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float eA = __builtin_amdgcn_exp2f(gc[i]);
@@ -252,6 +301,10 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
                 float kk[4], qq[4];
                 unpack_bf16x4(kr[c], kk);
                 unpack_bf16x4(qr[c], qq);
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kk[i] *= rk;
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float d1 = gc[i] - ref[i];

@@ -51,6 +51,19 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
     const int64_t tok = bos + r;
 
     // ---------------------------------------------------------------- loads (TPL)
+    const bool gated = p.pre.gate != 0;             // pre-stage gate parameters
+    float aexp = 0.f;
+    f32x4 dtv[NK];
+#pragma unroll
+    for (int c = 0; c < NK; ++c) dtv[c] = zero4();
+    if (gated) {
+        aexp = __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E);
+        if (p.pre.dt_bias) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c)
+                dtv[c] = *(const f32x4 *)(p.pre.dt_bias + (size_t)j * K + 16 * c + 4 * grp);
+        }
+    }
     float qf[NK][4], kf[NK][4], gl[NK][4];
     uint2 vraw[NV];
     float beta_r = 0.f;
@@ -81,6 +94,36 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
             unpack_bf16x4(kr[c], kf[c]);
             unpack_bf16x4(gr[c], gl[c]);
         }
+        // pre-stage on the valid rows (padding rows keep q = k = g = beta = 0)
+        if (p.pre.beta_sigmoid) beta_r = sigmoid_f(beta_r);
+        if (gated) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    gl[c][i] = gate_activation(p.pre, gl[c][i] + dtv[c][i], aexp);
+        }
+    }
+    if (p.pre.qk_l2norm) {
+        // L2 norm of each token's q and k row: this lane holds a quarter of row r, the three
+        // other lane groups the rest
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int c = 0; c < NK; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sq += qf[c][i] * qf[c][i];
+                sk += kf[c][i] * kf[c][i];
+            }
+        const float rq = l2norm_factor(sum_lane_groups(sq));
+        const float rk = l2norm_factor(sum_lane_groups(sk));
+#pragma unroll
+        for (int c = 0; c < NK; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qf[c][i] *= rq;
+                kf[c][i] *= rk;
+            }
     }
 
     // ---------------------------------------------------------------- cumsum (log2 units)
@@ -239,20 +282,49 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
 
     const float *q = (const float *)p.q, *k = (const float *)p.k;
     const float *v = (const float *)p.v, *g = (const float *)p.g;
+    const bool gated = p.pre.gate != 0;              // pre-stage gate (valid rows only)
+    const float aexp = gated ? __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E) : 0.f;
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int rr = idx / K, d = idx % K;
         const bool ok = rr < nvalid;
         const int64_t t = bos + rr;
         sq[rr][d] = ok ? q[(t * p.H + h) * K + d] : 0.f;
         sk[rr][d] = ok ? k[(t * p.H + h) * K + d] : 0.f;
-        sG[rr][d] = ok ? g[(t * p.HV + j) * K + d] : 0.f;
+        float gv = ok ? g[(t * p.HV + j) * K + d] : 0.f;
+        if (gated && ok)
+            gv = gate_activation(p.pre, gv + (p.pre.dt_bias ? p.pre.dt_bias[j * K + d] : 0.f),
+                                 aexp);
+        sG[rr][d] = gv;
     }
     for (int idx = tid; idx < 16 * V; idx += 256) {
         const int rr = idx / V, d = idx % V;
         sv[rr][d] = rr < nvalid ? v[((bos + rr) * p.HV + j) * V + d] : 0.f;
     }
-    if (tid < 16) sb[tid] = tid < nvalid ? ((const float *)p.beta)[(bos + tid) * p.HV + j] : 0.f;
+    if (tid < 16) {
+        float b = tid < nvalid ? ((const float *)p.beta)[(bos + tid) * p.HV + j] : 0.f;
+        if (p.pre.beta_sigmoid && tid < nvalid) b = sigmoid_f(b);
+        sb[tid] = b;
+    }
     __syncthreads();
+    if (p.pre.qk_l2norm) {
+        // 16 threads per token row (one DPP row of lanes): partial sums, xor reduction, scale
+        const int rr = tid >> 4, l = tid & 15;
+        float a = 0.f, b = 0.f;
+        for (int d = l; d < K; d += 16) {
+            a += sq[rr][d] * sq[rr][d];
+            b += sk[rr][d] * sk[rr][d];
+        }
+        for (int m = 1; m < 16; m <<= 1) {
+            a += __shfl_xor(a, m);
+            b += __shfl_xor(b, m);
+        }
+        const float fq = l2norm_factor(a), fk = l2norm_factor(b);
+        for (int d = l; d < K; d += 16) {
+            sq[rr][d] *= fq;
+            sk[rr][d] *= fk;
+        }
+        __syncthreads();
+    }
     for (int d = tid; d < K; d += 256) {               // inclusive cumsum per key dim
         float acc = 0.f;
         for (int rr = 0; rr < 16; ++rr) { acc += sG[rr][d]; sG[rr][d] = acc; }

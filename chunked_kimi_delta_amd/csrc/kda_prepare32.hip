@@ -6,7 +6,7 @@ namespace kda {
 
 // Two chunk slots per workgroup: the second slot's inputs are loaded before the first slot is
 // processed, so their memory latency is covered by the first slot's work.
-template <int K, int V>
+template <int K, int V, bool NORM>
 __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
 {
     using WS = WsBf16x32<K, V>;
@@ -25,19 +25,24 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
     if (ok1) prep32_load<K, V>(p, bos1, nv1, j, wave, lane, in1);
     const uint8_t *ws = p.ws + (size_t)j * p.seq.n_slots * (size_t)WS::BYTES;
     if (ok0)
-        prep32_chunk<K, V>(p, sh, in0, buffer_rsrc(ws + (size_t)slot0 * WS::BYTES, WS::BYTES),
-                           wave, lane);
+        prep32_chunk<K, V, NORM>(p, sh, in0,
+                                 buffer_rsrc(ws + (size_t)slot0 * WS::BYTES, WS::BYTES), j, wave,
+                                 lane);
     if (ok0 && ok1) __syncthreads();         // the shared block is reused by the second slot
     if (ok1)
-        prep32_chunk<K, V>(p, sh, in1, buffer_rsrc(ws + (size_t)slot1 * WS::BYTES, WS::BYTES),
-                           wave, lane);
+        prep32_chunk<K, V, NORM>(p, sh, in1,
+                                 buffer_rsrc(ws + (size_t)slot1 * WS::BYTES, WS::BYTES), j, wave,
+                                 lane);
 }
 
 template <int K, int V>
 hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st)
 {
     dim3 grid((p.seq.n_slots + 1) / 2, p.HV);
-    prepare32_bf16_kernel<K, V><<<grid, dim3(128), 0, st>>>(p);
+    if (p.pre.qk_l2norm)
+        prepare32_bf16_kernel<K, V, true><<<grid, dim3(128), 0, st>>>(p);
+    else
+        prepare32_bf16_kernel<K, V, false><<<grid, dim3(128), 0, st>>>(p);
     return hipGetLastError();
 }
 

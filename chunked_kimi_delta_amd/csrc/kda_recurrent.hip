@@ -34,6 +34,12 @@ struct TokenRow {
     f32x4 qkeb[K];               // per key dim: q, k, exp(g), beta * k
 };
 
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
 }  // namespace
 
 template <int K, int V, typename T>
@@ -57,6 +63,15 @@ __global__ __launch_bounds__(64) void recurrent_kernel(FwdParams p)
     const size_t st_off = ((size_t)s * p.HV + j) * (size_t)K * V + part * 64;
     const uint32_t st_bytes = (uint32_t)(((K - 1) * V + 64) * 4);
 
+    // pre-stage gate parameters of this lane's key dims (lane, lane + 64, ...)
+    constexpr int KL = K / 64;
+    const bool gated = p.pre.gate != 0;
+    const float aexp = gated ? __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E) : 0.f;
+    float dtl[KL];
+#pragma unroll
+    for (int u = 0; u < KL; ++u)
+        dtl[u] = gated && p.pre.dt_bias ? p.pre.dt_bias[(size_t)j * K + lane + 64 * u] : 0.f;
+
     float S[K];
     if (p.h0) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.h0 + st_off, st_bytes);
@@ -70,15 +85,36 @@ __global__ __launch_bounds__(64) void recurrent_kernel(FwdParams p)
     }
 
     for (int64_t t = bos; t < eos; ++t) {
-        const float b = ld_io(beta, t * p.HV + j);
+        float b = ld_io(beta, t * p.HV + j);
+        if (p.pre.beta_sigmoid) b = sigmoid_f(b);
         // stage this token's q, k, exp(g), beta k: lane l takes key dims l, l + 64, ...
+        float qv[KL], kv[KL], gv[KL];
 #pragma unroll
-        for (int kk = lane; kk < K; kk += 64) {
-            const float qv = ld_io(q, (t * p.H + h) * K + kk);
-            const float kv = ld_io(k, (t * p.H + h) * K + kk);
-            const float gv = ld_io(g, (t * p.HV + j) * K + kk);
-            row.qkeb[kk] = f32x4{qv, kv, __builtin_amdgcn_exp2f(gv * LOG2E), b * kv};
+        for (int u = 0; u < KL; ++u) {
+            const int kk = lane + 64 * u;
+            qv[u] = ld_io(q, (t * p.H + h) * K + kk);
+            kv[u] = ld_io(k, (t * p.H + h) * K + kk);
+            gv[u] = ld_io(g, (t * p.HV + j) * K + kk);
+            if (gated) gv[u] = gate_activation(p.pre, gv[u] + dtl[u], aexp);
         }
+        if (p.pre.qk_l2norm) {          // pre-stage: the token's q and k over all K dims
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int u = 0; u < KL; ++u) {
+                sq += qv[u] * qv[u];
+                sk += kv[u] * kv[u];
+            }
+            const float rq = l2norm_factor(wave_sum(sq)), rk = l2norm_factor(wave_sum(sk));
+#pragma unroll
+            for (int u = 0; u < KL; ++u) {
+                qv[u] *= rq;
+                kv[u] *= rk;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KL; ++u)
+            row.qkeb[lane + 64 * u] =
+                f32x4{qv[u], kv[u], __builtin_amdgcn_exp2f(gv[u] * LOG2E), b * kv[u]};
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();        // one wave: orders the stage before the reads
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");

@@ -37,9 +37,10 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,  /* null required pointer, bad shape, misalignment, B != 1 with
-                                 cu_seqlens, N != B without cu_seqlens, HV % H != 0         */
+                                 cu_seqlens, N != B without cu_seqlens, HV % H != 0, a gate
+                                 without A_log, a bounded gate's lower bound not < 0         */
     KDA_ERR_UNSUPPORTED = 2,  /* K or V outside {64, 128}, unknown io dtype, chunk not
-                                 offered for this io dtype                                   */
+                                 offered for this io dtype, unknown gate                     */
     KDA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than kda_fwd_workspace_bytes()    */
     KDA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)                    */
 } kda_status;
@@ -48,6 +49,20 @@ typedef enum {
     KDA_BF16 = 0,             /* q, k, v, g, beta, o in bf16; states fp32; fp32 accumulation */
     KDA_FP32 = 1              /* everything fp32                                             */
 } kda_dtype;
+
+/* Gate activation applied to g before use (kda_fwd_args.gate). With value head j and key dim
+   d, x = g[t, j, d] + dt_bias[j, d]:
+     KDA_GATE_NONE      g is the log decay as given
+     KDA_GATE_SOFTPLUS  g <- -exp(A_log[j]) * log(1 + exp(x))       ("手撕KDA" section 2.1,
+                                                                      the C++ pre-stage)
+     KDA_GATE_BOUNDED   g <- lower_bound / (1 + exp(-exp(A_log[j]) * x))
+                        ("KDA源码剖析之FlashKDA（上）" part 7, gate activation; lower_bound < 0,
+                        so the log decay lies in (lower_bound, 0))                          */
+typedef enum {
+    KDA_GATE_NONE = 0,
+    KDA_GATE_SOFTPLUS = 1,
+    KDA_GATE_BOUNDED = 2
+} kda_gate;
 
 typedef struct {
     /* Shapes. Dense batch: q is [B, T, H, K] and sequence b spans tokens [b*T, (b+1)*T) of
@@ -86,6 +101,16 @@ typedef struct {
                                  dominates), or 0 for the default: 1 for a dense batch with
                                  T <= 16, else 32 for bf16 io and 16 for fp32 io. Results agree
                                  to rounding.                                                */
+    /* Pre-stage, fused into the kernels that read the inputs (all zero: inputs used as given;
+       "KDA源码剖析之FlashKDA（上）" parts 6, 7 and 10; "手撕KDA" section 2.1). The activated
+       values replace q, k, g, beta everywhere above, including the g limit of `g`.           */
+    int32_t qk_l2norm;        /* nonzero: q and k of every token and q/k head are divided by
+                                 sqrt(sum over the K dims of the squares + 1e-6)             */
+    int32_t beta_sigmoid;     /* nonzero: beta <- 1 / (1 + exp(-beta))                       */
+    int32_t gate;             /* kda_gate                                                    */
+    float gate_lower_bound;   /* KDA_GATE_BOUNDED: finite and < 0                            */
+    const float *A_log;       /* [HV] fp32 device, one per value head; required for a gate   */
+    const float *dt_bias;     /* [HV, K] fp32 device (16-byte aligned), or NULL for zeros    */
 } kda_fwd_args;
 
 /* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).

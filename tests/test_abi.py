@@ -117,7 +117,7 @@ def test_strerror_and_version(lib):
     for st in range(5):
         assert kda._lib.strerror(st)
     assert "unknown" in kda._lib.strerror(99)
-    assert lib.kda_version() == 102
+    assert lib.kda_version() == 103
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):
@@ -135,3 +135,27 @@ def test_product_package_never_imports_the_oracle():
             src = open(path, encoding="utf-8").read()
             assert not re.search(r"^\s*(from|import)\s+oracle", src, flags=re.M), path
             assert "kda_oracle" not in src, path
+
+
+def test_prestage_arguments_are_checked(lib):
+    # gate validation comes before the workspace check (fake, never dereferenced pointers)
+    fake = 1 << 40
+    def mk(**kw):
+        a = args(T=32, **kw)
+        for name in ("q", "k", "v", "g", "beta", "o"):
+            setattr(a, name, fake)
+        return a
+    call = lambda a: lib.kda_fwd(ctypes.byref(a), None, 0, None)
+    assert call(mk(gate=3)) == _lib.KDA_ERR_UNSUPPORTED
+    assert call(mk(gate=1)) == _lib.KDA_ERR_INVALID_ARG                 # no A_log
+    assert call(mk(gate=2, A_log=fake, gate_lower_bound=0.5)) == _lib.KDA_ERR_INVALID_ARG
+    assert call(mk(gate=2, A_log=fake, gate_lower_bound=float("nan"))) == \
+        _lib.KDA_ERR_INVALID_ARG
+    assert call(mk(gate=1, A_log=fake, dt_bias=fake + 4)) == _lib.KDA_ERR_INVALID_ARG
+    # valid pre-stage arguments reach the workspace check
+    assert call(mk(gate=2, A_log=fake, gate_lower_bound=-5.0, dt_bias=fake, qk_l2norm=1,
+                   beta_sigmoid=1)) == _lib.KDA_ERR_WORKSPACE
+    assert call(mk(gate=1, A_log=fake + 4)) == _lib.KDA_ERR_WORKSPACE
+    # the workspace size does not depend on the pre-stage
+    f = lambda a: lib.kda_fwd_workspace_bytes(ctypes.byref(a))
+    assert f(mk(gate=1, A_log=fake, qk_l2norm=1)) == f(mk())

@@ -283,3 +283,96 @@ def test_default_chunk_short_dense_batches(T):
     o, fin = gpu_run(inp, chunk=0)
     o_ref, f_ref = oracle_run(inp)
     check_all(inp, o, fin, o_ref, f_ref, TOL["bf16"])
+
+
+# --------------------------------------------------------------------------- fused pre-stage
+
+def raw_plan(raw, chunk, pre, output_final_state=True):
+    inp = raw.inp
+    return kda.KdaFwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                          cu_seqlens=dev(inp.cu_seqlens), initial_state=dev(inp.h0),
+                          output_final_state=output_final_state, chunk=chunk,
+                          use_qk_l2norm=pre.get("l2", False),
+                          use_beta_sigmoid=pre.get("sig", False), gate=pre.get("gate"),
+                          A_log=dev(raw.A_log), dt_bias=dev(raw.dt_bias),
+                          gate_lower_bound=pre.get("lb", -5.0))
+
+
+def raw_oracle(raw, pre, units=None):
+    # the pre-stage in fp64 (oracle/prestage.py), then the recurrence: fp64 numpy for small
+    # cases; the C recurrence (inputs rounded to fp32, ~1e-7) when units are sampled
+    from oracle.prestage import prestage
+    from oracle.recurrent import kda_recurrent
+    inp = raw.inp
+    f = W.as_f32_numpy
+    q, k, g, beta = prestage(f(inp.q), f(inp.k), f(inp.g), f(inp.beta),
+                             qk_l2norm=pre.get("l2", False), beta_sigmoid=pre.get("sig", False),
+                             gate=pre.get("gate"), A_log=raw.A_log.numpy(),
+                             dt_bias=raw.dt_bias.numpy(), lower_bound=pre.get("lb", -5.0))
+    h0 = None if inp.h0 is None else inp.h0.numpy()
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    if units is None:
+        return kda_recurrent(q, k, f(inp.v), g, beta, inp.scale, h0, cu)
+    return kda_oracle_c(q, k, f(inp.v), g, beta, inp.scale, h0, cu, units=units)
+
+
+PRE_SHAPES = {
+    "bf16_gva_b2_t100_h0": W.custom(B=2, T=100, H=2, HV=4, K=128, V=128, h0_std=0.1),
+    "bf16_varlen_edges": W.custom(H=1, HV=2, K=128, V=128, h0_std=0.1,
+                                  lengths=(0, 1, 17, 33, 64)),
+    "bf16_k64v64_t50": W.custom(B=1, T=50, H=2, HV=2, K=64, V=64),
+    "fp32_k128v64_t70": W.custom(B=1, T=70, H=1, HV=2, K=128, V=64, dtype="fp32"),
+}
+PRE_CASES = [(n, c, gate) for n in PRE_SHAPES for c in CHUNKS[PRE_SHAPES[n].dtype]
+             for gate in ("softplus", "bounded")]
+
+
+@pytest.mark.parametrize("name,chunk,gate", PRE_CASES)
+def test_prestage_parity(name, chunk, gate):
+    # raw q/k, raw gate input, beta logits: all three pre-stage steps inside the kernels
+    w = PRE_SHAPES[name]
+    raw = W.make_raw_inputs(w, seed=21)
+    pre = {"l2": True, "sig": True, "gate": gate, "lb": -4.0}
+    plan = raw_plan(raw, chunk, pre)
+    o, fin = plan()
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    fin = fin.cpu().numpy().astype(np.float64)
+    o_ref, f_ref = raw_oracle(raw, pre)
+    check_all(raw.inp, o, fin, o_ref, f_ref, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("pre", [{"l2": True}, {"sig": True}, {"gate": "softplus"},
+                                 {"gate": "bounded", "lb": -2.5}],
+                         ids=["l2norm", "beta_sigmoid", "softplus_gate", "bounded_gate"])
+def test_prestage_steps_one_at_a_time(pre, chunk):
+    w = W.custom(B=1, T=77, H=2, HV=2, K=128, V=128, h0_std=0.1)
+    raw = W.make_raw_inputs(w, seed=22)
+    if not pre.get("sig"):           # logits are not a valid beta: use a plain one
+        raw.inp.beta = torch.sigmoid(raw.inp.beta.float()).to(raw.inp.beta.dtype)
+    if not pre.get("l2"):            # unnormalised q, k of std 2 would make the state blow up
+        raw.inp.q = (raw.inp.q.float() / 23.0).to(raw.inp.q.dtype)
+        raw.inp.k = (raw.inp.k.float() / 23.0).to(raw.inp.k.dtype)
+    if not pre.get("gate"):          # the raw gate input is not a decay: use a plain one
+        raw.inp.g = (-torch.rand(raw.inp.g.shape, generator=torch.Generator().manual_seed(3))
+                     * 0.1).to(raw.inp.g.dtype)
+    o, fin = raw_plan(raw, chunk, pre)()
+    torch.cuda.synchronize()
+    o_ref, f_ref = raw_oracle(raw, pre)
+    check_all(raw.inp, o.float().cpu().numpy().astype(np.float64),
+              fin.cpu().numpy().astype(np.float64), o_ref, f_ref, TOL["bf16"])
+
+
+def test_prestage_full_size_bounded_gate():
+    # the throughput shape with raw inputs and FlashKDA's bounded gate (lower bound -5), every
+    # unit against the oracle
+    w = W.WORKLOADS["h16_t4096"]
+    raw = W.make_raw_inputs(w, seed=0)
+    pre = {"l2": True, "sig": True, "gate": "bounded", "lb": -5.0}
+    o, fin = raw_plan(raw, 32, pre)()
+    torch.cuda.synchronize()
+    units = [(0, j) for j in range(w.HV)]
+    o_ref, f_ref = raw_oracle(raw, pre, units=units)
+    check_all(raw.inp, o.float().cpu().numpy().astype(np.float64),
+              fin.cpu().numpy().astype(np.float64), o_ref, f_ref, TOL["bf16"])

@@ -153,6 +153,47 @@ def make_inputs(w: Workload, seed: int = 0, g_override=None, beta_override=None)
     return Inputs(w, q, k, v, g, beta, h0, cu, scale=w.K ** -0.5)
 
 
+@dataclasses.dataclass
+class RawInputs:
+    """Raw projections for the fused pre-stage: q, k not normalised, g the raw gate input,
+    beta logits, plus the per-value-head gate parameters (fp32)."""
+    inp: Inputs                     # q, k, g, beta raw (io dtype); v, h0, cu_seqlens as usual
+    A_log: torch.Tensor             # [HV] fp32
+    dt_bias: torch.Tensor           # [HV, K] fp32
+
+
+def make_raw_inputs(w: Workload, seed: int = 0, qk_std: float = 2.0, g_mean: float = -1.0,
+                    A_lo: float = 0.5, A_hi: float = 2.0, dt_std: float = 0.5) -> RawInputs:
+    """Draw one seeded raw input set (CPU tensors) in the order lengths, q, k, v, g_raw,
+    beta_raw, h0, A_log, dt_bias:
+      q, k ~ N(0, qk_std) (not normalised)     v ~ N(0, 1)
+      g_raw ~ N(g_mean, 1)                      beta_raw ~ N(0, beta_std)
+      A_log = log U(A_lo, A_hi) per value head  dt_bias ~ N(0, dt_std) per value head and dim
+    With the softplus gate the log decay per token stays above about -2 A_hi * 1.5, so any 16
+    consecutive tokens sum well above -88 (the chunked kernels' range)."""
+    gen = torch.Generator().manual_seed(seed)
+    cu = None
+    B, T = w.B, w.T
+    if w.n_seqs is not None or w.lengths is not None:
+        lens = draw_lengths(w, gen)
+        B, T = 1, int(sum(lens))
+        cu = torch.tensor([0] + list(torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0)),
+                          dtype=torch.int64)
+    dt = _torch_dtype(w.dtype)
+    q = (torch.randn(B, T, w.H, w.K, generator=gen) * qk_std).to(dt)
+    k = (torch.randn(B, T, w.H, w.K, generator=gen) * qk_std).to(dt)
+    v = torch.randn(B, T, w.HV, w.V, generator=gen).to(dt)
+    g = (torch.randn(B, T, w.HV, w.K, generator=gen) + g_mean).to(dt)
+    beta = (torch.randn(B, T, w.HV, generator=gen) * w.beta_std).to(dt)
+    N = B if cu is None else cu.numel() - 1
+    h0 = None
+    if w.h0_std is not None:
+        h0 = torch.randn(N, w.HV, w.K, w.V, generator=gen) * w.h0_std
+    A_log = torch.log(torch.rand(w.HV, generator=gen) * (A_hi - A_lo) + A_lo)
+    dt_bias = torch.randn(w.HV, w.K, generator=gen) * dt_std
+    return RawInputs(Inputs(w, q, k, v, g, beta, h0, cu, scale=w.K ** -0.5), A_log, dt_bias)
+
+
 def as_f32_numpy(x: Optional[torch.Tensor]):
     """Exact fp32 copy of an io-dtype tensor (bf16 -> fp32 is exact) as a numpy array."""
     if x is None:
