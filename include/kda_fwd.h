@@ -11,10 +11,12 @@
  *     S <- S + beta[t, j] k[t, h, :] r^T;   o[t, j, :] = scale * S^T q[t, h, :]
  *
  * and final_state[s, j] is S after the last token. The library evaluates it in the chunked
- * form of the same section with chunks of 16 tokens: a token-parallel prepare kernel (in-chunk
- * cumsum of g, decayed q/k, the strictly lower triangular L and the masked Mqk, the inverse of
- * (I + L) by the Neumann doubling product of "KDA源码剖析之FlashKDA（上）" part 12, and
- * w = A (exp(G) k), u = A v) followed by a chunk-sequential state kernel.
+ * form of the same section with chunks of 16 or 32 tokens: a token-parallel prepare kernel
+ * (in-chunk cumsum of g, decayed q/k, the strictly lower triangular L and the masked Mqk, the
+ * inverse of (I + L) by the Neumann doubling product of "KDA源码剖析之FlashKDA（上）" part 12,
+ * and w = A (exp(G) k), u = A v) followed by a chunk-sequential state kernel; or token by token
+ * (chunk 1, for decoding). Optionally the kernels first apply the pre-stage that turns raw
+ * projections into q, k, g, beta (q/k L2 norm, beta sigmoid, a gate activation).
  *
  * Conventions
  *  - All tensor pointers are DEVICE pointers, caller-owned, contiguous (row-major), and
