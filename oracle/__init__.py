@@ -18,6 +18,9 @@ Contents
   prestage.py     fp64 pre-stage: q/k L2 normalisation, beta sigmoid and the two gate
                   activations (softplus and bounded sigmoid) that produce the recurrence's
                   q, k, g, beta from raw projections.
+  backward.py     fp64 gradients of the forward (dq, dk, dv, dg, dbeta, dh0): the reverse-mode
+                  token recurrence, derived by hand, plus torch.autograd on the fp64 forward
+                  as an independent check.
   native.py       ctypes loader for the C oracle.
   build.py        compiles kda_oracle.c with gcc.
 
