@@ -141,6 +141,91 @@ class KdaFwdPlan:
         return self.o, self.final_state
 
 
+class KdaBwdPlan:
+    """Validated arguments for repeated kda_bwd calls: gradients of the forward with respect to
+    q, k, v, g, beta (and initial_state) from d_o (like v) and dht (fp32 [N,HV,K,V] or None).
+
+    Inputs as for KdaFwdPlan without the pre-stage (the gradients are those of q, k, g, beta as
+    the recurrence reads them). Outputs, allocated once through torch and reused by every
+    call(), all fp32: dq, dk [B,T,H,K]; dv [B,T,HV,V]; dg [B,T,HV,K]; dbeta [B,T,HV]; dh0
+    [N,HV,K,V] (when want_dh0).
+    """
+
+    def __init__(self, q, k, v, g, beta, d_o, dht=None, scale=None, cu_seqlens=None,
+                 initial_state=None, want_dh0=True, workspace=None):
+        self.lib = load()
+        if q.dtype not in _IO:
+            raise TypeError(f"unsupported io dtype {q.dtype} (bf16 or fp32)")
+        dev = q.device
+        if dev.type != "cuda":
+            raise ValueError("inputs must be on a HIP device")
+        B, T, H, K = q.shape
+        HV, V = v.shape[2], v.shape[3]
+        dt = q.dtype
+        for t, name, shape in ((q, "q", (B, T, H, K)), (k, "k", (B, T, H, K)),
+                               (v, "v", (B, T, HV, V)), (g, "g", (B, T, HV, K)),
+                               (beta, "beta", (B, T, HV)), (d_o, "d_o", (B, T, HV, V))):
+            _check(t, name, dt, shape, dev)
+        if cu_seqlens is not None:
+            if cu_seqlens.dtype != torch.int64 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+                raise ValueError("cu_seqlens must be a 1-D int64 tensor on the inputs' device")
+            N = cu_seqlens.numel() - 1
+        else:
+            N = B
+        if initial_state is not None:
+            _check(initial_state, "initial_state", torch.float32, (N, HV, K, V), dev)
+        if dht is not None:
+            _check(dht, "dht", torch.float32, (N, HV, K, V), dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dq = torch.empty(B, T, H, K, **f32)
+        self.dk = torch.empty(B, T, H, K, **f32)
+        self.dv = torch.empty(B, T, HV, V, **f32)
+        self.dg = torch.empty(B, T, HV, K, **f32)
+        self.dbeta = torch.empty(B, T, HV, **f32)
+        self.dh0 = torch.empty(N, HV, K, V, **f32) if want_dh0 else None
+        a = KdaFwdArgs()
+        a.B, a.T, a.N, a.H, a.HV, a.K, a.V, a.io = B, T, N, H, HV, K, V, _IO[dt]
+        a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+        a.scale = float("nan") if scale is None else float(scale)
+        a.cu_seqlens = _ptr(cu_seqlens)
+        a.initial_state = _ptr(initial_state)
+        a.chunk = 16
+        self.args = a
+        self._keep = (q, k, v, g, beta, d_o, dht, cu_seqlens, initial_state)
+        self._ptrs = [_ptr(d_o), _ptr(dht)]
+        self._outs = [_ptr(x) for x in (self.dq, self.dk, self.dv, self.dg, self.dbeta,
+                                        self.dh0)]
+        need = int(self.lib.kda_bwd_workspace_bytes(ctypes.byref(a)))
+        if need == 0:
+            raise ValueError("unsupported shapes (K, V in {64, 128}; HV % H == 0)")
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        elif workspace.numel() < need:
+            raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+        self.workspace = workspace
+        self.ws_bytes = workspace.numel()
+        self.device = dev
+
+    def __call__(self, stream=None):
+        """Enqueue the backward on `stream` (default: torch's current stream); returns
+        (dq, dk, dv, dg, dbeta, dh0)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        st = self.lib.kda_bwd(ctypes.byref(self.args), *self._ptrs,
+                              ctypes.c_void_p(self.workspace.data_ptr()), self.ws_bytes,
+                              *self._outs, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"kda_bwd failed: {strerror(st)} ({st})")
+        return self.dq, self.dk, self.dv, self.dg, self.dbeta, self.dh0
+
+
+def kda_bwd(q, k, v, g, beta, d_o, dht=None, scale=None, cu_seqlens=None, initial_state=None,
+            want_dh0=True):
+    """KDA backward. Returns fp32 (dq, dk, dv, dg, dbeta, dh0 or None); see KdaBwdPlan."""
+    return KdaBwdPlan(q, k, v, g, beta, d_o, dht, scale, cu_seqlens, initial_state,
+                      want_dh0)()
+
+
 def kda_fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
             output_final_state=True, workspace=None, chunk=0, **prestage):
     """KDA forward. Returns (o, final_state or None); see KdaFwdPlan for shapes and the

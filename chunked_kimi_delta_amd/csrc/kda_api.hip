@@ -148,9 +148,118 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Backward workspace: the fp32 chunk records, then S at the start and Lam at the end of every
+// chunk slot, then (G > 1) per-value-head dq and dk. Offsets in bytes, each 256-aligned.
+struct BwdLayout {
+    size_t rec, ck_S, ck_L, part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Shape checks of the backward (the forward's, at chunk 16 with no pre-stage) and its layout.
+kda_status check_bwd(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots, BwdLayout *L)
+{
+    if (!a) return KDA_ERR_INVALID_ARG;
+    if (a->chunk != 0 && a->chunk != 16) return KDA_ERR_UNSUPPORTED;
+    if (a->qk_l2norm || a->beta_sigmoid || a->gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
+    kda_fwd_args c = *a;
+    c.chunk = 16;
+    size_t rec;
+    int ct;
+    const kda_status st = check_shapes(&c, T_total, n_slots, &rec, &ct);
+    if (st != KDA_OK) return st;
+    rec = (size_t)*n_slots * (size_t)a->HV * record_bytes<WsF32>(a->K, a->V);  // fp32 records
+    const size_t state = (size_t)*n_slots * (size_t)a->HV * (size_t)a->K * (size_t)a->V * 4;
+    const size_t part = a->HV > a->H ? (size_t)*T_total * (size_t)a->HV * (size_t)a->K * 4 : 0;
+    L->rec = 0;
+    L->ck_S = align256(rec);
+    L->ck_L = L->ck_S + align256(state);
+    L->part = L->ck_L + align256(state);
+    L->total = L->part + 2 * align256(part);
+    return KDA_OK;
+}
+
+template <int K, int V>
+hipError_t dispatch_bwd(const BwdParams &b, int io, hipStream_t st)
+{
+    return launch_backward<K, V>(b, io == KDA_BF16, st);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t kda_bwd_workspace_bytes(const kda_fwd_args *a)
+{
+    int64_t tt, ns;
+    BwdLayout L;
+    if (check_bwd(a, &tt, &ns, &L) != KDA_OK) return 0;
+    return L.total;
+}
+
+kda_status kda_bwd(const kda_fwd_args *a, const void *d_o, const float *dht, void *workspace,
+                   size_t ws_bytes, float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                   float *dh0, void *stream)
+{
+    int64_t tt, ns;
+    BwdLayout L;
+    const kda_status st = check_bwd(a, &tt, &ns, &L);
+    if (st != KDA_OK) return st;
+    if (tt > 0) {
+        const void *ptrs[] = {a->q, a->k, a->v, a->g, a->beta, d_o, dq, dk, dv, dg, dbeta};
+        for (const void *ptr : ptrs)
+            if (!ptr || !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    }
+    const void *opt[] = {a->initial_state, a->cu_seqlens, dht, dh0};
+    for (const void *ptr : opt)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    if (tt > 0 && (!workspace || ws_bytes < L.total || ((uintptr_t)workspace & 255u)))
+        return KDA_ERR_WORKSPACE;
+    if (a->N == 0) return KDA_OK;
+
+    BwdParams b = {};
+    FwdParams &p = b.f;
+    p.seq.cu = a->cu_seqlens;
+    p.seq.T = a->T;
+    p.seq.T_total = tt;
+    p.seq.N = a->N;
+    p.seq.n_slots = (int32_t)ns;
+    p.H = a->H;
+    p.HV = a->HV;
+    p.G = a->HV / a->H;
+    p.scale = (a->scale > 0.f && !isnan(a->scale)) ? a->scale : 1.0f / sqrtf((float)a->K);
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.g = a->g;
+    p.beta = a->beta;
+    p.h0 = a->initial_state;
+    p.o = nullptr;
+    p.ht = nullptr;
+    uint8_t *ws = (uint8_t *)workspace;
+    p.ws = ws;                                    // pre-stage fields stay zero (off)
+    b.d_o = d_o;
+    b.dht = dht;
+    b.ck_S = ws ? (float *)(ws + L.ck_S) : nullptr;
+    b.ck_L = ws ? (float *)(ws + L.ck_L) : nullptr;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.dg = dg;
+    b.dbeta = dbeta;
+    b.dh0 = dh0;
+    b.part_q = ws && p.G > 1 ? (float *)(ws + L.part) : nullptr;
+    b.part_k = ws && p.G > 1 ? (float *)(ws + L.part + (L.total - L.part) / 2) : nullptr;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (a->K == 64)
+        e = a->V == 64 ? dispatch_bwd<64, 64>(b, a->io, s) : dispatch_bwd<64, 128>(b, a->io, s);
+    else
+        e = a->V == 64 ? dispatch_bwd<128, 64>(b, a->io, s)
+                       : dispatch_bwd<128, 128>(b, a->io, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
 
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *a)
 {
@@ -184,13 +293,13 @@ const char *kda_strerror(int status)
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED:
         return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 with bf16 io; "
-               "gate 0, 1 or 2)";
+               "gate 0, 1 or 2; the backward: chunk 16, no pre-stage)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
     }
 }
 
-int kda_version(void) { return 103; }
+int kda_version(void) { return 104; }
 
 }  // extern "C"

@@ -68,6 +68,21 @@ struct FwdParams {
     Prestage pre;
 };
 
+// Arguments of the backward: the forward's (f.ws holds the fp32 chunk records), the incoming
+// gradients, the per-chunk state records and the gradient outputs (all fp32).
+struct BwdParams {
+    FwdParams f;
+    const void *d_o;          // d loss / d o, [T_total][HV][V] in the input storage type
+    const float *dht;         // d loss / d final_state, [N][HV][K][V] or null (zero)
+    float *ck_S, *ck_L;       // [HV][n_slots][K][V]: S at the start / Lam at the end of a chunk
+    float *dq, *dk;           // [T_total][H][K]
+    float *dv;                // [T_total][HV][V]
+    float *dg;                // [T_total][HV][K]
+    float *dbeta;             // [T_total][HV]
+    float *dh0;               // [N][HV][K][V] or null
+    float *part_q, *part_k;   // [T_total][HV][K] per-value-head dq, dk (G > 1 only)
+};
+
 // Workspace of one (value head, slot) chunk, bf16 io. All fragments are stored in the exact
 // per-lane order the state kernel's MFMAs consume, so every state-kernel load is a contiguous
 // 64-lane vector load:
@@ -345,9 +360,13 @@ __device__ __forceinline__ void vm_drain() {
 namespace kda {
 template <int K, int V> hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state_bf16(const FwdParams &p, hipStream_t st);
-template <int K, int V> hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st);
+// fp32 chunk records (WsF32) from fp32 or (in_bf16) bf16 inputs
+template <int K, int V>
+hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16 = false);
 template <int K, int V> hipError_t launch_state_f32(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_recurrent(const FwdParams &p, int io, hipStream_t st);
+template <int K, int V>
+hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st);
 }  // namespace kda

@@ -266,8 +266,15 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
 // =============================================================================== fp32 io
 // Plain fp32 evaluation of the same chunk quantities (a correctness mode: no MFMA, the
 // decayed Gram entries use exp of the exact exponent difference, the inverse is the same
-// Neumann doubling product). One 256-thread block per (chunk, value head).
-template <int K, int V>
+// Neumann doubling product). One 256-thread block per (chunk, value head). T is the storage
+// type of the inputs (float for fp32 io; uint16_t bf16 bits for the backward of bf16 io, which
+// evaluates the chunks in fp32 from the same inputs).
+__device__ __forceinline__ float ld_in(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_in(const uint16_t *p, int64_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+template <int K, int V, typename T>
 __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
 {
     using WS = WsF32<K, V>;
@@ -280,17 +287,17 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     int nvalid;
     if (!locate_slot(p.seq, slot, &s, &bos, &nvalid)) return;
 
-    const float *q = (const float *)p.q, *k = (const float *)p.k;
-    const float *v = (const float *)p.v, *g = (const float *)p.g;
+    const T *q = (const T *)p.q, *k = (const T *)p.k;
+    const T *v = (const T *)p.v, *g = (const T *)p.g;
     const bool gated = p.pre.gate != 0;              // pre-stage gate (valid rows only)
     const float aexp = gated ? __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E) : 0.f;
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int rr = idx / K, d = idx % K;
         const bool ok = rr < nvalid;
         const int64_t t = bos + rr;
-        sq[rr][d] = ok ? q[(t * p.H + h) * K + d] : 0.f;
-        sk[rr][d] = ok ? k[(t * p.H + h) * K + d] : 0.f;
-        float gv = ok ? g[(t * p.HV + j) * K + d] : 0.f;
+        sq[rr][d] = ok ? ld_in(q, (t * p.H + h) * K + d) : 0.f;
+        sk[rr][d] = ok ? ld_in(k, (t * p.H + h) * K + d) : 0.f;
+        float gv = ok ? ld_in(g, (t * p.HV + j) * K + d) : 0.f;
         if (gated && ok)
             gv = gate_activation(p.pre, gv + (p.pre.dt_bias ? p.pre.dt_bias[j * K + d] : 0.f),
                                  aexp);
@@ -298,10 +305,10 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     }
     for (int idx = tid; idx < 16 * V; idx += 256) {
         const int rr = idx / V, d = idx % V;
-        sv[rr][d] = rr < nvalid ? v[((bos + rr) * p.HV + j) * V + d] : 0.f;
+        sv[rr][d] = rr < nvalid ? ld_in(v, ((bos + rr) * p.HV + j) * V + d) : 0.f;
     }
     if (tid < 16) {
-        float b = tid < nvalid ? ((const float *)p.beta)[(bos + tid) * p.HV + j] : 0.f;
+        float b = tid < nvalid ? ld_in((const T *)p.beta, (bos + tid) * p.HV + j) : 0.f;
         if (p.pre.beta_sigmoid && tid < nvalid) b = sigmoid_f(b);
         sb[tid] = b;
     }
@@ -389,16 +396,19 @@ hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st)
 }
 
 template <int K, int V>
-hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st)
+hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16)
 {
     dim3 grid(p.seq.n_slots, p.HV);
-    prepare_f32_kernel<K, V><<<grid, dim3(256), 0, st>>>(p);
+    if (in_bf16)
+        prepare_f32_kernel<K, V, uint16_t><<<grid, dim3(256), 0, st>>>(p);
+    else
+        prepare_f32_kernel<K, V, float><<<grid, dim3(256), 0, st>>>(p);
     return hipGetLastError();
 }
 
 #define KDA_INST(K, V)                                                               \
     template hipError_t launch_prepare_bf16<K, V>(const FwdParams &, hipStream_t);  \
-    template hipError_t launch_prepare_f32<K, V>(const FwdParams &, hipStream_t);
+    template hipError_t launch_prepare_f32<K, V>(const FwdParams &, hipStream_t, bool);
 KDA_INST(64, 64)
 KDA_INST(64, 128)
 KDA_INST(128, 64)

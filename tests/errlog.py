@@ -6,3 +6,7 @@ PENDING: list[str] = []
 
 def report(eo: float, ef: float) -> None:
     PENDING.append(f"[err] rel L2 o={eo:.3e} final={ef:.3e}")
+
+
+def report_named(**errs: float) -> None:
+    PENDING.append("[err] rel L2 " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))

@@ -34,7 +34,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["kda_fwd", "kda_fwd_prepare", "kda_fwd_state",
+    assert declared_functions() == ["kda_bwd", "kda_bwd_workspace_bytes", "kda_fwd",
+                                    "kda_fwd_prepare", "kda_fwd_state",
                                     "kda_fwd_workspace_bytes", "kda_strerror", "kda_version"]
 
 
@@ -117,7 +118,7 @@ def test_strerror_and_version(lib):
     for st in range(5):
         assert kda._lib.strerror(st)
     assert "unknown" in kda._lib.strerror(99)
-    assert lib.kda_version() == 103
+    assert lib.kda_version() == 104
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):
@@ -159,3 +160,43 @@ def test_prestage_arguments_are_checked(lib):
     # the workspace size does not depend on the pre-stage
     f = lambda a: lib.kda_fwd_workspace_bytes(ctypes.byref(a))
     assert f(mk(gate=1, A_log=fake, qk_l2norm=1)) == f(mk())
+
+
+def test_bwd_workspace_bytes(lib):
+    f = lambda a: lib.kda_bwd_workspace_bytes(ctypes.byref(a))
+    up = lambda x: (x + 255) // 256 * 256
+    for kw in (dict(), dict(K=64, V=128), dict(B=2, N=2, T=45, H=4, HV=8, K=64, V=64),
+               dict(io=1, chunk=0)):
+        a = args(**kw)
+        B, T, N, H, HV, K, V = (getattr(a, n) for n in ("B", "T", "N", "H", "HV", "K", "V"))
+        slots = B * T // 16 + N
+        rec = lib.kda_fwd_workspace_bytes(ctypes.byref(args(**dict(kw, io=1, chunk=16))))
+        part = B * T * HV * K * 4 if HV > H else 0
+        assert f(a) == up(rec) + 2 * up(slots * HV * K * V * 4) + 2 * up(part), kw
+    assert f(args(chunk=32)) == 0 and f(args(chunk=1)) == 0     # 16-token chunks only
+    assert f(args(qk_l2norm=1)) == 0 and f(args(gate=1)) == 0   # no pre-stage
+    assert f(args(K=96)) == 0 and f(args(HV=24)) == 0
+
+
+def test_kda_bwd_rejects_bad_arguments(lib):
+    fake = 1 << 40                                 # never dereferenced: rejected before launch
+    call = lambda a, **kw: lib.kda_bwd(
+        ctypes.byref(a), kw.get("do"), kw.get("dht"), kw.get("ws"), kw.get("nbytes", 0),
+        *[kw.get(n, fake) for n in ("dq", "dk", "dv", "dg", "dbeta")], kw.get("dh0"), None)
+    a = args(T=32)
+    assert call(a, do=fake) == _lib.KDA_ERR_INVALID_ARG          # null q, k, v, g, beta
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(a, name, fake)
+    assert call(a) == _lib.KDA_ERR_INVALID_ARG                   # null d_o
+    assert call(a, do=fake, dq=None) == _lib.KDA_ERR_INVALID_ARG  # null output
+    assert call(a, do=fake, dh0=fake + 4) == _lib.KDA_ERR_INVALID_ARG
+    assert call(a, do=fake) == _lib.KDA_ERR_WORKSPACE
+    need = lib.kda_bwd_workspace_bytes(ctypes.byref(a))
+    assert call(a, do=fake, ws=fake, nbytes=need - 1) == _lib.KDA_ERR_WORKSPACE
+    assert call(a, do=fake, ws=fake + 16, nbytes=need) == _lib.KDA_ERR_WORKSPACE
+    assert call(args(T=32, chunk=32), do=fake) == _lib.KDA_ERR_UNSUPPORTED
+    assert call(args(T=32, beta_sigmoid=1), do=fake) == _lib.KDA_ERR_UNSUPPORTED
+    assert call(args(T=32, K=96), do=fake) == _lib.KDA_ERR_UNSUPPORTED
+    assert call(args(T=32, N=2), do=fake) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_bwd(None, None, None, None, 0, *([None] * 6), None) == \
+        _lib.KDA_ERR_INVALID_ARG

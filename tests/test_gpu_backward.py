@@ -1,0 +1,168 @@
+"""GPU parity of the backward (kda_bwd through the C ABI) against the fp64 oracle of
+oracle/backward.py, element by element.
+
+Bar: relative L2 error ||x_gpu - x_ref|| / ||x_ref|| of each gradient tensor (dq, dk, dv, dg,
+dbeta, dh0), computed in fp64, <= 1e-4 for bf16 and fp32 io alike: the kernels compute in fp32
+from exactly the values the oracle reads (bf16 -> fp32 is exact), so the only error is fp32
+rounding, as for the forward's fp32 io. Small cases compare every element; the full-size
+workloads compare a seeded sample of whole units (all tokens of one sequence and one q/k head
+with its value heads) and check finiteness everywhere.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from errlog import report_named
+from oracle.backward import kda_backward_recurrent
+
+import chunked_kimi_delta_amd as kda
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def dev(x):
+    return None if x is None else x.to(DEV).contiguous()
+
+
+def f64(x):
+    return None if x is None else x.float().cpu().numpy().astype(np.float64)
+
+
+def gpu_bwd(inp: W.Inputs, gr: W.Grads):
+    plan = kda.KdaBwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                          dev(gr.d_o), dev(gr.dht), scale=inp.scale,
+                          cu_seqlens=dev(inp.cu_seqlens), initial_state=dev(inp.h0))
+    out = plan()
+    torch.cuda.synchronize()
+    return tuple(f64(x) for x in out)
+
+
+def oracle_bwd(inp: W.Inputs, gr: W.Grads):
+    f = W.as_f32_numpy
+    return kda_backward_recurrent(
+        f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.scale,
+        None if inp.h0 is None else inp.h0.numpy(),
+        None if inp.cu_seqlens is None else inp.cu_seqlens.numpy(),
+        f(gr.d_o), None if gr.dht is None else gr.dht.numpy())
+
+
+def rel_l2(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+
+def check_grads(got, ref, tol=TOL):
+    errs = {}
+    for name, a, b in zip(NAMES, got, ref):
+        b = np.asarray(b).reshape(a.shape)
+        assert np.isfinite(a).all(), name
+        errs[name] = rel_l2(a, b)
+    report_named(**errs)
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, f"rel L2 above {tol}: {bad}"
+
+
+SMALL = {
+    "fp32_t64": W.WORKLOADS["tiny_fp32"],
+    "fp32_t45_h0": W.custom(B=1, T=45, H=1, HV=1, K=64, V=64, dtype="fp32", h0_std=0.5),
+    "bf16_b2_t100_gva_h0": W.custom(B=2, T=100, H=2, HV=4, K=128, V=128, h0_std=0.1),
+    "bf16_k64v128_t50": W.custom(B=1, T=50, H=1, HV=2, K=64, V=128),
+    "bf16_k128v64_t50_h0": W.custom(B=1, T=50, H=2, HV=2, K=128, V=64, h0_std=0.1),
+    "bf16_varlen_edges": W.custom(H=1, HV=2, K=128, V=128, h0_std=0.1,
+                                  lengths=(0, 1, 15, 16, 17, 100, 33, 0)),
+    "fp32_varlen_gva": W.custom(H=2, HV=4, K=128, V=128, dtype="fp32", h0_std=0.1,
+                                lengths=(5, 40, 0, 16)),
+    "bf16_strong_decay": W.custom(B=1, T=200, H=2, HV=2, K=128, V=128, g_lo=0.5, g_hi=0.9999,
+                                  beta_std=2.0),
+    "bf16_t1": W.custom(B=3, T=1, H=1, HV=1, K=128, V=128, h0_std=0.1),
+}
+
+
+@pytest.mark.parametrize("with_dht", [True, False])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_small_parity(name, with_dht):
+    inp = W.make_inputs(SMALL[name], seed=0)
+    gr = W.make_grads(inp, seed=0, dht_std=1.0 if with_dht else None)
+    check_grads(gpu_bwd(inp, gr), oracle_bwd(inp, gr))
+
+
+def test_backward_is_deterministic():
+    inp = W.make_inputs(SMALL["bf16_b2_t100_gva_h0"], seed=2)
+    gr = W.make_grads(inp, seed=2)
+    a, b = gpu_bwd(inp, gr), gpu_bwd(inp, gr)
+    for name, x, y in zip(NAMES, a, b):
+        assert np.array_equal(x, y), name
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_backward_empty_sequences_pass_dht_through(io):
+    w = W.custom(B=2, T=0, H=1, HV=2, K=128, V=64, dtype=io, h0_std=1.0)
+    inp = W.make_inputs(w, seed=3)
+    gr = W.make_grads(inp, seed=3)
+    out = gpu_bwd(inp, gr)
+    assert all(x.size == 0 for x in out[:5])
+    assert np.array_equal(out[5], gr.dht.numpy().astype(np.float64))
+
+
+def test_backward_beta0_gives_zero_dk_dv():
+    # with beta = 0 nothing is written to the state: k and v reach no output, so their
+    # gradients are exactly zero; the rest must still match the oracle
+    w = W.custom(B=1, T=90, H=2, HV=2, K=128, V=128, h0_std=0.5)
+    inp = W.make_inputs(w, seed=5, beta_override=0.0)
+    gr = W.make_grads(inp, seed=5)
+    got = gpu_bwd(inp, gr)
+    assert not got[1].any() and not got[2].any()
+    check_grads(got, oracle_bwd(inp, gr))
+
+
+def test_backward_g0_matches_oracle():
+    w = W.custom(B=1, T=90, H=2, HV=2, K=128, V=128, h0_std=0.5)
+    inp = W.make_inputs(w, seed=6, g_override=0.0)
+    gr = W.make_grads(inp, seed=6)
+    check_grads(gpu_bwd(inp, gr), oracle_bwd(inp, gr))
+
+
+def _unit_slice(inp: W.Inputs, gr: W.Grads, s: int, h: int):
+    """The inputs of sequence s and q/k head h with its G value heads, as a 1-sequence batch."""
+    bos, eos = inp.seq_bounds()[s]
+    G = inp.w.G
+    js = slice(h * G, (h + 1) * G)
+    tok = lambda x: x.reshape(-1, *x.shape[2:])[bos:eos].unsqueeze(0)
+    sub = W.Inputs(inp.w, tok(inp.q)[:, :, h:h + 1], tok(inp.k)[:, :, h:h + 1],
+                   tok(inp.v)[:, :, js], tok(inp.g)[:, :, js], tok(inp.beta)[:, :, js],
+                   None if inp.h0 is None else inp.h0[s:s + 1, js], None, inp.scale)
+    sgr = W.Grads(tok(gr.d_o)[:, :, js], None if gr.dht is None else gr.dht[s:s + 1, js])
+    return sub, sgr, (bos, eos, js)
+
+
+@pytest.mark.parametrize("name,n_units", [("h16_t4096", 3), ("varlen8_h32", 3),
+                                          ("gva_b4_t8192", 2)])
+def test_backward_full_size_sampled(name, n_units):
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, seed=0)
+    gr = W.make_grads(inp, seed=0)
+    print(f"[bwd full] {name}: GPU backward", file=sys.stderr, flush=True)
+    got = gpu_bwd(inp, gr)
+    for x in got:
+        assert np.isfinite(x).all()
+    dq, dk, dv, dg, db, dh0 = got
+    flat = lambda x: x.reshape(-1, *x.shape[2:])
+    units = W.sample_units(inp.N, w.H, n_units, seed=7)
+    for s, h in units:
+        sub, sgr, (bos, eos, js) = _unit_slice(inp, gr, s, h)
+        print(f"[bwd full] {name}: oracle unit s={s} h={h} ({eos - bos} tokens)",
+              file=sys.stderr, flush=True)
+        ref = oracle_bwd(sub, sgr)
+        mine = (flat(dq)[bos:eos, h:h + 1][None], flat(dk)[bos:eos, h:h + 1][None],
+                flat(dv)[bos:eos, js][None], flat(dg)[bos:eos, js][None],
+                flat(db)[bos:eos, js][None], dh0[s:s + 1, js])
+        check_grads(mine, ref)

@@ -194,6 +194,24 @@ def make_raw_inputs(w: Workload, seed: int = 0, qk_std: float = 2.0, g_mean: flo
     return RawInputs(Inputs(w, q, k, v, g, beta, h0, cu, scale=w.K ** -0.5), A_log, dt_bias)
 
 
+@dataclasses.dataclass
+class Grads:
+    d_o: torch.Tensor               # [B, T, HV, V] io dtype, CPU: gradient of o
+    dht: Optional[torch.Tensor]     # [N, HV, K, V] fp32 or None: gradient of the final state
+
+
+def make_grads(inp: Inputs, seed: int = 0, dht_std: Optional[float] = 1.0) -> Grads:
+    """Seeded incoming gradients for a backward pass over ``inp``: d_o ~ N(0, 1) in the io
+    dtype, dht ~ N(0, dht_std) in fp32 (None when dht_std is None)."""
+    gen = torch.Generator().manual_seed(10_000 + seed)
+    B, T, HV, V = inp.v.shape
+    K = inp.q.shape[3]
+    d_o = torch.randn(B, T, HV, V, generator=gen).to(inp.v.dtype)
+    dht = (None if dht_std is None
+           else torch.randn(inp.N, HV, K, V, generator=gen) * dht_std)
+    return Grads(d_o, dht)
+
+
 def as_f32_numpy(x: Optional[torch.Tensor]):
     """Exact fp32 copy of an io-dtype tensor (bf16 -> fp32 is exact) as a numpy array."""
     if x is None:
