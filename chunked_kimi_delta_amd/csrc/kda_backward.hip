@@ -13,8 +13,7 @@
 //     dDelta = Mqk^T dO + KR Lam_next,   Lam = diag(E) Lam_next + QD^T dO - W^T dDelta,
 // and every chunk then back-propagates its own quantities to its tokens independently. Launches:
 //   prepare_f32 (kda_prepare.hip)  the chunk records (W, QD, KR, U, Mqk, E) in fp32
-//   bwd_states_kernel              S at the start of every chunk
-//   bwd_chain_kernel               Lam at the end of every chunk, and dh0
+//   bwd_chains_kernel              S at the start and Lam at the end of every chunk, and dh0
 //   bwd_local_kernel               per (chunk, value head): dv, dg, dbeta and dq, dk
 //   bwd_group_sum_kernel           dq, dk summed over the value heads of a q/k head (G > 1)
 #include "kda_internal.h"
@@ -28,151 +27,233 @@ __device__ __forceinline__ float ldx(const uint16_t *p, int64_t i) {
     return bf16_bits_to_f32(p[i]);
 }
 
-// State at the start of every chunk: one block per (sequence, value head), thread n owns
-// column n of S (the fp32 state pass of kda_state.hip without the output).
-template <int K, int V>
-__global__ __launch_bounds__(V) void bwd_states_kernel(BwdParams b)
+// ---------------------------------------------------------------------------- the two chains
+// States forward (S at every chunk start) and the state gradient backward (Lam at every chunk
+// end, then dh0) in one launch: the two chains are independent, and every V column of S and
+// of Lam evolves on its own, so one workgroup owns one 16-column slice of one (sequence, value
+// head) for one of the two chains. Its 4 waves split the K rows: wave w keeps the K/64 tiles
+// of 16 rows x 16 columns it owns in fp32 registers (C-layout, which is also the B operand
+// layout of the fp32 16x16x4 MFMA, so a tile feeds the products with no data movement between
+// lanes). The 16 x 16 products that contract over K (w S, kr Lam) are summed over the waves
+// through LDS, double-buffered by chunk parity so that one barrier per chunk suffices; the
+// barrier orders LDS only, so the next chunk's record loads and this chunk's state stores stay
+// in flight across it.
+//   states:  delta = u - w S;  S <- diag(E) S + kr^T delta
+//   grads:   dDelta = Mqk^T dO + kr Lam;  Lam <- diag(E) Lam + qd^T dO - w^T dDelta
+// The chunk records are read as they are laid out ([16][K] row-major w, qd, kr; [16][V] u;
+// [16][16] Mqk; [K] E): A-operand rows of w and kr are contiguous 16-byte loads, their
+// transposes four 4-byte loads. Records of the next chunk are loaded before the current
+// chunk's products.
+constexpr int CHAIN_WAVES = 4;
+
+template <int K>
+struct ChainOps {
+    static constexpr int TPW = K / 16 / CHAIN_WAVES;   // row tiles per wave
+    f32x4 a[TPW];     // states: w rows;  grads: kr rows              (A operand, 16 x 16)
+    f32x4 at[TPW];    // states: kr^T;    grads: qd^T                 (A operand)
+    f32x4 bt[TPW];    // grads: w^T                                   (A operand)
+    f32x4 e[TPW];     // exp(gam) of the tile rows this lane holds
+    f32x4 x;          // states: u (C-layout);  grads: dO (C-layout)
+    f32x4 m;          // grads: Mqk^T (A operand; wave 0 only)
+};
+
+template <int K, int V, typename T, bool GRAD>
+__device__ __forceinline__ void chain_load(ChainOps<K> &o, const float *ch, const T *dout,
+                                           int64_t tok0, int64_t eos, int HV, int j, int n0,
+                                           int wave, int lane)
 {
-    const FwdParams &p = b.f;
     using WS = WsF32<K, V>;
-    __shared__ float sw[16][K], skr[16][K], seg[K];
-    const int n = threadIdx.x;
-    const int j = blockIdx.x % p.HV, s = blockIdx.x / p.HV;
-    const int64_t bos = seq_bos(p.seq, s), eos = seq_eos(p.seq, s, bos);
-    const int nc = (int)((eos - bos + CHUNK - 1) / CHUNK);
-    const size_t slot0 = (size_t)j * p.seq.n_slots + (size_t)(bos / CHUNK + s);
-    float S[K];
-    if (p.h0) {
-        const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + n;
+    constexpr int TPW = ChainOps<K>::TPW;
+    const int r = lane & 15, g = lane >> 4;
+    const float *W = ch + WS::W / 4, *QD = ch + WS::QD / 4, *KR = ch + WS::KR / 4;
 #pragma unroll
-        for (int d = 0; d < K; ++d) S[d] = h0[(size_t)d * V];
-    } else {
+    for (int x = 0; x < TPW; ++x) {
+        const int k0 = (wave * TPW + x) * 16;
+        const float *ra = (GRAD ? KR : W) + r * K + k0 + 4 * g;
+        o.a[x] = *(const f32x4 *)ra;
+        o.e[x] = *(const f32x4 *)(ch + WS::EG / 4 + k0 + 4 * g);
 #pragma unroll
-        for (int d = 0; d < K; ++d) S[d] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            o.at[x][i] = (GRAD ? QD : KR)[t * K + k0 + r];
+            if (GRAD) o.bt[x][i] = W[t * K + k0 + r];
+        }
     }
-    for (int c = 0; c < nc; ++c) {
-        float *ck = b.ck_S + (slot0 + c) * (size_t)K * V + n;
+    // Loads are unconditional and their values are used as loaded (rows past the sequence end
+    // read its last row and are zeroed at use): any arithmetic on a value here, or a load under
+    // a branch, would make the compiler wait for the load on the spot.
 #pragma unroll
-        for (int d = 0; d < K; ++d) ck[(size_t)d * V] = S[d];
-        const float *ch = (const float *)(p.ws + (slot0 + c) * (size_t)WS::BYTES);
-        for (int idx = n; idx < 16 * K; idx += V) {
-            sw[idx / K][idx % K] = ch[WS::W / 4 + idx];
-            skr[idx / K][idx % K] = ch[WS::KR / 4 + idx];
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        if (GRAD) {
+            const int64_t tok = tok0 + t, tc = tok < eos ? tok : eos - 1;
+            o.x[i] = ldx(dout, (tc * HV + j) * V + n0 + r);
+            o.m[i] = ch[WS::MQK / 4 + t * 16 + r];
+        } else {
+            o.x[i] = ch[WS::U / 4 + t * V + n0 + r];
         }
-        for (int idx = n; idx < K; idx += V) seg[idx] = ch[WS::EG / 4 + idx];
-        __syncthreads();
-        float dl[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float acc = ch[WS::U / 4 + t * V + n];
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) acc -= sw[t][kk] * S[kk];
-            dl[t] = acc;
-        }
-#pragma unroll
-        for (int kk = 0; kk < K; ++kk) {
-            float acc = seg[kk] * S[kk];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) acc += skr[t][kk] * dl[t];
-            S[kk] = acc;
-        }
-        __syncthreads();
     }
 }
 
-// Gradient of the state, newest chunk first: Lam (thread n: column n) starts as dht; before
-// chunk c is processed Lam is the gradient at its end and is recorded; after the first chunk
-// it is dh0.
-template <int K, int V, typename T>
-__global__ __launch_bounds__(V) void bwd_chain_kernel(BwdParams b)
+// One chain (GRAD: the state gradient, else the states) of one 16-column slice of one unit.
+template <int K, int V, typename T, bool GRAD>
+__device__ __forceinline__ void chain_run(const BwdParams &b, int unit, int n0, int wave,
+                                          int lane)
 {
     const FwdParams &p = b.f;
     using WS = WsF32<K, V>;
-    __shared__ float sw[16][K], sqd[16][K], skr[16][K], smq[16][16], seg[K];
-    const int n = threadIdx.x;
-    const int j = blockIdx.x % p.HV, s = blockIdx.x / p.HV;
+    constexpr int TPW = ChainOps<K>::TPW;
+    __shared__ f32x4 part[2][CHAIN_WAVES][64];
+    const int r = lane & 15, g = lane >> 4;
+    const int j = unit % p.HV, s = unit / p.HV;
     const int64_t bos = seq_bos(p.seq, s), eos = seq_eos(p.seq, s, bos);
     const int nc = (int)((eos - bos + CHUNK - 1) / CHUNK);
     const size_t slot0 = (size_t)j * p.seq.n_slots + (size_t)(bos / CHUNK + s);
+    const size_t unit_off = ((size_t)s * p.HV + j) * (size_t)K * V;
     const T *dout = (const T *)b.d_o;
-    float L[K];
-    if (b.dht) {
-        const float *dh = b.dht + ((size_t)s * p.HV + j) * (size_t)K * V + n;
+    // element (k0 + 4g + i, n0 + r) of a row-major K x V matrix, k0 the first row of tile x
+    auto at = [&](int x, int i) {
+        return (size_t)((wave * TPW + x) * 16 + 4 * g + i) * V + n0 + r;
+    };
+    auto rec = [&](int c) { return (const float *)(p.ws + (slot0 + c) * (size_t)WS::BYTES); };
+
+    f32x4 X[TPW];                     // S (states) or Lam (grads), C-layout tiles
+    const float *init = GRAD ? b.dht : p.h0;
 #pragma unroll
-        for (int d = 0; d < K; ++d) L[d] = dh[(size_t)d * V];
-    } else {
+    for (int x = 0; x < TPW; ++x)
 #pragma unroll
-        for (int d = 0; d < K; ++d) L[d] = 0.f;
+        for (int i = 0; i < 4; ++i) X[x][i] = init ? init[unit_off + at(x, i)] : 0.f;
+    // one chunk with the operands in `o` (loaded one chunk earlier)
+    auto step = [&](const ChainOps<K> &o, int it) {
+        const int c = GRAD ? nc - 1 - it : it;
+        float *cko = (GRAD ? b.ck_L : b.ck_S) + (slot0 + c) * (size_t)K * V;
+#pragma unroll
+        for (int x = 0; x < TPW; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cko[at(x, i)] = X[x][i];
+        f32x4 ox = o.x;
+        if (GRAD) {                   // dO rows past the sequence end are zero
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ox[i] = bos + 16 * c + 4 * g + i < eos ? ox[i] : 0.f;
+        }
+        // this wave's share of the K contraction: w S (states) or kr Lam (+ Mqk^T dO, once)
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) acc = mm16_f32(o.a[x], X[x], acc);
+        if (GRAD && wave == 0) acc = mm16_f32(o.m, ox, acc);
+        const int par = it & 1;
+        part[par][wave][lane] = acc;
+        lds_barrier();
+        f32x4 d = zero4();
+#pragma unroll
+        for (int w = 0; w < CHAIN_WAVES; ++w) {
+            const f32x4 pw = part[par][w][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] += pw[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // states: delta = u - w S;  grads: -dDelta
+            d[i] = GRAD ? -d[i] : o.x[i] - d[i];
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            f32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = o.e[x][i] * X[x][i];
+            if (GRAD) {
+                y = mm16_f32(o.at[x], ox, y);                         // + qd^T dO
+                y = mm16_f32(o.bt[x], d, y);                          // - w^T dDelta
+            } else {
+                y = mm16_f32(o.at[x], d, y);                          // + kr^T delta
+            }
+            X[x] = y;
+        }
+    };
+    auto load = [&](ChainOps<K> &o, int it) {
+        const int c = GRAD ? nc - 1 - it : it;
+        chain_load<K, V, T, GRAD>(o, rec(c), dout, bos + 16 * c, eos, p.HV, j, n0, wave, lane);
+    };
+    // two operand sets used alternately (a copy from one to the other would wait for the loads)
+    if (nc > 0) {
+        ChainOps<K> o0, o1;
+        load(o0, 0);
+        for (int it = 0; it < nc; it += 2) {
+            load(o1, it + 1 < nc ? it + 1 : it);
+            step(o0, it);
+            if (it + 1 >= nc) break;
+            load(o0, it + 2 < nc ? it + 2 : it + 1);
+            step(o1, it + 1);
+        }
     }
-    for (int c = nc - 1; c >= 0; --c) {
-        float *ck = b.ck_L + (slot0 + c) * (size_t)K * V + n;
+    if (GRAD && b.dh0) {
 #pragma unroll
-        for (int d = 0; d < K; ++d) ck[(size_t)d * V] = L[d];
-        const float *ch = (const float *)(p.ws + (slot0 + c) * (size_t)WS::BYTES);
-        for (int idx = n; idx < 16 * K; idx += V) {
-            sw[idx / K][idx % K] = ch[WS::W / 4 + idx];
-            sqd[idx / K][idx % K] = ch[WS::QD / 4 + idx];
-            skr[idx / K][idx % K] = ch[WS::KR / 4 + idx];
-        }
-        for (int idx = n; idx < 256; idx += V) smq[idx / 16][idx % 16] = ch[WS::MQK / 4 + idx];
-        for (int idx = n; idx < K; idx += V) seg[idx] = ch[WS::EG / 4 + idx];
-        __syncthreads();
-        float dO[16], dd[16];
+        for (int x = 0; x < TPW; ++x)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int64_t tok = bos + 16 * c + t;
-            dO[t] = tok < eos ? ldx(dout, (tok * p.HV + j) * V + n) : 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {            // dDelta = Mqk^T dO + KR Lam
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc += smq[m][t] * dO[m];
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) acc += skr[t][kk] * L[kk];
-            dd[t] = acc;
-        }
-#pragma unroll
-        for (int kk = 0; kk < K; ++kk) {           // Lam = E Lam + QD^T dO - W^T dDelta
-            float acc = seg[kk] * L[kk];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) acc += sqd[t][kk] * dO[t] - sw[t][kk] * dd[t];
-            L[kk] = acc;
-        }
-        __syncthreads();
-    }
-    if (b.dh0) {
-        float *dh = b.dh0 + ((size_t)s * p.HV + j) * (size_t)K * V + n;
-#pragma unroll
-        for (int d = 0; d < K; ++d) dh[(size_t)d * V] = L[d];
+            for (int i = 0; i < 4; ++i) b.dh0[unit_off + at(x, i)] = X[x][i];
     }
 }
 
-// One block (256 threads) per (chunk slot, value head): recompute the chunk in fp32 and
-// back-propagate O, S_next (through delta, U, W, A, the inverse, L, Mqk and the decay factors)
-// to the chunk's tokens. Products are formed from exponent differences (every factor
-// e^{Gam_i - Gam_j}, i >= j, and e^{gam - Gam} is at most 1). V is visited in blocks of 16
-// columns so that only a K x 16 block of S and of Lam sits in LDS (about 105 KB in all at
-// K = V = 128, within the 160 KB of one CU).
+template <int K, int V, typename T>
+__global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams b)
+{
+    constexpr int NSL = V / 16;
+    int unit, sub;
+    if (!state_unit(blockIdx.x, 2 * NSL, b.f.seq.N * b.f.HV, &unit, &sub)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n0 = (sub >> 1) * 16;
+    if (sub & 1)
+        chain_run<K, V, T, true>(b, unit, n0, wave, lane);
+    else
+        chain_run<K, V, T, false>(b, unit, n0, wave, lane);
+}
+
+// One block (4 waves) per (chunk slot, value head): recompute the chunk in fp32 and
+// back-propagate O and S_next (through delta, U, W, A, the inverse, L, Mqk and the decay
+// factors) to the chunk's tokens. Products are formed from exponent differences (every factor
+// e^{Gam_i - Gam_j}, i >= j, and e^{gam - Gam} is at most 1).
+// The contractions over V run on the fp32 matrix cores, one 16-column block of V at a time,
+// with the K rows split over the waves as in the chains (wave w owns the row tiles
+// w * K/64 ...): per block
+//     delta = A v - W S,  dDelta = Mqk^T dO + KR Lam           (partials summed through LDS)
+//     dQD += dO S^T,  dKR += delta Lam^T,  dW -= dDelta S^T     (the wave's own K tiles)
+//     dE += rowsum(Lam . S),  dMqk += dO delta^T,  dA += dDelta v^T,  dv = A^T dDelta
+// S and Lam are read from the row-major K x V records in two register layouts: C-layout (the B
+// operand of a product over K) and its transpose (the B operand of a product over V, one
+// 16-byte load per tile). The rest of the chunk's algebra (16 x 16 and 16 x K) is scalar.
 template <int K, int V>
-struct LocalShare {
-    static constexpr int VB = 16;
+struct alignas(16) LocalShare {
     float q[16][K + 1], k[16][K + 1], gm[16][K + 1];   // q, k, Gam (cumsum of g)
-    float v[16][V + 1];
     float w[16][K + 1], kr[16][K + 1];                 // W = A KD, KR
-    float dqd[16][K + 1], dkr[16][K + 1], dw[16][K + 1];
-    float S[K][VB + 1], L[K][VB + 1];                  // blocks of S and Lam_next
-    float dO[16][VB + 1], dl[16][VB + 1], dd[16][VB + 1];
+    union alignas(16) {
+        struct { float dqd[16][K + 1], dkr[16][K + 1], dw[16][K + 1]; };
+        float part[2][2][CHAIN_WAVES][16][20];         // V-block partials of delta, dDelta
+    };
     float G[16][17], Mq[16][17], X[16][17], A[16][17], P[16][17], T1[16][17];
     float dA[16][17], dMq[16][17], dL[16][17];
     float beta[16], dbeta[16], E[K], dE[K];
+};
+
+// four consecutive values of an io-dtype row as fp32
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ f32x4 ld4(const uint16_t *p) {
+    const uint2 raw = *(const uint2 *)p;
+    float o[4];
+    unpack_bf16x4(raw, o);
+    return f32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Operands of one V block for one wave (loaded one block ahead; used as loaded, rows past the
+// chunk's end are zeroed at use).
+template <int K>
+struct BlockOps {
+    static constexpr int TPW = K / 16 / CHAIN_WAVES;
+    f32x4 sc[TPW], sa[TPW], lc[TPW], la[TPW];   // S, Lam: C-layout and transposed layout
+    f32x4 doc, doa, vc, va;                     // dO, v: C-layout (rows 4g+i) and row r
 };
 
 template <int K, int V, typename T>
 __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
 {
     const FwdParams &p = b.f;
-    constexpr int VB = LocalShare<K, V>::VB;
+    constexpr int TPW = BlockOps<K>::TPW, NB = V / 16;
     __shared__ LocalShare<K, V> sh;
     const int tid = threadIdx.x;
     const int slot = blockIdx.x, j = blockIdx.y, h = j / p.G;
@@ -194,10 +275,6 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         sh.k[r][d] = ok ? ldx(k, (t * p.H + h) * K + d) : 0.f;
         sh.gm[r][d] = ok ? ldx(g, (t * p.HV + j) * K + d) : 0.f;
     }
-    for (int idx = tid; idx < 16 * V; idx += 256) {
-        const int r = idx / V, d = idx % V;
-        sh.v[r][d] = r < nvalid ? ldx(v, ((bos + r) * p.HV + j) * V + d) : 0.f;
-    }
     if (tid < 16) {
         sh.beta[tid] = tid < nvalid ? ldx(bt, (bos + tid) * p.HV + j) : 0.f;
         sh.dbeta[tid] = 0.f;
@@ -207,7 +284,6 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         float acc = 0.f;
         for (int r = 0; r < 16; ++r) { acc += sh.gm[r][d]; sh.gm[r][d] = acc; }
         sh.E[d] = __expf(acc);
-        sh.dE[d] = 0.f;
     }
     __syncthreads();
 
@@ -243,87 +319,158 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         __syncthreads();
     }
     sh.A[i16][j16] = sh.X[i16][j16] * sh.beta[j16];
-    sh.dA[i16][j16] = 0.f;
-    sh.dMq[i16][j16] = 0.f;
     __syncthreads();
 
-    // ---- W = A KD and KR; zero the K-wide accumulators
+    // ---- W = A KD and KR
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int t = idx / K, d = idx % K;
         float acc = 0.f;
         for (int m = 0; m < 16; ++m) acc += sh.A[t][m] * sh.k[m][d] * __expf(sh.gm[m][d]);
         sh.w[t][d] = acc;
         sh.kr[t][d] = sh.k[t][d] * __expf(sh.gm[15][d] - sh.gm[t][d]);
-        sh.dqd[t][d] = 0.f;
-        sh.dkr[t][d] = 0.f;
-        sh.dw[t][d] = 0.f;
     }
     __syncthreads();
 
-    // ---- V in blocks of VB columns
+    // ---- the V blocks on the matrix cores
+    const int wave = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
+    f32x4 Wa[TPW], KRa[TPW], Aa, At, Mqt;        // loop-invariant A operands
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int k0 = (wave * TPW + x) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Wa[x][i] = sh.w[r][k0 + 4 * gq + i];
+            KRa[x][i] = sh.kr[r][k0 + 4 * gq + i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        Aa[i] = sh.A[r][4 * gq + i];
+        At[i] = sh.A[4 * gq + i][r];
+        Mqt[i] = sh.Mq[4 * gq + i][r];
+    }
     const float *cS = b.ck_S + gslot * (size_t)K * V;
     const float *cL = b.ck_L + gslot * (size_t)K * V;
-    for (int vb = 0; vb < V; vb += VB) {
-        for (int idx = tid; idx < K * VB; idx += 256) {
-            const int d = idx / VB, n = idx % VB;
-            sh.S[d][n] = cS[(size_t)d * V + vb + n];
-            sh.L[d][n] = cL[(size_t)d * V + vb + n];
-        }
-        {
-            const int t = i16, n = j16;
-            const int64_t tok = bos + t;
-            sh.dO[t][n] = t < nvalid ? ldx(dout, (tok * p.HV + j) * V + vb + n) : 0.f;
-        }
-        __syncthreads();
-        {   // delta = A v - W S, dDelta = Mqk^T dO + KR Lam (one entry per thread)
-            const int t = i16, n = j16;
-            float u = 0.f, dd = 0.f;
-            for (int m = 0; m < 16; ++m) {
-                u += sh.A[t][m] * sh.v[m][vb + n];
-                dd += sh.Mq[m][t] * sh.dO[m][n];
-            }
-            for (int d = 0; d < K; ++d) {
-                u -= sh.w[t][d] * sh.S[d][n];
-                dd += sh.kr[t][d] * sh.L[d][n];
-            }
-            sh.dl[t][n] = u;
-            sh.dd[t][n] = dd;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < 16 * K; idx += 256) {   // K-wide accumulations over the block
-            const int t = idx / K, d = idx % K;
-            float aq = 0.f, ar = 0.f, aw = 0.f;
+    const int rc = r < nvalid ? r : nvalid - 1;               // clamped rows: loads stay inside
+    int rq[4];
 #pragma unroll
-            for (int n = 0; n < VB; ++n) {
-                aq += sh.dO[t][n] * sh.S[d][n];
-                ar += sh.dl[t][n] * sh.L[d][n];
-                aw += sh.dd[t][n] * sh.S[d][n];
-            }
-            sh.dqd[t][d] += aq;
-            sh.dkr[t][d] += ar;
-            sh.dw[t][d] -= aw;
-        }
-        for (int d = tid; d < K; d += 256) {
-            float acc = 0.f;
+    for (int i = 0; i < 4; ++i) rq[i] = 4 * gq + i < nvalid ? 4 * gq + i : nvalid - 1;
+    auto load = [&](BlockOps<K> &o, int nb) {
+        const int n0 = nb * 16;
 #pragma unroll
-            for (int n = 0; n < VB; ++n) acc += sh.L[d][n] * sh.S[d][n];
-            sh.dE[d] += acc;
-        }
-        {   // dMqk += dO delta^T, dA += dDelta v^T (dU = dDelta); dv = A^T dDelta
-            const int r = i16, c = j16;
-            float am = 0.f, aa = 0.f, dv = 0.f;
+        for (int x = 0; x < TPW; ++x) {
+            const int k0 = (wave * TPW + x) * 16;
 #pragma unroll
-            for (int n = 0; n < VB; ++n) {
-                am += sh.dO[r][n] * sh.dl[c][n];
-                aa += sh.dd[r][n] * sh.v[c][vb + n];
+            for (int i = 0; i < 4; ++i) {
+                o.sc[x][i] = cS[(size_t)(k0 + 4 * gq + i) * V + n0 + r];
+                o.lc[x][i] = cL[(size_t)(k0 + 4 * gq + i) * V + n0 + r];
             }
-            sh.dMq[r][c] += am;
-            sh.dA[r][c] += aa;
-            for (int m = 0; m < 16; ++m) dv += sh.A[m][r] * sh.dd[m][c];
-            if (r < nvalid) b.dv[((bos + r) * p.HV + j) * V + vb + c] = dv;
+            o.sa[x] = *(const f32x4 *)(cS + (size_t)(k0 + r) * V + n0 + 4 * gq);
+            o.la[x] = *(const f32x4 *)(cL + (size_t)(k0 + r) * V + n0 + 4 * gq);
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o.doc[i] = ldx(dout, ((bos + rq[i]) * p.HV + j) * V + n0 + r);
+            o.vc[i] = ldx(v, ((bos + rq[i]) * p.HV + j) * V + n0 + r);
+        }
+        o.doa = ld4(dout + ((bos + rc) * p.HV + j) * V + n0 + 4 * gq);
+        o.va = ld4(v + ((bos + rc) * p.HV + j) * V + n0 + 4 * gq);
+    };
+    f32x4 aq[TPW], ar[TPW], aw[TPW], aMq = zero4(), aA = zero4();
+    float aE[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) { aq[x] = ar[x] = aw[x] = zero4(); aE[x] = 0.f; }
+    auto step = [&](const BlockOps<K> &o, int nb) {
+        const int n0 = nb * 16;
+        f32x4 doc = o.doc, doa = o.doa, vc = o.vc, va = o.va;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool okq = 4 * gq + i < nvalid;
+            doc[i] = okq ? doc[i] : 0.f;
+            vc[i] = okq ? vc[i] : 0.f;
+            doa[i] = r < nvalid ? doa[i] : 0.f;
+            va[i] = r < nvalid ? va[i] : 0.f;
+        }
+        f32x4 pd = zero4(), pk = zero4();
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            pd = mm16_f32(Wa[x], o.sc[x], pd);
+            pk = mm16_f32(KRa[x], o.lc[x], pk);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pd[i] = -pd[i];
+        if (wave == 0) {
+            pd = mm16_f32(Aa, vc, pd);                     // + A v
+            pk = mm16_f32(Mqt, doc, pk);                   // + Mqk^T dO
+        }
+        const int par = nb & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sh.part[par][0][wave][4 * gq + i][r] = pd[i];
+            sh.part[par][1][wave][4 * gq + i][r] = pk[i];
+        }
+        lds_barrier();
+        f32x4 ddc = zero4(), dtr = zero4(), ddtr = zero4();
+#pragma unroll
+        for (int w = 0; w < CHAIN_WAVES; ++w) {
+            const f32x4 t0 = *(const f32x4 *)&sh.part[par][0][w][r][4 * gq];
+            const f32x4 t1 = *(const f32x4 *)&sh.part[par][1][w][r][4 * gq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ddc[i] += sh.part[par][1][w][4 * gq + i][r];
+                dtr[i] += t0[i];
+                ddtr[i] += t1[i];
+            }
+        }
+        // dtr, ddtr: delta, dDelta in the transposed layout (row r); ddc: dDelta in C-layout
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            aq[x] = mm16_f32(doa, o.sa[x], aq[x]);          // dQD += dO S^T
+            ar[x] = mm16_f32(dtr, o.la[x], ar[x]);          // dKR += delta Lam^T
+            aw[x] = mm16_f32(ddtr, o.sa[x], aw[x]);         // dW  -= dDelta S^T (sign later)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) aE[x] += o.sa[x][i] * o.la[x][i];
+        }
+        if (wave == 0) aMq = mm16_f32(doa, dtr, aMq);       // dMqk += dO delta^T
+        if (wave == 1) aA = mm16_f32(ddtr, va, aA);         // dA += dDelta v^T
+        if (wave == 2) {                                    // dv = A^T dDelta
+            const f32x4 dv = mm16_f32(At, ddc, zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * gq + i < nvalid)
+                    b.dv[((bos + 4 * gq + i) * p.HV + j) * V + n0 + r] = dv[i];
+        }
+    };
+    {
+        BlockOps<K> o0, o1;
+        load(o0, 0);
+        for (int nb = 0; nb < NB; nb += 2) {
+            load(o1, nb + 1 < NB ? nb + 1 : nb);
+            step(o0, nb);
+            if (nb + 1 >= NB) break;
+            load(o0, nb + 2 < NB ? nb + 2 : nb + 1);
+            step(o1, nb + 1);
+        }
     }
+    __syncthreads();                                        // partials done: reuse as dQD...
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int k0 = (wave * TPW + x) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sh.dqd[4 * gq + i][k0 + r] = aq[x][i];
+            sh.dkr[4 * gq + i][k0 + r] = ar[x][i];
+            sh.dw[4 * gq + i][k0 + r] = -aw[x][i];
+        }
+        const float e = sum_lane_groups(aE[x]);
+        if (gq == 0) sh.dE[k0 + r] = e;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (wave == 0) sh.dMq[4 * gq + i][r] = aMq[i];
+        if (wave == 1) sh.dA[4 * gq + i][r] = aA[i];
+    }
+    __syncthreads();
 
     // ---- dA += dW KD^T; dbeta (columns of A); dX = dA diag(beta)
     {
@@ -455,13 +602,13 @@ hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st)
     hipError_t e;
     if (p.seq.T_total > 0 && (e = launch_prepare_f32<K, V>(p, st, in_bf16)) != hipSuccess)
         return e;
-    const unsigned units = (unsigned)(p.seq.N * p.HV);
+    const int64_t units = (int64_t)p.seq.N * p.HV;
     if (units == 0) return hipSuccess;
-    bwd_states_kernel<K, V><<<dim3(units), dim3(V), 0, st>>>(b);
+    const dim3 cgrid((unsigned)((units + 7) / 8 * 8 * 2 * (V / 16)));
     if (in_bf16)
-        bwd_chain_kernel<K, V, uint16_t><<<dim3(units), dim3(V), 0, st>>>(b);
+        bwd_chains_kernel<K, V, uint16_t><<<cgrid, dim3(64 * CHAIN_WAVES), 0, st>>>(b);
     else
-        bwd_chain_kernel<K, V, float><<<dim3(units), dim3(V), 0, st>>>(b);
+        bwd_chains_kernel<K, V, float><<<cgrid, dim3(64 * CHAIN_WAVES), 0, st>>>(b);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.seq.T_total == 0) return hipSuccess;
     dim3 grid(p.seq.n_slots, p.HV);

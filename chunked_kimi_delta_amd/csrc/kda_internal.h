@@ -193,6 +193,18 @@ __device__ __forceinline__ bool locate_slot(const SeqGeom &sg, int slot, int *s_
     return true;
 }
 
+// Workgroup -> (unit = sequence * HV + value head, sub-slice in [0, NV)). Workgroups are
+// dispatched to the 8 XCDs round-robin (workgroup w runs on XCD w % 8), and each XCD has its
+// own L2. The map keeps all NV workgroups of one unit on one XCD so the chunk operands they
+// share are fetched into that L2 once. The grid is padded to a multiple of 8 units; units
+// beyond N*HV return false.
+__device__ __forceinline__ bool state_unit(int wg, int NV, int units, int *unit, int *slice) {
+    const int xcd = wg & 7, idx = wg >> 3;
+    *unit = (idx / NV) * 8 + xcd;
+    *slice = idx % NV;
+    return *unit < units;
+}
+
 // ----------------------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -346,6 +358,21 @@ __device__ __forceinline__ float gate_activation(const Prestage &pre, float x, f
 // 1 / sqrt(sum of squares + eps): the L2-norm factor of a q or k row.
 __device__ __forceinline__ float l2norm_factor(float sumsq) {
     return __builtin_amdgcn_rsqf(sumsq + L2NORM_EPS);
+}
+
+// Workgroup fences that order LDS accesses only. Around s_barrier they make LDS writes visible
+// to the other waves without waiting for this wave's outstanding global loads and stores (a
+// full __syncthreads() waits for those too, which would drain every prefetch in flight).
+__device__ __forceinline__ void lds_release() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_acquire() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_barrier() {
+    lds_release();
+    __builtin_amdgcn_s_barrier();
+    lds_acquire();
 }
 
 // Wait for every outstanding vector memory load of this wave (vmcnt 0; the LDS/scalar and

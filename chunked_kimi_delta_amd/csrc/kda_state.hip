@@ -25,17 +25,6 @@
 
 namespace kda {
 
-// Workgroup -> (sequence s, value head j, 16-column slice). Workgroups are dispatched to the
-// 8 XCDs round-robin (workgroup w runs on XCD w % 8), and each XCD has its own L2. The map
-// keeps all V/16 slices of one (s, j) on one XCD so the chunk operands they share (w, qd, kr,
-// Mqk, exp(gam)) are fetched into that L2 once. Units beyond N*HV (grid padding) return.
-__device__ __forceinline__ bool state_unit(int wg, int NV, int units, int *unit, int *slice) {
-    const int xcd = wg & 7, idx = wg >> 3;
-    *unit = (idx / NV) * 8 + xcd;
-    *slice = idx % NV;
-    return *unit < units;
-}
-
 // Output rows of one chunk for one wave: a buffer resource whose range ends after the last
 // valid token of the chunk, so stores to rows past the end of the sequence are dropped by the
 // hardware range check instead of a branch.
@@ -98,13 +87,6 @@ struct Handoff {
     f16x8 sh[2][K / 32][64];
     f16x4 dh[2][64];
 };
-
-__device__ __forceinline__ void lds_release() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-}
-__device__ __forceinline__ void lds_acquire() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Chain wave, one chunk: delta = u - w S, hand (S, delta) to the output wave, then
 // S <- diag(exp(gam)) S + kr^T delta. Each operand group of `f` is refilled from `nxt` (two
