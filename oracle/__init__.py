@@ -20,7 +20,8 @@ Contents
                   q, k, g, beta from raw projections.
   backward.py     fp64 gradients of the forward (dq, dk, dv, dg, dbeta, dh0): the reverse-mode
                   token recurrence, derived by hand, plus torch.autograd on the fp64 forward
-                  as an independent check.
+                  as an independent check; with the pre-stage's reverse mode (prestage.py),
+                  the gradients with respect to raw inputs, A_log and dt_bias.
   native.py       ctypes loader for the C oracle.
   build.py        compiles kda_oracle.c with gcc.
 

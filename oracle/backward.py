@@ -27,11 +27,17 @@ carrying dS from the final-state gradient backwards.
 
 ``kda_backward_autograd`` computes the same gradients by PyTorch's reverse-mode
 differentiation of the forward written with plain fp64 CPU tensor ops, as an independent check.
+
+``kda_backward_raw`` is the backward of the forward with its pre-stage: the pre-stage
+(prestage.py) turns raw inputs into q, k, g, beta, the recurrence's backward gives their
+gradients, and the pre-stage's reverse mode carries them back to the raw inputs and to the
+gate parameters A_log and dt_bias.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from oracle import prestage as PS
 from oracle.recurrent import _bounds
 
 
@@ -137,3 +143,19 @@ def kda_backward_autograd(q, k, v, g, beta, scale=None, initial_state=None, cu_s
     grads = torch.autograd.grad(loss, [q, k, v, g, beta, h0], allow_unused=True)
     return tuple(np.zeros(x.shape) if gr is None else gr.detach().numpy()
                  for gr, x in zip(grads, [q, k, v, g, beta, h0]))
+
+
+def kda_backward_raw(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
+                     do=None, dht=None, qk_l2norm=False, beta_sigmoid=False, gate=None,
+                     A_log=None, dt_bias=None, lower_bound=-5.0):
+    """Gradients with respect to the RAW inputs of the forward with its pre-stage:
+    (dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias); dA_log, ddt_bias are None without a
+    gate."""
+    qa, ka, ga, ba = PS.prestage(q, k, g, beta, qk_l2norm, beta_sigmoid, gate, A_log, dt_bias,
+                                 lower_bound)
+    dq, dk, dv, dg, db, dh0 = kda_backward_recurrent(qa, ka, v, ga, ba, scale, initial_state,
+                                                     cu_seqlens, do, dht)
+    dq, dk, dg, db, dA, ddt = PS.prestage_backward(q, k, g, beta, dq, dk, dg, db, qk_l2norm,
+                                                   beta_sigmoid, gate, A_log, dt_bias,
+                                                   lower_bound)
+    return dq, dk, dv, dg, db, dh0, dA, ddt

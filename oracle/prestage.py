@@ -21,6 +21,17 @@ Per token t and head, on the values the GPU reads (bf16 or fp32, upcast exactly)
 
 Reading (the pages have one head per gate parameter and HV == H): A_log has one entry and
 dt_bias one row of K entries per VALUE head, because g and beta are per value head.
+
+``prestage_backward`` is the reverse mode of these steps (the backward of the pre-stage that
+the C++ reference of "手撕KDA" section 2.1 runs after its chunk backward), written from the
+derivatives of the definitions above:
+  l2 norm     y = x r, r = (|x|^2 + eps)^(-1/2):   dx = r dy - r^3 x (x . dy)
+  sigmoid     d sigma / dx = sigma (1 - sigma)
+  softplus    d softplus / dx = sigma(x)
+  gates       softplus form  dg/dx = -exp(A_log) sigma(x),          dg/dA_log = g
+              bounded form   dg/dx = lb sigma (1 - sigma) exp(A_log), dg/dA_log = x dg/dx
+              (sigma taken at exp(A_log) x); dt_bias and A_log collect their gradients over
+              every token.
 """
 from __future__ import annotations
 
@@ -82,3 +93,54 @@ def prestage(q, k, g, beta, qk_l2norm=False, beta_sigmoid=False, gate=None, A_lo
     if gate is not None:
         g = gate_activation(g, A_log, dt_bias, gate, lower_bound)
     return q, k, g, beta
+
+
+def l2_normalize_vjp(x, dy, eps=L2_EPS):
+    """Gradient with respect to x of sum(dy * l2_normalize(x)), over the last axis."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+    return r * dy - r ** 3 * x * np.sum(x * dy, axis=-1, keepdims=True)
+
+
+def gate_activation_vjp(g_raw, A_log, dt_bias, mode, dg, lower_bound=-5.0):
+    """Gradients of sum(dg * gate_activation(...)) with respect to g_raw [.., HV, K], A_log
+    [HV] and dt_bias [HV, K] (returned even when dt_bias is None: the gradient of a zero
+    bias)."""
+    g_raw = np.asarray(g_raw, np.float64)
+    dg = np.asarray(dg, np.float64)
+    HV, K = g_raw.shape[-2], g_raw.shape[-1]
+    a = np.exp(np.asarray(A_log, np.float64)).reshape(HV, 1)
+    x = g_raw + (0.0 if dt_bias is None else np.asarray(dt_bias, np.float64).reshape(HV, K))
+    if mode == "softplus":
+        dgdx = -a * sigmoid(x)
+        dgda = -a * softplus(x)                       # = g
+    elif mode == "bounded":
+        s = sigmoid(a * x)
+        dgdx = float(lower_bound) * s * (1.0 - s) * a
+        dgda = dgdx * x
+    else:
+        raise ValueError(f"unknown gate mode {mode!r}")
+    dx = dg * dgdx
+    lead = tuple(range(dx.ndim - 2))
+    return dx, np.sum(dg * dgda, axis=lead + (dx.ndim - 1,)), np.sum(dx, axis=lead)
+
+
+def prestage_backward(q, k, g, beta, dq, dk, dg, dbeta, qk_l2norm=False, beta_sigmoid=False,
+                      gate=None, A_log=None, dt_bias=None, lower_bound=-5.0):
+    """Gradients with respect to the raw inputs of ``prestage`` given the gradients (dq, dk,
+    dg, dbeta) of its outputs. Returns (dq_raw, dk_raw, dg_raw, dbeta_raw, dA_log, ddt_bias);
+    the last two are None without a gate."""
+    dq = np.asarray(dq, np.float64)
+    dk = np.asarray(dk, np.float64)
+    dg = np.asarray(dg, np.float64)
+    dbeta = np.asarray(dbeta, np.float64)
+    if qk_l2norm:
+        dq, dk = l2_normalize_vjp(q, dq), l2_normalize_vjp(k, dk)
+    if beta_sigmoid:
+        s = sigmoid(beta)
+        dbeta = dbeta * s * (1.0 - s)
+    dA = ddt = None
+    if gate is not None:
+        dg, dA, ddt = gate_activation_vjp(g, A_log, dt_bias, gate, dg, lower_bound)
+    return dq, dk, dg, dbeta, dA, ddt
