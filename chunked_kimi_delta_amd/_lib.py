@@ -60,7 +60,7 @@ def load():
     lib.kda_bwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaFwdArgs)]
     lib.kda_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_bwd.argtypes = ([ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p, ctypes.c_void_p,
-                             ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 7)
+                             ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 9)
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_strerror.argtypes = [ctypes.c_int]
     lib.kda_strerror.restype = ctypes.c_char_p

@@ -143,16 +143,20 @@ class KdaFwdPlan:
 
 class KdaBwdPlan:
     """Validated arguments for repeated kda_bwd calls: gradients of the forward with respect to
-    q, k, v, g, beta (and initial_state) from d_o (like v) and dht (fp32 [N,HV,K,V] or None).
+    q, k, v, g, beta, initial_state and (with a gate) A_log, dt_bias, from d_o (like v) and dht
+    (fp32 [N,HV,K,V] or None).
 
-    Inputs as for KdaFwdPlan without the pre-stage (the gradients are those of q, k, g, beta as
-    the recurrence reads them). Outputs, allocated once through torch and reused by every
-    call(), all fp32: dq, dk [B,T,H,K]; dv [B,T,HV,V]; dg [B,T,HV,K]; dbeta [B,T,HV]; dh0
-    [N,HV,K,V] (when want_dh0).
+    Inputs and pre-stage keywords as for KdaFwdPlan (with the pre-stage on, q, k, g, beta are
+    the raw inputs and their gradients are the raw ones). Outputs, allocated once through
+    torch and reused by every call(), all fp32: dq, dk [B,T,H,K]; dv [B,T,HV,V]; dg [B,T,HV,K];
+    dbeta [B,T,HV]; dh0 [N,HV,K,V] (when want_dh0); dA_log [HV] and ddt_bias [HV,K] (with a
+    gate).
     """
 
     def __init__(self, q, k, v, g, beta, d_o, dht=None, scale=None, cu_seqlens=None,
-                 initial_state=None, want_dh0=True, workspace=None):
+                 initial_state=None, want_dh0=True, workspace=None, use_qk_l2norm=False,
+                 use_beta_sigmoid=False, gate=None, A_log=None, dt_bias=None,
+                 gate_lower_bound=-5.0):
         self.lib = load()
         if q.dtype not in _IO:
             raise TypeError(f"unsupported io dtype {q.dtype} (bf16 or fp32)")
@@ -183,6 +187,10 @@ class KdaBwdPlan:
         self.dg = torch.empty(B, T, HV, K, **f32)
         self.dbeta = torch.empty(B, T, HV, **f32)
         self.dh0 = torch.empty(N, HV, K, V, **f32) if want_dh0 else None
+        if gate not in _GATES:
+            raise ValueError(f"gate must be None, 'softplus' or 'bounded' (got {gate!r})")
+        self.dA_log = torch.empty(HV, **f32) if gate is not None else None
+        self.ddt_bias = torch.empty(HV, K, **f32) if gate is not None else None
         a = KdaFwdArgs()
         a.B, a.T, a.N, a.H, a.HV, a.K, a.V, a.io = B, T, N, H, HV, K, V, _IO[dt]
         a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
@@ -190,11 +198,22 @@ class KdaBwdPlan:
         a.cu_seqlens = _ptr(cu_seqlens)
         a.initial_state = _ptr(initial_state)
         a.chunk = 16
+        a.qk_l2norm = int(bool(use_qk_l2norm))
+        a.beta_sigmoid = int(bool(use_beta_sigmoid))
+        a.gate = _GATES[gate]
+        a.gate_lower_bound = float(gate_lower_bound)
+        if gate is not None:
+            if A_log is None:
+                raise ValueError("a gate needs A_log")
+            _check(A_log, "A_log", torch.float32, (HV,), dev)
+            if dt_bias is not None:
+                _check(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+            a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
         self.args = a
-        self._keep = (q, k, v, g, beta, d_o, dht, cu_seqlens, initial_state)
+        self._keep = (q, k, v, g, beta, d_o, dht, cu_seqlens, initial_state, A_log, dt_bias)
         self._ptrs = [_ptr(d_o), _ptr(dht)]
         self._outs = [_ptr(x) for x in (self.dq, self.dk, self.dv, self.dg, self.dbeta,
-                                        self.dh0)]
+                                        self.dh0, self.dA_log, self.ddt_bias)]
         need = int(self.lib.kda_bwd_workspace_bytes(ctypes.byref(a)))
         if need == 0:
             raise ValueError("unsupported shapes (K, V in {64, 128}; HV % H == 0)")
@@ -208,7 +227,7 @@ class KdaBwdPlan:
 
     def __call__(self, stream=None):
         """Enqueue the backward on `stream` (default: torch's current stream); returns
-        (dq, dk, dv, dg, dbeta, dh0)."""
+        (dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias)."""
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         st = self.lib.kda_bwd(ctypes.byref(self.args), *self._ptrs,
@@ -216,14 +235,16 @@ class KdaBwdPlan:
                               *self._outs, ctypes.c_void_p(stream.cuda_stream))
         if st != 0:
             raise RuntimeError(f"kda_bwd failed: {strerror(st)} ({st})")
-        return self.dq, self.dk, self.dv, self.dg, self.dbeta, self.dh0
+        return (self.dq, self.dk, self.dv, self.dg, self.dbeta, self.dh0, self.dA_log,
+                self.ddt_bias)
 
 
 def kda_bwd(q, k, v, g, beta, d_o, dht=None, scale=None, cu_seqlens=None, initial_state=None,
-            want_dh0=True):
-    """KDA backward. Returns fp32 (dq, dk, dv, dg, dbeta, dh0 or None); see KdaBwdPlan."""
+            want_dh0=True, **prestage):
+    """KDA backward. Returns fp32 (dq, dk, dv, dg, dbeta, dh0 or None, dA_log or None,
+    ddt_bias or None); see KdaBwdPlan for shapes and the pre-stage keywords."""
     return KdaBwdPlan(q, k, v, g, beta, d_o, dht, scale, cu_seqlens, initial_state,
-                      want_dh0)()
+                      want_dh0, **prestage)()
 
 
 def kda_fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,

@@ -61,6 +61,21 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     return KDA_OK;
 }
 
+// The pre-stage fields of the arguments (shared by the forward and the backward).
+kda_status check_prestage(const kda_fwd_args *a)
+{
+    if (a->gate != KDA_GATE_NONE && a->gate != KDA_GATE_SOFTPLUS && a->gate != KDA_GATE_BOUNDED)
+        return KDA_ERR_UNSUPPORTED;
+    if (a->gate != KDA_GATE_NONE) {
+        if (!a->A_log || ((uintptr_t)a->A_log & 3u)) return KDA_ERR_INVALID_ARG;
+        if (a->dt_bias && !aligned16(a->dt_bias)) return KDA_ERR_INVALID_ARG;
+        if (a->gate == KDA_GATE_BOUNDED &&
+            !(a->gate_lower_bound < 0.f && a->gate_lower_bound > -INFINITY))
+            return KDA_ERR_INVALID_ARG;
+    }
+    return KDA_OK;
+}
+
 enum Stage { STAGE_PREPARE = 1, STAGE_STATE = 2, STAGE_BOTH = 3 };
 
 template <int K, int V>
@@ -98,15 +113,8 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     if (a->initial_state && !aligned16(a->initial_state)) return KDA_ERR_INVALID_ARG;
     if (a->final_state && !aligned16(a->final_state)) return KDA_ERR_INVALID_ARG;
     if (a->cu_seqlens && !aligned16(a->cu_seqlens)) return KDA_ERR_INVALID_ARG;
-    if (a->gate != KDA_GATE_NONE && a->gate != KDA_GATE_SOFTPLUS && a->gate != KDA_GATE_BOUNDED)
-        return KDA_ERR_UNSUPPORTED;
-    if (a->gate != KDA_GATE_NONE) {
-        if (!a->A_log || ((uintptr_t)a->A_log & 3u)) return KDA_ERR_INVALID_ARG;
-        if (a->dt_bias && !aligned16(a->dt_bias)) return KDA_ERR_INVALID_ARG;
-        if (a->gate == KDA_GATE_BOUNDED &&
-            !(a->gate_lower_bound < 0.f && a->gate_lower_bound > -INFINITY))
-            return KDA_ERR_INVALID_ARG;
-    }
+    const kda_status ps = check_prestage(a);
+    if (ps != KDA_OK) return ps;
     if (tt > 0 && need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
         return KDA_ERR_WORKSPACE;
     if (a->N == 0) return KDA_OK;
@@ -149,19 +157,19 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
 }
 
 // Backward workspace: the fp32 chunk records, then S at the start and Lam at the end of every
-// chunk slot, then (G > 1) per-value-head dq and dk. Offsets in bytes, each 256-aligned.
+// chunk slot, then (G > 1 or q/k L2 norm) per-value-head dq and dk, then (gate on) per-chunk
+// partials of dA_log and dt_bias. Offsets in bytes, each 256-aligned.
 struct BwdLayout {
-    size_t rec, ck_S, ck_L, part, total;
+    size_t rec, ck_S, ck_L, part_q, part_k, part_A, part_dt, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Shape checks of the backward (the forward's, at chunk 16 with no pre-stage) and its layout.
+// Shape checks of the backward (the forward's, at chunk 16) and its workspace layout.
 kda_status check_bwd(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots, BwdLayout *L)
 {
     if (!a) return KDA_ERR_INVALID_ARG;
     if (a->chunk != 0 && a->chunk != 16) return KDA_ERR_UNSUPPORTED;
-    if (a->qk_l2norm || a->beta_sigmoid || a->gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED;
     kda_fwd_args c = *a;
     c.chunk = 16;
     size_t rec;
@@ -169,13 +177,19 @@ kda_status check_bwd(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots, 
     const kda_status st = check_shapes(&c, T_total, n_slots, &rec, &ct);
     if (st != KDA_OK) return st;
     rec = (size_t)*n_slots * (size_t)a->HV * record_bytes<WsF32>(a->K, a->V);  // fp32 records
-    const size_t state = (size_t)*n_slots * (size_t)a->HV * (size_t)a->K * (size_t)a->V * 4;
-    const size_t part = a->HV > a->H ? (size_t)*T_total * (size_t)a->HV * (size_t)a->K * 4 : 0;
+    const size_t slots = (size_t)*n_slots * (size_t)a->HV;
+    const size_t state = slots * (size_t)a->K * (size_t)a->V * 4;
+    const bool qk_part = a->HV > a->H || a->qk_l2norm;
+    const size_t part = qk_part ? (size_t)*T_total * (size_t)a->HV * (size_t)a->K * 4 : 0;
+    const bool gated = a->gate != KDA_GATE_NONE;
     L->rec = 0;
     L->ck_S = align256(rec);
     L->ck_L = L->ck_S + align256(state);
-    L->part = L->ck_L + align256(state);
-    L->total = L->part + 2 * align256(part);
+    L->part_q = L->ck_L + align256(state);
+    L->part_k = L->part_q + align256(part);
+    L->part_A = L->part_k + align256(part);
+    L->part_dt = L->part_A + (gated ? align256(slots * 4) : 0);
+    L->total = L->part_dt + (gated ? align256(slots * (size_t)a->K * 4) : 0);
     return KDA_OK;
 }
 
@@ -199,12 +213,16 @@ size_t kda_bwd_workspace_bytes(const kda_fwd_args *a)
 
 kda_status kda_bwd(const kda_fwd_args *a, const void *d_o, const float *dht, void *workspace,
                    size_t ws_bytes, float *dq, float *dk, float *dv, float *dg, float *dbeta,
-                   float *dh0, void *stream)
+                   float *dh0, float *dA_log, float *ddt_bias, void *stream)
 {
     int64_t tt, ns;
     BwdLayout L;
-    const kda_status st = check_bwd(a, &tt, &ns, &L);
+    kda_status st = check_bwd(a, &tt, &ns, &L);
     if (st != KDA_OK) return st;
+    if ((st = check_prestage(a)) != KDA_OK) return st;
+    if (a->gate != KDA_GATE_NONE &&
+        (!dA_log || ((uintptr_t)dA_log & 3u) || (ddt_bias && !aligned16(ddt_bias))))
+        return KDA_ERR_INVALID_ARG;
     if (tt > 0) {
         const void *ptrs[] = {a->q, a->k, a->v, a->g, a->beta, d_o, dq, dk, dv, dg, dbeta};
         for (const void *ptr : ptrs)
@@ -237,7 +255,13 @@ kda_status kda_bwd(const kda_fwd_args *a, const void *d_o, const float *dht, voi
     p.o = nullptr;
     p.ht = nullptr;
     uint8_t *ws = (uint8_t *)workspace;
-    p.ws = ws;                                    // pre-stage fields stay zero (off)
+    p.ws = ws;
+    p.pre.qk_l2norm = a->qk_l2norm != 0;
+    p.pre.beta_sigmoid = a->beta_sigmoid != 0;
+    p.pre.gate = a->gate;
+    p.pre.lower_bound = a->gate_lower_bound;
+    p.pre.A_log = a->A_log;
+    p.pre.dt_bias = a->dt_bias;
     b.d_o = d_o;
     b.dht = dht;
     b.ck_S = ws ? (float *)(ws + L.ck_S) : nullptr;
@@ -248,8 +272,13 @@ kda_status kda_bwd(const kda_fwd_args *a, const void *d_o, const float *dht, voi
     b.dg = dg;
     b.dbeta = dbeta;
     b.dh0 = dh0;
-    b.part_q = ws && p.G > 1 ? (float *)(ws + L.part) : nullptr;
-    b.part_k = ws && p.G > 1 ? (float *)(ws + L.part + (L.total - L.part) / 2) : nullptr;
+    const bool qk_part = p.G > 1 || p.pre.qk_l2norm;
+    b.part_q = ws && qk_part ? (float *)(ws + L.part_q) : nullptr;
+    b.part_k = ws && qk_part ? (float *)(ws + L.part_k) : nullptr;
+    b.dA_log = dA_log;
+    b.ddt_bias = ddt_bias;
+    b.part_A = ws && p.pre.gate ? (float *)(ws + L.part_A) : nullptr;
+    b.part_dt = ws && p.pre.gate ? (float *)(ws + L.part_dt) : nullptr;
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -293,7 +322,7 @@ const char *kda_strerror(int status)
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED:
         return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 with bf16 io; "
-               "gate 0, 1 or 2; the backward: chunk 16, no pre-stage)";
+               "gate 0, 1 or 2; the backward: chunk 16)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";

@@ -15,7 +15,14 @@
 //   prepare_f32 (kda_prepare.hip)  the chunk records (W, QD, KR, U, Mqk, E) in fp32
 //   bwd_chains_kernel              S at the start and Lam at the end of every chunk, and dh0
 //   bwd_local_kernel               per (chunk, value head): dv, dg, dbeta and dq, dk
-//   bwd_group_sum_kernel           dq, dk summed over the value heads of a q/k head (G > 1)
+//   bwd_qk_finalize_kernel         dq, dk summed over the value heads of a q/k head (G > 1)
+//                                  and carried through the q/k L2 norm (when it is on)
+//   bwd_param_kernel               dA_log, dt_bias: per-chunk partials summed (gate on)
+// With the pre-stage on, the kernels read raw inputs and apply it on load (prepare_f32 and the
+// local kernel), and the gradients leave through its reverse mode: dbeta times
+// sigma (1 - sigma), dg times the gate's slope (with dA_log and dt_bias summed over all tokens),
+// dq and dk through the L2 norm, dx = r dy - r^3 x (x . dy) (the backward of the pre-stage in
+// the C++ reference of "手撕KDA" section 2.1).
 #include "kda_internal.h"
 
 namespace kda {
@@ -260,26 +267,58 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
     int s;
     int64_t bos;
     int nvalid;
-    if (!locate_slot(p.seq, slot, &s, &bos, &nvalid)) return;
+    const bool gated = p.pre.gate != 0;
+    if (!locate_slot(p.seq, slot, &s, &bos, &nvalid)) {
+        if (gated) {               // slots without a chunk contribute nothing to the sums
+            const size_t ps = (size_t)j * p.seq.n_slots + slot;
+            for (int d = tid; d < K; d += 256) b.part_dt[ps * K + d] = 0.f;
+            if (tid == 0) b.part_A[ps] = 0.f;
+        }
+        return;
+    }
     const size_t gslot = (size_t)j * p.seq.n_slots + slot;
     const float sc = p.scale;
     const T *q = (const T *)p.q, *k = (const T *)p.k, *v = (const T *)p.v;
     const T *g = (const T *)p.g, *bt = (const T *)p.beta, *dout = (const T *)b.d_o;
+    const float aexp = gated ? __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E) : 0.f;
+    auto dtb = [&](int d) { return gated && p.pre.dt_bias ? p.pre.dt_bias[j * K + d] : 0.f; };
 
-    // ---- inputs of the chunk (rows past the end are zero) and the cumsum of g
+    // ---- inputs of the chunk (rows past the end are zero), pre-stage, the cumsum of g
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int r = idx / K, d = idx % K;
         const bool ok = r < nvalid;
         const int64_t t = bos + r;
         sh.q[r][d] = ok ? ldx(q, (t * p.H + h) * K + d) : 0.f;
         sh.k[r][d] = ok ? ldx(k, (t * p.H + h) * K + d) : 0.f;
-        sh.gm[r][d] = ok ? ldx(g, (t * p.HV + j) * K + d) : 0.f;
+        float gv = ok ? ldx(g, (t * p.HV + j) * K + d) : 0.f;
+        if (gated && ok) gv = gate_activation(p.pre, gv + dtb(d), aexp);
+        sh.gm[r][d] = gv;
     }
     if (tid < 16) {
-        sh.beta[tid] = tid < nvalid ? ldx(bt, (bos + tid) * p.HV + j) : 0.f;
+        float bv = tid < nvalid ? ldx(bt, (bos + tid) * p.HV + j) : 0.f;
+        if (p.pre.beta_sigmoid && tid < nvalid) bv = sigmoid_f(bv);
+        sh.beta[tid] = bv;
         sh.dbeta[tid] = 0.f;
     }
     __syncthreads();
+    if (p.pre.qk_l2norm) {         // 16 threads per token row: partial sums, xor reduction
+        const int rr = tid >> 4, l = tid & 15;
+        float a = 0.f, c = 0.f;
+        for (int d = l; d < K; d += 16) {
+            a += sh.q[rr][d] * sh.q[rr][d];
+            c += sh.k[rr][d] * sh.k[rr][d];
+        }
+        for (int m = 1; m < 16; m <<= 1) {
+            a += __shfl_xor(a, m);
+            c += __shfl_xor(c, m);
+        }
+        const float fq = l2norm_factor(a), fk = l2norm_factor(c);
+        for (int d = l; d < K; d += 16) {
+            sh.q[rr][d] *= fq;
+            sh.k[rr][d] *= fk;
+        }
+        __syncthreads();
+    }
     for (int d = tid; d < K; d += 256) {
         float acc = 0.f;
         for (int r = 0; r < 16; ++r) { acc += sh.gm[r][d]; sh.gm[r][d] = acc; }
@@ -518,9 +557,10 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
 
     // ---- per (token, key dim): dk, dq and dGam; dKD = A^T dW
     // dGam is written over dQD: entry (t, d) of dQD is read only by the thread that owns (t, d)
-    float *dq_out = p.G > 1 ? b.part_q : b.dq;
-    float *dk_out = p.G > 1 ? b.part_k : b.dk;
-    const int qk_heads = p.G > 1 ? p.HV : p.H, qk_head = p.G > 1 ? j : h;
+    const bool via_part = p.G > 1 || p.pre.qk_l2norm;
+    float *dq_out = via_part ? b.part_q : b.dq;
+    float *dk_out = via_part ? b.part_k : b.dk;
+    const int qk_heads = via_part ? p.HV : p.H, qk_head = via_part ? j : h;
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int t = idx / K, d = idx % K;
         float dkd = 0.f;
@@ -560,37 +600,134 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         sh.dqd[t][d] = dgam;
     }
     __syncthreads();
-    // ---- dgam = dE E + sum_t dKR KR; dg_tau = sum_{t >= tau} dGam_t + dgam; dbeta out
+    // ---- dgam = dE E + sum_t dKR KR; dg_tau = sum_{t >= tau} dGam_t + dgam; through the
+    // gate (raw g reloaded): dg_raw = dg * slope, and this chunk's share of dA_log, ddt_bias
+    float gA = 0.f;
     for (int d = tid; d < K; d += 256) {
         float dgam = sh.dE[d] * sh.E[d];
         for (int t = 0; t < 16; ++t) dgam += sh.dkr[t][d] * sh.kr[t][d];
-        float acc = dgam;
+        float acc = dgam, adt = 0.f;
         for (int t = 15; t >= 0; --t) {
             acc += sh.dqd[t][d];
-            if (t < nvalid) b.dg[((bos + t) * p.HV + j) * K + d] = acc;
+            if (t < nvalid) {
+                const int64_t o = ((bos + t) * p.HV + j) * K + d;
+                float dgo = acc;
+                if (gated) {
+                    const float x = ldx(g, o) + dtb(d);
+                    float slope, dfa;                  // dg/dx and dg/dA_log
+                    if (p.pre.gate == 1) {
+                        slope = -aexp * sigmoid_f(x);
+                        dfa = -aexp * softplus_f(x);
+                    } else {
+                        const float sg = sigmoid_f(aexp * x);
+                        slope = p.pre.lower_bound * sg * (1.f - sg) * aexp;
+                        dfa = slope * x;
+                    }
+                    dgo = acc * slope;
+                    adt += dgo;
+                    gA += acc * dfa;
+                }
+                b.dg[o] = dgo;
+            }
         }
+        if (gated) b.part_dt[gslot * K + d] = adt;
     }
-    if (tid < nvalid) b.dbeta[(bos + tid) * p.HV + j] = sh.dbeta[tid];
+    if (gated) {                   // block sum of gA (the threads d < K carry a share)
+        gA = wave_sum(gA);
+        __syncthreads();
+        if ((tid & 63) == 0) sh.dA[0][tid >> 6] = gA;
+        __syncthreads();
+        if (tid == 0) b.part_A[gslot] = sh.dA[0][0] + sh.dA[0][1] + sh.dA[0][2] + sh.dA[0][3];
+    }
+    if (tid < nvalid) {
+        float db = sh.dbeta[tid];
+        if (p.pre.beta_sigmoid) {
+            const float sg = sigmoid_f(ldx(bt, (bos + tid) * p.HV + j));
+            db *= sg * (1.f - sg);
+        }
+        b.dbeta[(bos + tid) * p.HV + j] = db;
+    }
 }
 
-// dq, dk of q/k head h = sum of the partials of its G value heads (fixed order: deterministic)
-template <int K>
-__global__ void bwd_group_sum_kernel(BwdParams b)
+// dq, dk of q/k head h: the partials of its G value heads summed in a fixed order
+// (deterministic), then, with the L2 norm on, carried through it: with r = (|x|^2 + eps)^-1/2
+// and y = x r for the raw row x, dx = r (dy - y (y . dy)). One wave per (token, q/k head) row.
+template <int K, typename T>
+__global__ __launch_bounds__(256) void bwd_qk_finalize_kernel(BwdParams b)
 {
-    const int64_t n = b.f.seq.T_total * b.f.H * K;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t tok = i / ((int64_t)b.f.H * K);
-        const int h = (int)((i / K) % b.f.H), d = (int)(i % K);
-        float aq = 0.f, ak = 0.f;
-        for (int jj = 0; jj < b.f.G; ++jj) {
-            const int64_t o = (tok * b.f.HV + h * b.f.G + jj) * K + d;
-            aq += b.part_q[o];
-            ak += b.part_k[o];
+    const FwdParams &p = b.f;
+    constexpr int PL = K / 64;                      // elements per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = p.seq.T_total * p.H;
+    const int64_t wid = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t row = wid; row < rows; row += nw) {
+        const int64_t tok = row / p.H;
+        const int h = (int)(row % p.H);
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const float *part = which ? b.part_k : b.part_q;
+            float dy[PL];
+#pragma unroll
+            for (int e = 0; e < PL; ++e) {
+                float acc = 0.f;
+                for (int jj = 0; jj < p.G; ++jj)
+                    acc += part[(tok * p.HV + h * p.G + jj) * K + lane + 64 * e];
+                dy[e] = acc;
+            }
+            if (p.pre.qk_l2norm) {
+                const T *x = (const T *)(which ? p.k : p.q) + (tok * p.H + h) * K;
+                float xv[PL], ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < PL; ++e) {
+                    xv[e] = ldx(x, lane + 64 * e);
+                    ss += xv[e] * xv[e];
+                }
+                const float r = l2norm_factor(wave_sum(ss));
+                float yd = 0.f;
+#pragma unroll
+                for (int e = 0; e < PL; ++e) yd += xv[e] * r * dy[e];
+                yd = wave_sum(yd);
+#pragma unroll
+                for (int e = 0; e < PL; ++e) dy[e] = r * (dy[e] - xv[e] * r * yd);
+            }
+            float *out = (which ? b.dk : b.dq) + (tok * p.H + h) * K;
+#pragma unroll
+            for (int e = 0; e < PL; ++e) out[lane + 64 * e] = dy[e];
         }
-        b.dq[i] = aq;
-        b.dk[i] = ak;
     }
+}
+
+// dA_log[j] and ddt_bias[j][:]: per-chunk partials summed over the slots in a fixed order.
+template <int K>
+__global__ __launch_bounds__(256) void bwd_param_kernel(BwdParams b)
+{
+    const FwdParams &p = b.f;
+    __shared__ float red[256];
+    const int j = blockIdx.x, tid = threadIdx.x;
+    const size_t s0 = (size_t)j * p.seq.n_slots;
+    if (p.seq.T_total == 0) {      // no tokens: no chunk partials were written
+        for (int d = tid; d < K; d += 256)
+            if (b.ddt_bias) b.ddt_bias[j * K + d] = 0.f;
+        if (tid == 0) b.dA_log[j] = 0.f;
+        return;
+    }
+    if (b.ddt_bias) {
+        for (int d = tid; d < K; d += 256) {
+            float acc = 0.f;
+            for (int sl = 0; sl < p.seq.n_slots; ++sl) acc += b.part_dt[(s0 + sl) * K + d];
+            b.ddt_bias[j * K + d] = acc;
+        }
+    }
+    float acc = 0.f;
+    for (int sl = tid; sl < p.seq.n_slots; sl += 256) acc += b.part_A[s0 + sl];
+    red[tid] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) b.dA_log[j] = red[0];
 }
 
 }  // namespace
@@ -610,14 +747,22 @@ hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st)
     else
         bwd_chains_kernel<K, V, float><<<cgrid, dim3(64 * CHAIN_WAVES), 0, st>>>(b);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.seq.T_total == 0) return hipSuccess;
-    dim3 grid(p.seq.n_slots, p.HV);
-    if (in_bf16)
-        bwd_local_kernel<K, V, uint16_t><<<grid, dim3(256), 0, st>>>(b);
-    else
-        bwd_local_kernel<K, V, float><<<grid, dim3(256), 0, st>>>(b);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.G > 1) bwd_group_sum_kernel<K><<<dim3(1024), dim3(256), 0, st>>>(b);
+    if (p.seq.T_total > 0) {
+        dim3 grid(p.seq.n_slots, p.HV);
+        if (in_bf16)
+            bwd_local_kernel<K, V, uint16_t><<<grid, dim3(256), 0, st>>>(b);
+        else
+            bwd_local_kernel<K, V, float><<<grid, dim3(256), 0, st>>>(b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (p.G > 1 || p.pre.qk_l2norm) {
+            if (in_bf16)
+                bwd_qk_finalize_kernel<K, uint16_t><<<dim3(1024), dim3(256), 0, st>>>(b);
+            else
+                bwd_qk_finalize_kernel<K, float><<<dim3(1024), dim3(256), 0, st>>>(b);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    if (p.pre.gate) bwd_param_kernel<K><<<dim3(p.HV), dim3(256), 0, st>>>(b);
     return hipGetLastError();
 }
 

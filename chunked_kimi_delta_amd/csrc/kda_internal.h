@@ -80,7 +80,12 @@ struct BwdParams {
     float *dg;                // [T_total][HV][K]
     float *dbeta;             // [T_total][HV]
     float *dh0;               // [N][HV][K][V] or null
-    float *part_q, *part_k;   // [T_total][HV][K] per-value-head dq, dk (G > 1 only)
+    float *part_q, *part_k;   // [T_total][HV][K] per-value-head dq, dk of the activated q, k
+                              // (G > 1 or q/k L2 norm; else null and dq, dk are written
+                              // directly)
+    float *dA_log;            // [HV] gradient of A_log (gate on)
+    float *ddt_bias;          // [HV][K] gradient of dt_bias (gate on), or null
+    float *part_A, *part_dt;  // [HV][n_slots], [HV][n_slots][K]: per-chunk parameter partials
 };
 
 // Workspace of one (value head, slot) chunk, bf16 io. All fragments are stored in the exact
@@ -325,6 +330,13 @@ __device__ __forceinline__ float row_inclusive_scan(float x) {
 __device__ __forceinline__ float sum_lane_groups(float x) {
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Sum of x over the 64 lanes of a wave (every lane gets the sum).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
     return x;
 }
 

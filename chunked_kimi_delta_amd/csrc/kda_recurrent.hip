@@ -34,12 +34,6 @@ struct TokenRow {
     f32x4 qkeb[K];               // per key dim: q, k, exp(g), beta * k
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-    return x;
-}
-
 }  // namespace
 
 template <int K, int V, typename T>

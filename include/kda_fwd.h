@@ -140,37 +140,47 @@ kda_status kda_fwd_state(const kda_fwd_args *args, void *workspace, size_t ws_by
                          void *stream);
 
 /* ---------------------------------------------------------------------------- backward
-   Gradients of the forward above with respect to q, k, v, g, beta and initial_state, given
-   the gradients of a loss with respect to o (d_o) and to final_state (dht): the reverse sweep
-   of the C++ chunk backward of "手撕KDA" section 2.1, which walks the chunks newest first and
-   carries the gradient of the state from the final-state gradient back to the initial state.
+   Gradients of the forward above with respect to q, k, v, g, beta, initial_state and (with a
+   gate) A_log and dt_bias, given the gradients of a loss with respect to o (d_o) and to
+   final_state (dht): the reverse sweep of the C++ chunk backward of "手撕KDA" section 2.1,
+   which walks the chunks newest first and carries the gradient of the state from the
+   final-state gradient back to the initial state, followed by the backward of its pre-stage.
    The library records the state at every chunk start in a forward pass over the chunks, runs
-   the state-gradient chain newest first, and then back-propagates every (chunk, value head)
-   independently to its tokens (through the chunk's u, w, Mqk, the inverse of (I + L) and the
-   in-chunk cumsum of g). fp32 arithmetic, 16-token chunks.
+   the state-gradient chain newest first (both chains in one launch), then back-propagates
+   every (chunk, value head) independently to its tokens (through the chunk's u, w, Mqk, the
+   inverse of (I + L) and the in-chunk cumsum of g) and finally through the pre-stage. fp32
+   arithmetic, 16-token chunks.
 
-   Arguments: `args` as for kda_fwd (o and final_state are not read; chunk must be 0 or 16;
-   the pre-stage fields must be zero: the gradients are those of q, k, g, beta as the
-   recurrence reads them). Device buffers, 16-byte aligned, caller-owned:
-     d_o    [B, T, HV, V]  io dtype   gradient of o (required when B*T > 0)
-     dht    [N, HV, K, V]  fp32       gradient of final_state, or NULL for zero
-     dq, dk [B, T, H, K]   fp32       written (summed over the value heads of a q/k head)
-     dv     [B, T, HV, V]  fp32       written
-     dg     [B, T, HV, K]  fp32       written
-     dbeta  [B, T, HV]     fp32       written
-     dh0    [N, HV, K, V]  fp32       gradient of initial_state, or NULL to skip
+   Arguments: `args` as for kda_fwd with the same inputs (raw inputs when the pre-stage is on;
+   o and final_state are not read; chunk must be 0 or 16). Device buffers, caller-owned,
+   16-byte aligned unless stated:
+     d_o      [B, T, HV, V]  io dtype   gradient of o (required when B*T > 0)
+     dht      [N, HV, K, V]  fp32       gradient of final_state, or NULL for zero
+     dq, dk   [B, T, H, K]   fp32       written (summed over the value heads of a q/k head)
+     dv       [B, T, HV, V]  fp32       written
+     dg       [B, T, HV, K]  fp32       written
+     dbeta    [B, T, HV]     fp32       written
+     dh0      [N, HV, K, V]  fp32       gradient of initial_state, or NULL to skip
+     dA_log   [HV]           fp32       gradient of A_log (4-byte aligned); required with a
+                                        gate, ignored without
+     ddt_bias [HV, K]        fp32       gradient of dt_bias (also when dt_bias is NULL: the
+                                        gradient of a zero bias), or NULL to skip
+   dq, dk, dg, dbeta are the gradients of the arguments as passed: with the pre-stage on, of
+   the raw q, k, g, beta.
    `workspace`: at least kda_bwd_workspace_bytes(args) bytes, 256-byte aligned, contents on
-   entry irrelevant (the fp32 chunk records, the state at every chunk start and the state
-   gradient at every chunk end: about 2 * (B*T/16 + N) * HV * K * V * 4 bytes, plus
-   2 * B*T * HV * K * 4 bytes when HV > H). Status codes as for kda_fwd; KDA_ERR_UNSUPPORTED
-   also for a chunk other than 0 or 16 and for a pre-stage that is switched on. The same g
-   limit as fp32 io of the forward applies (none in practice: every exponent the kernels
-   form is a difference of in-chunk cumsums with the later one first). Deterministic.    */
+   entry irrelevant: the fp32 chunk records, the state at every chunk start and the state
+   gradient at every chunk end (about 2 * (B*T/16 + N) * HV * K * V * 4 bytes), plus
+   2 * B*T * HV * K * 4 bytes when HV > H or the q/k L2 norm is on, plus (B*T/16 + N) * HV *
+   (K + 1) * 4 bytes with a gate. Status codes as for kda_fwd; KDA_ERR_UNSUPPORTED also for a
+   chunk other than 0 or 16; KDA_ERR_INVALID_ARG also for a missing or misaligned dA_log with
+   a gate. The g limit of fp32 io of the forward applies (none in practice: every exponent the
+   kernels form is a difference of in-chunk cumsums with the later one first). Deterministic
+   (fixed-order sums, no atomics). With N = 0 nothing is written.                          */
 size_t kda_bwd_workspace_bytes(const kda_fwd_args *args);
 
 kda_status kda_bwd(const kda_fwd_args *args, const void *d_o, const float *dht,
                    void *workspace, size_t ws_bytes, float *dq, float *dk, float *dv, float *dg,
-                   float *dbeta, float *dh0, void *stream);
+                   float *dbeta, float *dh0, float *dA_log, float *ddt_bias, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_strerror(int status);

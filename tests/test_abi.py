@@ -173,8 +173,12 @@ def test_bwd_workspace_bytes(lib):
         rec = lib.kda_fwd_workspace_bytes(ctypes.byref(args(**dict(kw, io=1, chunk=16))))
         part = B * T * HV * K * 4 if HV > H else 0
         assert f(a) == up(rec) + 2 * up(slots * HV * K * V * 4) + 2 * up(part), kw
+    base = f(args())
+    slots = 4096 // 16 + 1
+    assert f(args(qk_l2norm=1)) == base + 2 * up(4096 * 16 * 128 * 4)     # dq, dk partials
+    assert f(args(gate=1)) == base + up(slots * 16 * 4) + up(slots * 16 * 128 * 4)
+    assert f(args(beta_sigmoid=1)) == base
     assert f(args(chunk=32)) == 0 and f(args(chunk=1)) == 0     # 16-token chunks only
-    assert f(args(qk_l2norm=1)) == 0 and f(args(gate=1)) == 0   # no pre-stage
     assert f(args(K=96)) == 0 and f(args(HV=24)) == 0
 
 
@@ -182,7 +186,8 @@ def test_kda_bwd_rejects_bad_arguments(lib):
     fake = 1 << 40                                 # never dereferenced: rejected before launch
     call = lambda a, **kw: lib.kda_bwd(
         ctypes.byref(a), kw.get("do"), kw.get("dht"), kw.get("ws"), kw.get("nbytes", 0),
-        *[kw.get(n, fake) for n in ("dq", "dk", "dv", "dg", "dbeta")], kw.get("dh0"), None)
+        *[kw.get(n, fake) for n in ("dq", "dk", "dv", "dg", "dbeta")], kw.get("dh0"),
+        kw.get("dA"), kw.get("ddt"), None)
     a = args(T=32)
     assert call(a, do=fake) == _lib.KDA_ERR_INVALID_ARG          # null q, k, v, g, beta
     for name in ("q", "k", "v", "g", "beta"):
@@ -195,8 +200,16 @@ def test_kda_bwd_rejects_bad_arguments(lib):
     assert call(a, do=fake, ws=fake, nbytes=need - 1) == _lib.KDA_ERR_WORKSPACE
     assert call(a, do=fake, ws=fake + 16, nbytes=need) == _lib.KDA_ERR_WORKSPACE
     assert call(args(T=32, chunk=32), do=fake) == _lib.KDA_ERR_UNSUPPORTED
-    assert call(args(T=32, beta_sigmoid=1), do=fake) == _lib.KDA_ERR_UNSUPPORTED
+    pre = args(T=32, gate=1, A_log=fake)
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(pre, name, fake)
+    assert call(pre, do=fake) == _lib.KDA_ERR_INVALID_ARG          # a gate needs dA_log
+    assert call(pre, do=fake, dA=fake + 2) == _lib.KDA_ERR_INVALID_ARG
+    assert call(pre, do=fake, dA=fake, ddt=fake + 4) == _lib.KDA_ERR_INVALID_ARG
+    assert call(pre, do=fake, dA=fake) == _lib.KDA_ERR_WORKSPACE
+    pre.gate = 3
+    assert call(pre, do=fake, dA=fake) == _lib.KDA_ERR_UNSUPPORTED
     assert call(args(T=32, K=96), do=fake) == _lib.KDA_ERR_UNSUPPORTED
     assert call(args(T=32, N=2), do=fake) == _lib.KDA_ERR_INVALID_ARG
-    assert lib.kda_bwd(None, None, None, None, 0, *([None] * 6), None) == \
+    assert lib.kda_bwd(None, None, None, None, 0, *([None] * 8), None) == \
         _lib.KDA_ERR_INVALID_ARG

@@ -152,9 +152,9 @@ def test_backward_full_size_sampled(name, n_units):
     gr = W.make_grads(inp, seed=0)
     print(f"[bwd full] {name}: GPU backward", file=sys.stderr, flush=True)
     got = gpu_bwd(inp, gr)
-    for x in got:
+    for x in got[:6]:
         assert np.isfinite(x).all()
-    dq, dk, dv, dg, db, dh0 = got
+    dq, dk, dv, dg, db, dh0 = got[:6]
     flat = lambda x: x.reshape(-1, *x.shape[2:])
     units = W.sample_units(inp.N, w.H, n_units, seed=7)
     for s, h in units:
@@ -166,3 +166,93 @@ def test_backward_full_size_sampled(name, n_units):
                 flat(dv)[bos:eos, js][None], flat(dg)[bos:eos, js][None],
                 flat(db)[bos:eos, js][None], dh0[s:s + 1, js])
         check_grads(mine, ref)
+
+
+# --------------------------------------------------------------------------- with the pre-stage
+
+PRE_SHAPES = {
+    "bf16_gva_b2_t100_h0": W.custom(B=2, T=100, H=2, HV=4, K=128, V=128, h0_std=0.1),
+    "bf16_varlen_edges": W.custom(H=1, HV=2, K=128, V=128, h0_std=0.1,
+                                  lengths=(0, 1, 17, 33, 64)),
+    "bf16_k64v64_t50": W.custom(B=1, T=50, H=2, HV=2, K=64, V=64),
+    "fp32_k128v64_t70": W.custom(B=1, T=70, H=1, HV=2, K=128, V=64, dtype="fp32"),
+}
+PNAMES = NAMES + ("dA_log", "ddt_bias")
+
+
+def gpu_bwd_raw(raw: W.RawInputs, gr: W.Grads, pre):
+    inp = raw.inp
+    plan = kda.KdaBwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                          dev(gr.d_o), dev(gr.dht), scale=inp.scale,
+                          cu_seqlens=dev(inp.cu_seqlens), initial_state=dev(inp.h0),
+                          use_qk_l2norm=pre.get("l2", False),
+                          use_beta_sigmoid=pre.get("sig", False), gate=pre.get("gate"),
+                          A_log=dev(raw.A_log), dt_bias=dev(pre.get("dt", raw.dt_bias)),
+                          gate_lower_bound=pre.get("lb", -5.0))
+    out = plan()
+    torch.cuda.synchronize()
+    return tuple(f64(x) for x in out)
+
+
+def oracle_bwd_raw(raw: W.RawInputs, gr: W.Grads, pre):
+    from oracle.backward import kda_backward_raw
+    inp = raw.inp
+    f = W.as_f32_numpy
+    dt = pre.get("dt", raw.dt_bias)
+    return kda_backward_raw(
+        f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.scale,
+        None if inp.h0 is None else inp.h0.numpy(),
+        None if inp.cu_seqlens is None else inp.cu_seqlens.numpy(),
+        f(gr.d_o), None if gr.dht is None else gr.dht.numpy(),
+        pre.get("l2", False), pre.get("sig", False), pre.get("gate"), raw.A_log.numpy(),
+        None if dt is None else dt.numpy(), pre.get("lb", -5.0))
+
+
+def check_raw(got, ref, pre):
+    check_grads(got[:6], ref[:6])
+    if pre.get("gate"):
+        errs = {n: rel_l2(a, b) for n, a, b in zip(PNAMES[6:], got[6:], ref[6:])}
+        report_named(**errs)
+        assert all(e <= TOL for e in errs.values()), errs
+    else:
+        assert got[6] is None and got[7] is None
+
+
+@pytest.mark.parametrize("gate", ["softplus", "bounded"])
+@pytest.mark.parametrize("name", list(PRE_SHAPES))
+def test_backward_prestage_parity(name, gate):
+    raw = W.make_raw_inputs(PRE_SHAPES[name], seed=31)
+    gr = W.make_grads(raw.inp, seed=31)
+    pre = {"l2": True, "sig": True, "gate": gate, "lb": -4.0}
+    check_raw(gpu_bwd_raw(raw, gr, pre), oracle_bwd_raw(raw, gr, pre), pre)
+
+
+@pytest.mark.parametrize("step", ["l2", "sig", "softplus_no_bias", "bounded"])
+def test_backward_prestage_steps_one_at_a_time(step):
+    pre = {"l2": {"l2": True}, "sig": {"sig": True},
+           "softplus_no_bias": {"gate": "softplus", "dt": None},
+           "bounded": {"gate": "bounded", "lb": -6.0}}[step]
+    # the ordinary inputs (unit q, k rows, log decays, beta in (0, 1)) with the raw form of the
+    # one input the step activates: unnormalised q, k would make the recurrence diverge
+    raw = W.make_raw_inputs(W.custom(B=1, T=45, H=2, HV=4, K=128, V=128, h0_std=0.2), seed=7)
+    base = W.make_inputs(raw.inp.w, seed=7)
+    if "l2" in pre:
+        base.q, base.k = raw.inp.q, raw.inp.k
+    if "sig" in pre:
+        base.beta = base.beta * 4 - 2
+    if "gate" in pre:
+        base.g = raw.inp.g
+    raw = W.RawInputs(base, raw.A_log, raw.dt_bias)
+    gr = W.make_grads(raw.inp, seed=7)
+    check_raw(gpu_bwd_raw(raw, gr, pre), oracle_bwd_raw(raw, gr, pre), pre)
+
+
+def test_backward_prestage_full_size_bounded_gate():
+    # every unit of h16_t4096 (dA_log and dt_bias sum over all of them)
+    raw = W.make_raw_inputs(W.WORKLOADS["h16_t4096"], seed=3)
+    gr = W.make_grads(raw.inp, seed=3)
+    pre = {"l2": True, "sig": True, "gate": "bounded", "lb": -5.0}
+    print("[bwd pre full] GPU backward", file=sys.stderr, flush=True)
+    got = gpu_bwd_raw(raw, gr, pre)
+    print("[bwd pre full] oracle", file=sys.stderr, flush=True)
+    check_raw(got, oracle_bwd_raw(raw, gr, pre), pre)
