@@ -10,6 +10,9 @@ roofline figures comes from a second pass of --steps steps, the two stages launc
 (kda_fwd_prepare, kda_fwd_state: the same kernels) with HIP events around each launch on the
 stream it runs on.
 
+With --backward the step is one kda_bwd call instead (gradients of every input from seeded
+d_o and dht), reported under its own metric; the default line is the forward.
+
 Extra fields beyond the driver contract:
   roofline        dominant kernel: achieved algorithmic throughput / MI355X peak
   roofline_path   the whole forward against the HBM roof (algorithmic bytes / step time)
@@ -33,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KDA fwd tokens/s (all heads) @H=16,T=4096,K=V=128 bf16; HBM GB/s, MFMA %"
+METRIC_BWD = "KDA bwd tokens/s (all heads); gradients of q, k, v, g, beta, h0 (fp32)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense; fp16 == bf16
 
@@ -134,6 +138,82 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
     return res
 
 
+def backward_work(inp):
+    """Algorithmic bytes of one backward: read q, k (per q/k head), v, g, beta, d_o in the io
+    dtype and the fp32 initial state and dht; write fp32 dq, dk, dv, dg, dbeta and dh0."""
+    w = inp.w
+    es = 2 if w.dtype == "bf16" else 4
+    T_total, N = inp.T_total, inp.N
+    H, HV, K, V = w.H, w.HV, w.K, w.V
+    rd = T_total * (H * 2 * K * es + HV * (2 * V * es + K * es + es))
+    rd += N * HV * K * V * 4 * (1 + (inp.h0 is not None))
+    wr = T_total * (H * 2 * K * 4 + HV * (V + K + 1) * 4) + N * HV * K * V * 4
+    return rd + wr
+
+
+def cpu_baseline_bwd(inp, gr, min_seconds: float):
+    """The fp64 oracle backward (numpy reverse recurrence, unchanged) on one (sequence, value
+    head) slice of up to 512 tokens, repeated for at least `min_seconds`; scaled to the
+    workload's tokens/s (all heads)."""
+    import workloads as W
+    from oracle.backward import kda_backward_recurrent
+    T = min(512, inp.q.shape[1])
+    f = lambda x: W.as_f32_numpy(x)[:1, :T]
+    args = [f(inp.q)[:, :, :1], f(inp.k)[:, :, :1], f(inp.v)[:, :, :1], f(inp.g)[:, :, :1],
+            f(inp.beta)[:, :, :1]]
+    do = f(gr.d_o)[:, :, :1]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        kda_backward_recurrent(*args, inp.scale, None, None, do, None)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 1000:
+            break
+    return {"value": round(reps * T / inp.w.HV / el, 2), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle backward (fp64 numpy reverse recurrence) of {T} tokens of one "
+                      f"value head, repeated {reps}x in {el:.1f} s; tokens/s of all "
+                      f"{inp.w.HV} heads = head-tokens/s / {inp.w.HV}"}
+
+
+def run_backward(a, torch, W, kda):
+    w = W.WORKLOADS[a.workload]
+    inp = W.make_inputs(w, seed=0)
+    gr = W.make_grads(inp, seed=0)
+    dev = torch.device("cuda:0")
+    d = lambda x: None if x is None else x.to(dev).contiguous()
+    plan = kda.KdaBwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta), d(gr.d_o),
+                          d(gr.dht), scale=inp.scale, cu_seqlens=d(inp.cu_seqlens),
+                          initial_state=d(inp.h0))
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(a.warmup):
+        plan(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        plan(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    nb = backward_work(inp)
+    gbs = nb / (ms * 1e-3) / 1e9
+    cpu = cpu_baseline_bwd(inp, gr, a.cpu_seconds) if a.cpu_seconds > 0 else None
+    out = {
+        "metric": METRIC_BWD, "value": round(inp.T_total / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
+                   "K": w.K, "V": w.V, "chunk": 16, "io": w.dtype,
+                   "tokens_per_step": inp.T_total, "parallelism": "single-gpu"},
+        "roofline_path": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
+                          "alg_bytes_per_step": nb},
+        "kernel_timing": "per-kernel durations: rocprofv3 --kernel-trace of this command",
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inp, min_seconds: float):
     """The fp64 C oracle (unchanged) on the host cores: the whole workload, repeated until at
     least `min_seconds` of wall time have passed (bounded at 1000 repetitions)."""
@@ -183,6 +263,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<kernel>_<workload>.txt from two --pmc runs")
     ap.add_argument("--command", default="", help="the profiling command, for the summaries")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (kda_bwd) instead of the forward")
     a = ap.parse_args()
 
     if a.summarize_trace:
@@ -207,6 +289,10 @@ def main():
     import torch
     import workloads as W
     import chunked_kimi_delta_amd as kda
+
+    if a.backward:
+        run_backward(a, torch, W, kda)
+        return
 
     w = W.WORKLOADS[a.workload]
     pre = {}

@@ -47,6 +47,8 @@ __device__ __forceinline__ float ldx(const uint16_t *p, int64_t i) {
 // in flight across it.
 //   states:  delta = u - w S;  S <- diag(E) S + kr^T delta
 //   grads:   dDelta = Mqk^T dO + kr Lam;  Lam <- diag(E) Lam + qd^T dO - w^T dDelta
+// S and Lam are recorded per chunk in tile order ([V/16 slice][K/16 tile][64 lanes][4 fp32],
+// the C-layout registers as they are), one 1 KB contiguous block per tile and wave.
 // The chunk records are read as they are laid out ([16][K] row-major w, qd, kr; [16][V] u;
 // [16][16] Mqk; [K] E): A-operand rows of w and kr are contiguous 16-byte loads, their
 // transposes four 4-byte loads. Records of the next chunk are loaded before the current
@@ -133,11 +135,15 @@ __device__ __forceinline__ void chain_run(const BwdParams &b, int unit, int n0, 
     // one chunk with the operands in `o` (loaded one chunk earlier)
     auto step = [&](const ChainOps<K> &o, int it) {
         const int c = GRAD ? nc - 1 - it : it;
-        float *cko = (GRAD ? b.ck_L : b.ck_S) + (slot0 + c) * (size_t)K * V;
+        // the record of this chunk, tile order: [V/16 slice][K/16 tile][64 lanes][4]; two
+        // 8-byte stores per tile (see bstore16 for why stores stay at 8 bytes)
+        float *cko = (GRAD ? b.ck_L : b.ck_S) + (slot0 + c) * (size_t)K * V +
+                     ((size_t)(n0 / 16) * (K / 16) + wave * TPW) * 256 + lane * 4;
 #pragma unroll
-        for (int x = 0; x < TPW; ++x)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cko[at(x, i)] = X[x][i];
+        for (int x = 0; x < TPW; ++x) {
+            *(float2 *)(cko + x * 256) = float2{X[x][0], X[x][1]};
+            *(float2 *)(cko + x * 256 + 2) = float2{X[x][2], X[x][3]};
+        }
         f32x4 ox = o.x;
         if (GRAD) {                   // dO rows past the sequence end are zero
 #pragma unroll
@@ -222,21 +228,43 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams 
 //     delta = A v - W S,  dDelta = Mqk^T dO + KR Lam           (partials summed through LDS)
 //     dQD += dO S^T,  dKR += delta Lam^T,  dW -= dDelta S^T     (the wave's own K tiles)
 //     dE += rowsum(Lam . S),  dMqk += dO delta^T,  dA += dDelta v^T,  dv = A^T dDelta
-// S and Lam are read from the row-major K x V records in two register layouts: C-layout (the B
-// operand of a product over K) and its transpose (the B operand of a product over V, one
-// 16-byte load per tile). The rest of the chunk's algebra (16 x 16 and 16 x K) is scalar.
+// S and Lam are read as the chains recorded them (C-layout tiles, one 16-byte load per tile and
+// lane) and are needed in two register layouts: C-layout (the B operand of a product over K)
+// and its transpose (the B operand of a product over V), made through a wave-private LDS tile.
+// The rest of the chunk's algebra (16 x 16 and 16 x K) is scalar.
 template <int K, int V>
 struct alignas(16) LocalShare {
     float q[16][K + 1], k[16][K + 1], gm[16][K + 1];   // q, k, Gam (cumsum of g)
-    float w[16][K + 1], kr[16][K + 1];                 // W = A KD, KR
-    union alignas(16) {
-        struct { float dqd[16][K + 1], dkr[16][K + 1], dw[16][K + 1]; };
-        float part[2][2][CHAIN_WAVES][16][20];         // V-block partials of delta, dDelta
+    float kr[16][K + 1];                               // KR
+    union alignas(16) {                                // three phases, one region
+        float w[16][K + 1];                            // W = A KD (until its registers are set)
+        struct {                                       // the V loop
+            float part[2][2][CHAIN_WAVES][16][20];     // V-block partials of delta, dDelta
+            float tr[CHAIN_WAVES][16][17];             // per-wave tile transposes
+        };
+        struct { float dqd[16][K + 1], dkr[16][K + 1], dw[16][K + 1]; };   // after it
     };
     float G[16][17], Mq[16][17], X[16][17], A[16][17], P[16][17], T1[16][17];
     float dA[16][17], dMq[16][17], dL[16][17];
     float beta[16], dbeta[16], E[K], dE[K];
 };
+
+// A 16 x 16 fp32 tile held in C-layout (lane: rows 4g + i, column r) returned in the transposed
+// arrangement (lane: row r, columns 4g + i), through a wave-private LDS tile. LDS operations of
+// one wave complete in order, so no barrier is needed; the scheduling barriers keep the
+// compiler from moving the accesses of one use across those of the next.
+__device__ __forceinline__ f32x4 tile_transpose(float (&t)[16][17], f32x4 c, int r, int g)
+{
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[4 * g + i][r] = c[i];
+    __builtin_amdgcn_wave_barrier();
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = t[r][4 * g + i];
+    __builtin_amdgcn_wave_barrier();
+    return o;
+}
 
 // four consecutive values of an io-dtype row as fp32
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *(const f32x4 *)p; }
@@ -252,7 +280,7 @@ __device__ __forceinline__ f32x4 ld4(const uint16_t *p) {
 template <int K>
 struct BlockOps {
     static constexpr int TPW = K / 16 / CHAIN_WAVES;
-    f32x4 sc[TPW], sa[TPW], lc[TPW], la[TPW];   // S, Lam: C-layout and transposed layout
+    f32x4 sc[TPW], lc[TPW];                     // S, Lam tiles (C-layout)
     f32x4 doc, doa, vc, va;                     // dO, v: C-layout (rows 4g+i) and row r
 };
 
@@ -388,8 +416,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         At[i] = sh.A[4 * gq + i][r];
         Mqt[i] = sh.Mq[4 * gq + i][r];
     }
-    const float *cS = b.ck_S + gslot * (size_t)K * V;
-    const float *cL = b.ck_L + gslot * (size_t)K * V;
+    __syncthreads();                                  // w's region is the V loop's from here
+    const float *cS = b.ck_S + gslot * (size_t)K * V + wave * TPW * 256 + lane * 4;
+    const float *cL = b.ck_L + gslot * (size_t)K * V + wave * TPW * 256 + lane * 4;
     const int rc = r < nvalid ? r : nvalid - 1;               // clamped rows: loads stay inside
     int rq[4];
 #pragma unroll
@@ -398,14 +427,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         const int n0 = nb * 16;
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
-            const int k0 = (wave * TPW + x) * 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o.sc[x][i] = cS[(size_t)(k0 + 4 * gq + i) * V + n0 + r];
-                o.lc[x][i] = cL[(size_t)(k0 + 4 * gq + i) * V + n0 + r];
-            }
-            o.sa[x] = *(const f32x4 *)(cS + (size_t)(k0 + r) * V + n0 + 4 * gq);
-            o.la[x] = *(const f32x4 *)(cL + (size_t)(k0 + r) * V + n0 + 4 * gq);
+            o.sc[x] = *(const f32x4 *)(cS + ((size_t)nb * (K / 16) + x) * 256);
+            o.lc[x] = *(const f32x4 *)(cL + ((size_t)nb * (K / 16) + x) * 256);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -429,6 +452,13 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
             vc[i] = okq ? vc[i] : 0.f;
             doa[i] = r < nvalid ? doa[i] : 0.f;
             va[i] = r < nvalid ? va[i] : 0.f;
+        }
+        // transposed layouts of the S and Lam tiles: element (r, 4g + i) of the tile
+        f32x4 sa[TPW], la[TPW];
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            sa[x] = tile_transpose(sh.tr[wave], o.sc[x], r, gq);
+            la[x] = tile_transpose(sh.tr[wave], o.lc[x], r, gq);
         }
         f32x4 pd = zero4(), pk = zero4();
 #pragma unroll
@@ -464,11 +494,11 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         // dtr, ddtr: delta, dDelta in the transposed layout (row r); ddc: dDelta in C-layout
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
-            aq[x] = mm16_f32(doa, o.sa[x], aq[x]);          // dQD += dO S^T
-            ar[x] = mm16_f32(dtr, o.la[x], ar[x]);          // dKR += delta Lam^T
-            aw[x] = mm16_f32(ddtr, o.sa[x], aw[x]);         // dW  -= dDelta S^T (sign later)
+            aq[x] = mm16_f32(doa, sa[x], aq[x]);            // dQD += dO S^T
+            ar[x] = mm16_f32(dtr, la[x], ar[x]);            // dKR += delta Lam^T
+            aw[x] = mm16_f32(ddtr, sa[x], aw[x]);           // dW  -= dDelta S^T (sign later)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) aE[x] += o.sa[x][i] * o.la[x][i];
+            for (int i = 0; i < 4; ++i) aE[x] += sa[x][i] * la[x][i];
         }
         if (wave == 0) aMq = mm16_f32(doa, dtr, aMq);       // dMqk += dO delta^T
         if (wave == 1) aA = mm16_f32(ddtr, va, aA);         // dA += dDelta v^T
