@@ -242,7 +242,13 @@ struct alignas(16) LocalShare {
             float part[2][2][CHAIN_WAVES][16][20];     // V-block partials of delta, dDelta
             float tr[CHAIN_WAVES][16][17];             // per-wave tile transposes
         };
-        struct { float dqd[16][K + 1], dkr[16][K + 1], dw[16][K + 1]; };   // after it
+        struct {                                       // after it
+            float dqd[16][K + 1], dkr[16][K + 1];
+            union {
+                struct { float dw[16][K + 1], dkd[16][K + 1]; };
+                float red[256 / K][16][K];             // per-key-dim pass: partial sums
+            };
+        };
     };
     float G[16][17], Mq[16][17], X[16][17], A[16][17], P[16][17], T1[16][17];
     float dA[16][17], dMq[16][17], dL[16][17];
@@ -525,11 +531,16 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
         const int k0 = (wave * TPW + x) * 16;
+        f32x4 nw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nw[i] = -aw[x][i];
+        const f32x4 dkd = mm16_f32(At, nw, zero4());          // dKD = A^T dW
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sh.dqd[4 * gq + i][k0 + r] = aq[x][i];
             sh.dkr[4 * gq + i][k0 + r] = ar[x][i];
-            sh.dw[4 * gq + i][k0 + r] = -aw[x][i];
+            sh.dw[4 * gq + i][k0 + r] = nw[i];
+            sh.dkd[4 * gq + i][k0 + r] = dkd[i];
         }
         const float e = sum_lane_groups(aE[x]);
         if (gq == 0) sh.dE[k0 + r] = e;
@@ -585,49 +596,71 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
     }
     __syncthreads();
 
-    // ---- per (token, key dim): dk, dq and dGam; dKD = A^T dW
-    // dGam is written over dQD: entry (t, d) of dQD is read only by the thread that owns (t, d)
-    const bool via_part = p.G > 1 || p.pre.qk_l2norm;
-    float *dq_out = via_part ? b.part_q : b.dq;
-    float *dk_out = via_part ? b.part_k : b.dk;
-    const int qk_heads = via_part ? p.HV : p.H, qk_head = via_part ? j : h;
-    for (int idx = tid; idx < 16 * K; idx += 256) {
-        const int t = idx / K, d = idx % K;
-        float dkd = 0.f;
-        for (int m = 0; m < 16; ++m) dkd += sh.A[m][t] * sh.dw[m][d];
-        const float gt = sh.gm[t][d], et = __expf(gt);
-        const float kt = sh.k[t][d], qt = sh.q[t][d];
-        const float ert = __expf(sh.gm[15][d] - gt);
-        float dk = dkd * et + sh.dkr[t][d] * ert;
-        float dq = sc * sh.dqd[t][d] * et;
-        float dgam = dkd * kt * et + sh.dqd[t][d] * sc * qt * et - sh.dkr[t][d] * kt * ert;
-        for (int m = 0; m < 16; ++m) {
-            const float km = sh.k[m][d], qm = sh.q[m][d], gmm = sh.gm[m][d];
-            if (m < t) {        // t is the row i of G, Mqk: e^{Gam_t - Gam_m}
-                const float e = __expf(gt - gmm);
-                const float wg = sh.T1[t][m] * km * e, wq = sh.dMq[t][m] * sc * km * e;
-                dk += wg;
-                dq += wq;
-                dgam += kt * wg + qt * wq;
-            }
-            if (m > t) {        // t is the column j: e^{Gam_m - Gam_t}
-                const float e = __expf(gmm - gt);
-                const float wg = sh.T1[m][t] * km * e, wq = sh.dMq[m][t] * sc * qm * e;
-                dk += wg + wq;
-                dgam -= kt * (wg + wq);
-            }
-            if (m == t) {       // diagonal of Mqk: q_t k_t, no decay
-                const float wq = sh.dMq[t][t] * sc;
-                dq += wq * kt;
-                dk += wq * qt;
+    // ---- per key dim d: dk, dq and dGam of the 16 tokens, from the chunk-level gradients
+    // (dQD, dKR, dKD) and the pairs (i > j) of G and Mqk, each pair's e^{Gam_i - Gam_j}
+    // evaluated once. The P = 256 / K waves-groups of a key dim share the rows i between them
+    // (a wave-uniform split balanced to 120 / P pairs each) and their partial sums are added
+    // through LDS afterwards; dGam is then written over dQD.
+    {
+        constexpr int P = 256 / K;
+        const int d = tid % K, pp = tid / K;              // pp is uniform within a wave
+        float kk[16], qq[16], gg[16], ak[16], aqv[16], ag[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            kk[t] = sh.k[t][d];
+            qq[t] = sh.q[t][d];
+            gg[t] = sh.gm[t][d];
+            ak[t] = aqv[t] = ag[t] = 0.f;
+        }
+        // rows {15,14,1,0}, {13,12,3,2}, {11,10,5,4}, {9,8,7,6}: 30 pairs each (P = 4);
+        // P = 2 joins the first two and the last two
+        constexpr int own4[16] = {0, 0, 1, 1, 2, 2, 3, 3, 3, 3, 2, 2, 1, 1, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (own4[i] * P / 4 != pp) continue;
+            const float ei = __expf(gg[i]), eri = __expf(gg[15] - gg[i]);
+            const float dkd = sh.dkd[i][d], dkr = sh.dkr[i][d], dqd = sh.dqd[i][d];
+            const float wd = sh.dMq[i][i] * sc;            // diagonal of Mqk: q_i k_i
+            ak[i] += dkd * ei + dkr * eri + wd * qq[i];
+            aqv[i] += sc * dqd * ei + wd * kk[i];
+            ag[i] += (dkd * kk[i] + sc * dqd * qq[i]) * ei - dkr * kk[i] * eri;
+#pragma unroll
+            for (int jx = 0; jx < i; ++jx) {
+                const float e = __expf(gg[i] - gg[jx]);
+                const float w1 = sh.T1[i][jx] * e, w2 = sh.dMq[i][jx] * sc * e;
+                ak[i] += w1 * kk[jx];
+                aqv[i] += w2 * kk[jx];
+                const float c = w1 * kk[i] + w2 * qq[i];
+                ak[jx] += c;
+                const float gx = c * kk[jx];
+                ag[i] += gx;
+                ag[jx] -= gx;
             }
         }
-        if (t < nvalid) {
-            const int64_t tok = bos + t;
-            dq_out[(tok * qk_heads + qk_head) * K + d] = dq;
-            dk_out[(tok * qk_heads + qk_head) * K + d] = dk;
+        const bool via_part = p.G > 1 || p.pre.qk_l2norm;
+        float *dq_out = via_part ? b.part_q : b.dq;
+        float *dk_out = via_part ? b.part_k : b.dk;
+        const int qk_heads = via_part ? p.HV : p.H, qk_head = via_part ? j : h;
+#pragma unroll
+        for (int which = 0; which < 3; ++which) {         // dk, dq, dGam in turn
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                sh.red[pp][t][d] = which == 0 ? ak[t] : which == 1 ? aqv[t] : ag[t];
+            __syncthreads();
+            for (int idx = tid; idx < 16 * K; idx += 256) {
+                const int t = idx / K, dd = idx % K;
+                float v2 = 0.f;
+#pragma unroll
+                for (int q2 = 0; q2 < P; ++q2) v2 += sh.red[q2][t][dd];
+                if (which == 2) {
+                    sh.dqd[t][dd] = v2;
+                } else if (t < nvalid) {
+                    float *out = which == 0 ? dk_out : dq_out;
+                    out[((bos + t) * qk_heads + qk_head) * K + dd] = v2;
+                }
+            }
         }
-        sh.dqd[t][d] = dgam;
     }
     __syncthreads();
     // ---- dgam = dE E + sum_t dKR KR; dg_tau = sum_{t >= tau} dGam_t + dgam; through the
