@@ -176,7 +176,7 @@ kda_status check_bwd(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots, 
     int ct;
     const kda_status st = check_shapes(&c, T_total, n_slots, &rec, &ct);
     if (st != KDA_OK) return st;
-    rec = (size_t)*n_slots * (size_t)a->HV * record_bytes<WsF32>(a->K, a->V);  // fp32 records
+    rec = (size_t)*n_slots * (size_t)a->HV * record_bytes<WsF32B>(a->K, a->V);  // fp32 records
     const size_t slots = (size_t)*n_slots * (size_t)a->HV;
     const size_t state = slots * (size_t)a->K * (size_t)a->V * 4;
     const bool qk_part = a->HV > a->H || a->qk_l2norm;

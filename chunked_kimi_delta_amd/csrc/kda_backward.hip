@@ -124,7 +124,9 @@ __device__ __forceinline__ void chain_run(const BwdParams &b, int unit, int n0, 
     auto at = [&](int x, int i) {
         return (size_t)((wave * TPW + x) * 16 + 4 * g + i) * V + n0 + r;
     };
-    auto rec = [&](int c) { return (const float *)(p.ws + (slot0 + c) * (size_t)WS::BYTES); };
+    auto rec = [&](int c) {
+        return (const float *)(p.ws + (slot0 + c) * (size_t)WsF32B<K, V>::BYTES);
+    };
 
     f32x4 X[TPW];                     // S (states) or Lam (grads), C-layout tiles
     const float *init = GRAD ? b.dht : p.h0;
@@ -235,9 +237,8 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams 
 template <int K, int V>
 struct alignas(16) LocalShare {
     float q[16][K + 1], k[16][K + 1], gm[16][K + 1];   // q, k, Gam (cumsum of g)
-    float kr[16][K + 1];                               // KR
-    union alignas(16) {                                // three phases, one region
-        float w[16][K + 1];                            // W = A KD (until its registers are set)
+    float kd[16][K + 1];                               // KD = k e^Gam
+    union alignas(16) {                                // two phases, one region
         struct {                                       // the V loop
             float part[2][2][CHAIN_WAVES][16][20];     // V-block partials of delta, dDelta
             float tr[CHAIN_WAVES][16][17];             // per-wave tile transposes
@@ -358,49 +359,18 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         for (int r = 0; r < 16; ++r) { acc += sh.gm[r][d]; sh.gm[r][d] = acc; }
         sh.E[d] = __expf(acc);
     }
-    __syncthreads();
-
-    // ---- G (strict lower), Mqk (lower with diagonal), L = diag(beta) G, P = L, INV = I - L
+    // ---- the chunk's inverse X, Gram G and Mqk from its record (the prepare kernel's)
+    using WSB = WsF32B<K, V>;
+    const float *rec = (const float *)(p.ws + gslot * (size_t)WSB::BYTES);
     const int i16 = tid >> 4, j16 = tid & 15;
-    {
-        float Gv = 0.f, Mv = 0.f;
-        if (i16 >= j16) {
-            for (int d = 0; d < K; ++d) {
-                const float e = __expf(sh.gm[i16][d] - sh.gm[j16][d]);
-                Gv += sh.k[i16][d] * sh.k[j16][d] * e;
-                Mv += sh.q[i16][d] * sh.k[j16][d] * e;
-            }
-        }
-        sh.G[i16][j16] = i16 > j16 ? Gv : 0.f;
-        sh.Mq[i16][j16] = i16 >= j16 ? sc * Mv : 0.f;
-        const float Lv = i16 > j16 ? sh.beta[i16] * Gv : 0.f;
-        sh.P[i16][j16] = Lv;
-        sh.X[i16][j16] = (i16 == j16 ? 1.f : 0.f) - Lv;
-    }
+    sh.X[i16][j16] = rec[WSB::XM / 4 + tid];
+    sh.G[i16][j16] = rec[WSB::GM / 4 + tid];
+    sh.Mq[i16][j16] = rec[WSB::MQK / 4 + tid];
     __syncthreads();
-    for (int it = 0; it < 3; ++it) {     // Neumann doubling: P <- P^2, X <- X + X P
-        float acc = 0.f;
-        for (int m = 0; m < 16; ++m) acc += sh.P[i16][m] * sh.P[m][j16];
-        __syncthreads();
-        sh.P[i16][j16] = acc;
-        __syncthreads();
-        float add = 0.f;
-        for (int m = 0; m < 16; ++m) add += sh.X[i16][m] * sh.P[m][j16];
-        sh.T1[i16][j16] = sh.X[i16][j16] + add;
-        __syncthreads();
-        sh.X[i16][j16] = sh.T1[i16][j16];
-        __syncthreads();
-    }
     sh.A[i16][j16] = sh.X[i16][j16] * sh.beta[j16];
-    __syncthreads();
-
-    // ---- W = A KD and KR
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int t = idx / K, d = idx % K;
-        float acc = 0.f;
-        for (int m = 0; m < 16; ++m) acc += sh.A[t][m] * sh.k[m][d] * __expf(sh.gm[m][d]);
-        sh.w[t][d] = acc;
-        sh.kr[t][d] = sh.k[t][d] * __expf(sh.gm[15][d] - sh.gm[t][d]);
+        sh.kd[t][d] = sh.k[t][d] * __expf(sh.gm[t][d]);
     }
     __syncthreads();
 
@@ -410,11 +380,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
         const int k0 = (wave * TPW + x) * 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Wa[x][i] = sh.w[r][k0 + 4 * gq + i];
-            KRa[x][i] = sh.kr[r][k0 + 4 * gq + i];
-        }
+        Wa[x] = *(const f32x4 *)(rec + WSB::W / 4 + r * K + k0 + 4 * gq);
+        KRa[x] = *(const f32x4 *)(rec + WSB::KR / 4 + r * K + k0 + 4 * gq);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -422,7 +389,6 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         At[i] = sh.A[4 * gq + i][r];
         Mqt[i] = sh.Mq[4 * gq + i][r];
     }
-    __syncthreads();                                  // w's region is the V loop's from here
     const float *cS = b.ck_S + gslot * (size_t)K * V + wave * TPW * 256 + lane * 4;
     const float *cL = b.ck_L + gslot * (size_t)K * V + wave * TPW * 256 + lane * 4;
     const int rc = r < nvalid ? r : nvalid - 1;               // clamped rows: loads stay inside
@@ -556,7 +522,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
     {
         const int r = i16, c = j16;
         float acc = 0.f;
-        for (int d = 0; d < K; ++d) acc += sh.dw[r][d] * sh.k[c][d] * __expf(sh.gm[c][d]);
+        for (int d = 0; d < K; ++d) acc += sh.dw[r][d] * sh.kd[c][d];
         sh.dA[r][c] += acc;
     }
     __syncthreads();
@@ -668,7 +634,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
     float gA = 0.f;
     for (int d = tid; d < K; d += 256) {
         float dgam = sh.dE[d] * sh.E[d];
-        for (int t = 0; t < 16; ++t) dgam += sh.dkr[t][d] * sh.kr[t][d];
+        for (int t = 0; t < 16; ++t) dgam += sh.dkr[t][d] * rec[WSB::KR / 4 + t * K + d];
         float acc = dgam, adt = 0.f;
         for (int t = 15; t >= 0; --t) {
             acc += sh.dqd[t][d];
@@ -800,7 +766,8 @@ hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st)
 {
     const FwdParams &p = b.f;
     hipError_t e;
-    if (p.seq.T_total > 0 && (e = launch_prepare_f32<K, V>(p, st, in_bf16)) != hipSuccess)
+    if (p.seq.T_total > 0 &&
+        (e = launch_prepare_f32<K, V>(p, st, in_bf16, true)) != hipSuccess)
         return e;
     const int64_t units = (int64_t)p.seq.N * p.HV;
     if (units == 0) return hipSuccess;

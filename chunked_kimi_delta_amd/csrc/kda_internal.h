@@ -152,6 +152,16 @@ struct WsF32 {
     static constexpr int BYTES = (END + 255) / 256 * 256;
 };
 
+// The backward's fp32 chunk record: WsF32 followed by the inverse X = (I + L)^{-1} and the
+// strictly lower Gram G (L = diag(beta) G), both [16][16] fp32 row-major.
+template <int K, int V>
+struct WsF32B : WsF32<K, V> {
+    static constexpr int XM = WsF32<K, V>::END;
+    static constexpr int GM = XM + 1024;
+    static constexpr int END = GM + 1024;
+    static constexpr int BYTES = (END + 255) / 256 * 256;
+};
+
 // ----------------------------------------------------------------------------- sequences
 
 __device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
@@ -399,9 +409,10 @@ __device__ __forceinline__ void vm_drain() {
 namespace kda {
 template <int K, int V> hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state_bf16(const FwdParams &p, hipStream_t st);
-// fp32 chunk records (WsF32) from fp32 or (in_bf16) bf16 inputs
+// fp32 chunk records from fp32 or (in_bf16) bf16 inputs: WsF32, or WsF32B for the backward
 template <int K, int V>
-hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16 = false);
+hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16 = false,
+                              bool for_backward = false);
 template <int K, int V> hipError_t launch_state_f32(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st);

@@ -274,10 +274,11 @@ __device__ __forceinline__ float ld_in(const uint16_t *p, int64_t i) {
     return bf16_bits_to_f32(p[i]);
 }
 
-template <int K, int V, typename T>
+template <int K, int V, typename T, bool BWD>
 __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
 {
     using WS = WsF32<K, V>;
+    constexpr int STRIDE = BWD ? WsF32B<K, V>::BYTES : WS::BYTES;
     __shared__ float sq[16][K + 1], sk[16][K + 1], sG[16][K + 1], sv[16][V + 1];
     __shared__ float sb[16], sL[16][17], sI[16][17], sP[16][17], sT[16][17];
     const int tid = threadIdx.x;
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     sP[i][jj] = sI[i][jj] * sb[jj];   // A = INV diag(beta)
     __syncthreads();
 
-    float *ws = (float *)(p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)WS::BYTES);
+    float *ws = (float *)(p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)STRIDE);
     for (int idx = tid; idx < 16 * K; idx += 256) {
         const int t = idx / K, d = idx % K;
         float acc = 0.f;
@@ -385,6 +386,10 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     }
     ws[WS::MQK / 4 + i * 16 + jj] = Mv;
     for (int d = tid; d < K; d += 256) ws[WS::EG / 4 + d] = __expf(sG[15][d]);
+    if (BWD) {                        // the inverse and the Gram, for the local gradients
+        ws[WsF32B<K, V>::XM / 4 + i * 16 + jj] = sI[i][jj];
+        ws[WsF32B<K, V>::GM / 4 + i * 16 + jj] = i > jj ? Lij : 0.f;
+    }
 }
 
 template <int K, int V>
@@ -396,19 +401,24 @@ hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st)
 }
 
 template <int K, int V>
-hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16)
+hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16,
+                              bool for_backward)
 {
     dim3 grid(p.seq.n_slots, p.HV);
-    if (in_bf16)
-        prepare_f32_kernel<K, V, uint16_t><<<grid, dim3(256), 0, st>>>(p);
+    if (in_bf16 && for_backward)
+        prepare_f32_kernel<K, V, uint16_t, true><<<grid, dim3(256), 0, st>>>(p);
+    else if (in_bf16)
+        prepare_f32_kernel<K, V, uint16_t, false><<<grid, dim3(256), 0, st>>>(p);
+    else if (for_backward)
+        prepare_f32_kernel<K, V, float, true><<<grid, dim3(256), 0, st>>>(p);
     else
-        prepare_f32_kernel<K, V, float><<<grid, dim3(256), 0, st>>>(p);
+        prepare_f32_kernel<K, V, float, false><<<grid, dim3(256), 0, st>>>(p);
     return hipGetLastError();
 }
 
 #define KDA_INST(K, V)                                                               \
     template hipError_t launch_prepare_bf16<K, V>(const FwdParams &, hipStream_t);  \
-    template hipError_t launch_prepare_f32<K, V>(const FwdParams &, hipStream_t, bool);
+    template hipError_t launch_prepare_f32<K, V>(const FwdParams &, hipStream_t, bool, bool);
 KDA_INST(64, 64)
 KDA_INST(64, 128)
 KDA_INST(128, 64)
