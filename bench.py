@@ -151,6 +151,19 @@ def backward_work(inp):
     return rd + wr
 
 
+def backward_flops(inp):
+    """Algorithmic FLOPs of one backward (multiply-add = 2) with 16-token chunks, per chunk of
+    one value head (C = 16): the states chain (w S, kr^T delta: 2 C K V), the gradient chain
+    (kr Lam, qd^T dO, w^T dDelta: 3 C K V, Mqk^T dO: C^2 V), the local products (w S, kr Lam,
+    dO S^T, delta Lam^T, dDelta S^T: 5 C K V; A v, Mqk^T dO, dO delta^T, dDelta v^T, A^T dDelta:
+    5 C^2 V) and the record (Gram, Mqk, w, u: C^2 (3 K + V) + C^2 V, the Neumann product)."""
+    w = inp.w
+    C, K, V = 16, w.K, w.V
+    n = sum((b - a + C - 1) // C for a, b in inp.seq_bounds()) * w.HV
+    mac = 10 * C * K * V + 6 * C * C * V + C * C * (3 * K + V) + 6 * 16 ** 3 + C * C * V
+    return 2 * mac * n
+
+
 def cpu_baseline_bwd(inp, gr, min_seconds: float):
     """The fp64 oracle backward (numpy reverse recurrence, unchanged) on one (sequence, value
     head) slice of up to 512 tokens, repeated for at least `min_seconds`; scaled to the
@@ -196,6 +209,8 @@ def run_backward(a, torch, W, kda):
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
     nb = backward_work(inp)
     gbs = nb / (ms * 1e-3) / 1e9
+    nf = backward_flops(inp)
+    tfs = nf / (ms * 1e-3) / 1e12
     cpu = cpu_baseline_bwd(inp, gr, a.cpu_seconds) if a.cpu_seconds > 0 else None
     out = {
         "metric": METRIC_BWD, "value": round(inp.T_total / (ms * 1e-3), 1), "unit": "tokens/s",
@@ -205,6 +220,10 @@ def run_backward(a, torch, W, kda):
         "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
                    "K": w.K, "V": w.V, "chunk": 16, "io": w.dtype,
                    "tokens_per_step": inp.T_total, "parallelism": "single-gpu"},
+        "roofline": {"kernel": "kda_bwd (all launches of one call)", "bound": "mfma",
+                     "achieved": round(tfs, 2), "peak": MFMA_PEAK_TFLOPS["fp32"],
+                     "unit": "TFLOP/s", "frac": round(tfs / MFMA_PEAK_TFLOPS["fp32"], 5),
+                     "traffic": None, "alg_flops_per_step": nf},
         "roofline_path": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
                           "alg_bytes_per_step": nb},

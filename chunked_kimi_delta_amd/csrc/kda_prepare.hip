@@ -370,13 +370,19 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     __syncthreads();
 
     float *ws = (float *)(p.ws + ((size_t)j * p.seq.n_slots + slot) * (size_t)STRIDE);
-    for (int idx = tid; idx < 16 * K; idx += 256) {
+    for (int idx = tid; idx < 16 * K; idx += 256) {   // qd, kr; KD = k e^Gam over q's slot
+        const int t = idx / K, d = idx % K;
+        const float e = __expf(sG[t][d]);
+        ws[WS::QD / 4 + t * K + d] = p.scale * sq[t][d] * e;
+        ws[WS::KR / 4 + t * K + d] = sk[t][d] * __expf(sG[15][d] - sG[t][d]);
+        sq[t][d] = sk[t][d] * e;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 16 * K; idx += 256) {   // w = A KD
         const int t = idx / K, d = idx % K;
         float acc = 0.f;
-        for (int m = 0; m < 16; ++m) acc += sP[t][m] * sk[m][d] * __expf(sG[m][d]);
+        for (int m = 0; m < 16; ++m) acc += sP[t][m] * sq[m][d];
         ws[WS::W / 4 + t * K + d] = acc;
-        ws[WS::QD / 4 + t * K + d] = p.scale * sq[t][d] * __expf(sG[t][d]);
-        ws[WS::KR / 4 + t * K + d] = sk[t][d] * __expf(sG[15][d] - sG[t][d]);
     }
     for (int idx = tid; idx < 16 * V; idx += 256) {
         const int t = idx / V, d = idx % V;
