@@ -233,6 +233,34 @@ def run_backward(a, torch, W, kda):
     print(json.dumps(out), flush=True)
 
 
+def summarize_mfma(d: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE
+    and the SQ_INSTS_VALU_MFMA_MOPS_* counters: per kernel, the matrix-core busy share and the
+    MFMA FLOPs issued (MOPS x 512, the counters' own unit). The busy share is the busy cycles
+    summed over all 1,024 SIMDs divided by 1,024 times the kernel's active cycles; the collected
+    GRBM_GUI_ACTIVE is the sum of the eight XCDs' counters, so the active cycles are that / 8
+    (with it, the share matches the issued FLOPs over the kernel time at the dense peak)."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        e = per.setdefault(r["Kernel_Name"], {})
+        e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = ["# rocprofv3 matrix-core counters", "", "Command:", "", "```", command, "```", "",
+           "| kernel | dispatches | MFMA busy | MFMA GFLOP / dispatch (f16, bf16, f32) |",
+           "|---|---|---|---|"]
+    for k, e in per.items():
+        if "kda::" not in k:
+            continue
+        m = lambda c: statistics.mean(e[c]) if c in e else 0.0
+        busy = m("SQ_VALU_MFMA_BUSY_CYCLES") / (m("GRBM_GUI_ACTIVE") / 8 * 1024) * 100
+        fl = [m(f"SQ_INSTS_VALU_MFMA_MOPS_{t}") * 512 / 1e9 for t in ("F16", "BF16", "F32")]
+        out.append(f"| `{k}` | {len(e.get('GRBM_GUI_ACTIVE', []))} | {busy:.1f}% | "
+                   + ", ".join(f"{x:.3f}" for x in fl) + " |")
+    out += ["", f"kernel sources digest: `{source_digest()}`", ""]
+    return "\n".join(out)
+
+
 def cpu_baseline(inp, min_seconds: float):
     """The fp64 C oracle (unchanged) on the host cores: the whole workload, repeated until at
     least `min_seconds` of wall time have passed (bounded at 1000 repetitions)."""
@@ -282,12 +310,17 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<kernel>_<workload>.txt from two --pmc runs")
     ap.add_argument("--command", default="", help="the profiling command, for the summaries")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --pmc matrix-core run and exit")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (kda_bwd) instead of the forward")
     a = ap.parse_args()
 
     if a.summarize_trace:
         print(summarize_trace(a.summarize_trace, a.command))
+        return
+    if a.summarize_mfma:
+        print(summarize_mfma(a.summarize_mfma, a.command))
         return
     if a.summarize_traffic:
         res = summarize_traffic(a.summarize_traffic[0], a.summarize_traffic[1], a.workload,

@@ -110,7 +110,6 @@ __device__ __forceinline__ void chain_run(const BwdParams &b, int unit, int n0, 
                                           int lane)
 {
     const FwdParams &p = b.f;
-    using WS = WsF32<K, V>;
     constexpr int TPW = ChainOps<K>::TPW;
     __shared__ f32x4 part[2][CHAIN_WAVES][64];
     const int r = lane & 15, g = lane >> 4;

@@ -46,18 +46,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *o, int64_t row
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, num, 0x00020000);
 }
 
-__device__ __forceinline__ void release_lds() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-}
-__device__ __forceinline__ void acquire_lds() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-__device__ __forceinline__ void lds_barrier() {
-    release_lds();
-    __builtin_amdgcn_s_barrier();
-    acquire_lds();
-}
-
 // Operands of one chunk for the chain wave that owns key rows [K/2 h, K/2 (h + 1)).
 template <int K, int V>
 struct HalfFrag {
