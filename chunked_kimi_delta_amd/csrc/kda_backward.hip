@@ -29,6 +29,8 @@ namespace kda {
 
 namespace {
 
+typedef float f32v2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float ldx(const float *p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ldx(const uint16_t *p, int64_t i) {
     return bf16_bits_to_f32(p[i]);
@@ -54,6 +56,7 @@ __device__ __forceinline__ float ldx(const uint16_t *p, int64_t i) {
 // transposes four 4-byte loads. Records of the next chunk are loaded before the current
 // chunk's products.
 constexpr int CHAIN_WAVES = 4;
+constexpr int CK_AUX = 2;          // cache policy of the state-record stores
 
 template <int K>
 struct ChainOps {
@@ -136,14 +139,16 @@ __device__ __forceinline__ void chain_run(const BwdParams &b, int unit, int n0, 
     // one chunk with the operands in `o` (loaded one chunk earlier)
     auto step = [&](const ChainOps<K> &o, int it) {
         const int c = GRAD ? nc - 1 - it : it;
-        // the record of this chunk, tile order: [V/16 slice][K/16 tile][64 lanes][4]; two
-        // 8-byte stores per tile (see bstore16 for why stores stay at 8 bytes)
-        float *cko = (GRAD ? b.ck_L : b.ck_S) + (slot0 + c) * (size_t)K * V +
-                     ((size_t)(n0 / 16) * (K / 16) + wave * TPW) * 256 + lane * 4;
+        // the record of this chunk, tile order: [V/16 slice][K/16 tile][64 lanes][4], as two
+        // 8-byte buffer stores per tile (bstore8: plain 8-byte stores to adjacent addresses are
+        // merged into one 16-byte store by the compiler, see bstore16 for why that matters)
+        const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(
+            (GRAD ? b.ck_L : b.ck_S) + (slot0 + c) * (size_t)K * V, K * V * 4);
+        const int cbase = (((n0 / 16) * (K / 16) + wave * TPW) * 256 + lane * 4) * 4;
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
-            *(float2 *)(cko + x * 256) = float2{X[x][0], X[x][1]};
-            *(float2 *)(cko + x * 256 + 2) = float2{X[x][2], X[x][3]};
+            bstore8<CK_AUX>(cr, cbase + x * 1024, 0, f32v2{X[x][0], X[x][1]});
+            bstore8<CK_AUX>(cr, cbase + x * 1024 + 8, 0, f32v2{X[x][2], X[x][3]});
         }
         f32x4 ox = o.x;
         if (GRAD) {                   // dO rows past the sequence end are zero
@@ -398,8 +403,10 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
         const int n0 = nb * 16;
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
-            o.sc[x] = *(const f32x4 *)(cS + ((size_t)nb * (K / 16) + x) * 256);
-            o.lc[x] = *(const f32x4 *)(cL + ((size_t)nb * (K / 16) + x) * 256);
+            // read once: non-temporal, so they do not evict the chunk records from L2
+            const size_t to = ((size_t)nb * (K / 16) + x) * 256;
+            o.sc[x] = __builtin_nontemporal_load((const f32x4 *)(cS + to));
+            o.lc[x] = __builtin_nontemporal_load((const f32x4 *)(cL + to));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
