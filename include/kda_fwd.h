@@ -16,7 +16,8 @@
  * inverse of (I + L) by the Neumann doubling product of "KDA源码剖析之FlashKDA（上）" part 12,
  * and w = A (exp(G) k), u = A v) followed by a chunk-sequential state kernel; or token by token
  * (chunk 1, for decoding). Optionally the kernels first apply the pre-stage that turns raw
- * projections into q, k, g, beta (q/k L2 norm, beta sigmoid, a gate activation).
+ * projections into q, k, g, beta (q/k L2 norm, beta sigmoid, a gate activation). kda_bwd
+ * computes the gradients of all inputs of that forward (declared at the end of this file).
  *
  * Conventions
  *  - All tensor pointers are DEVICE pointers, caller-owned, contiguous (row-major), and
