@@ -12,7 +12,8 @@
 // (Lam = d loss / d S) is carried across chunks newest first,
 //     dDelta = Mqk^T dO + KR Lam_next,   Lam = diag(E) Lam_next + QD^T dO - W^T dDelta,
 // and every chunk then back-propagates its own quantities to its tokens independently. Launches:
-//   prepare_f32 (kda_prepare.hip)  the chunk records (W, QD, KR, U, Mqk, E) in fp32
+//   prepare_f32 (kda_prepare.hip)  the chunk records in fp32: W, QD, KR, U, Mqk, E and, for the
+//                                  local gradients, the inverse X and the Gram G (WsF32B)
 //   bwd_chains_kernel              S at the start and Lam at the end of every chunk, and dh0
 //   bwd_local_kernel               per (chunk, value head): dv, dg, dbeta and dq, dk
 //   bwd_qk_finalize_kernel         dq, dk summed over the value heads of a q/k head (G > 1)
@@ -50,13 +51,14 @@ __device__ __forceinline__ float ldx(const uint16_t *p, int64_t i) {
 //   states:  delta = u - w S;  S <- diag(E) S + kr^T delta
 //   grads:   dDelta = Mqk^T dO + kr Lam;  Lam <- diag(E) Lam + qd^T dO - w^T dDelta
 // S and Lam are recorded per chunk in tile order ([V/16 slice][K/16 tile][64 lanes][4 fp32],
-// the C-layout registers as they are), one 1 KB contiguous block per tile and wave.
+// the C-layout registers as they are), one 1 KB contiguous block per tile and wave, with
+// non-temporal stores.
 // The chunk records are read as they are laid out ([16][K] row-major w, qd, kr; [16][V] u;
 // [16][16] Mqk; [K] E): A-operand rows of w and kr are contiguous 16-byte loads, their
 // transposes four 4-byte loads. Records of the next chunk are loaded before the current
 // chunk's products.
 constexpr int CHAIN_WAVES = 4;
-constexpr int CK_AUX = 2;          // cache policy of the state-record stores
+constexpr int CK_AUX = 2;          // state-record stores: the non-temporal (nt) cache policy
 
 template <int K>
 struct ChainOps {
@@ -224,20 +226,22 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams 
         chain_run<K, V, T, false>(b, unit, n0, wave, lane);
 }
 
-// One block (4 waves) per (chunk slot, value head): recompute the chunk in fp32 and
-// back-propagate O and S_next (through delta, U, W, A, the inverse, L, Mqk and the decay
-// factors) to the chunk's tokens. Products are formed from exponent differences (every factor
-// e^{Gam_i - Gam_j}, i >= j, and e^{gam - Gam} is at most 1).
+// One block (4 waves) per (chunk slot, value head): back-propagate O and S_next (through
+// delta, U, W, A, the inverse, L, Mqk and the decay factors) to the chunk's tokens, reading X, G,
+// Mqk, W and KR from the chunk's record. Products are formed from exponent differences (every
+// factor e^{Gam_i - Gam_j}, i >= j, and e^{gam - Gam} is at most 1).
 // The contractions over V run on the fp32 matrix cores, one 16-column block of V at a time,
 // with the K rows split over the waves as in the chains (wave w owns the row tiles
 // w * K/64 ...): per block
 //     delta = A v - W S,  dDelta = Mqk^T dO + KR Lam           (partials summed through LDS)
 //     dQD += dO S^T,  dKR += delta Lam^T,  dW -= dDelta S^T     (the wave's own K tiles)
 //     dE += rowsum(Lam . S),  dMqk += dO delta^T,  dA += dDelta v^T,  dv = A^T dDelta
-// S and Lam are read as the chains recorded them (C-layout tiles, one 16-byte load per tile and
-// lane) and are needed in two register layouts: C-layout (the B operand of a product over K)
-// and its transpose (the B operand of a product over V), made through a wave-private LDS tile.
-// The rest of the chunk's algebra (16 x 16 and 16 x K) is scalar.
+// S and Lam are read as the chains recorded them (C-layout tiles, one non-temporal 16-byte
+// load per tile and lane) and are needed in two register layouts: C-layout (the B operand of a
+// product over K) and its transpose (the B operand of a product over V), made through a
+// wave-private LDS tile. dKD = A^T dW is one product per tile of the V loop's accumulators;
+// the rest of the chunk's algebra (16 x 16 and 16 x K) is scalar, the pairs of G and Mqk in
+// one pass per key dim.
 template <int K, int V>
 struct alignas(16) LocalShare {
     float q[16][K + 1], k[16][K + 1], gm[16][K + 1];   // q, k, Gam (cumsum of g)
