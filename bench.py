@@ -263,7 +263,8 @@ def summarize_mfma(d: str, command: str) -> str:
 
 def cpu_baseline(inp, min_seconds: float):
     """The fp64 C oracle (unchanged) on the host cores: the whole workload, repeated until at
-    least `min_seconds` of wall time have passed (bounded at 1000 repetitions)."""
+    least `min_seconds` of wall time have passed (bounded at 1000 repetitions); then the same
+    on one thread for a third of that time, to show the scaling."""
     import workloads as W
     from oracle.native import kda_oracle_c
     try:
@@ -275,17 +276,21 @@ def cpu_baseline(inp, min_seconds: float):
     args = [f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta)]
     h0 = None if inp.h0 is None else inp.h0.numpy()
     cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        kda_oracle_c(*args, inp.scale, h0, cu, n_threads=cores, want_o=True)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or reps >= 1000:
-            break
+    def run(threads, seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            kda_oracle_c(*args, inp.scale, h0, cu, n_threads=threads, want_o=True)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                return reps, el
+    reps, el = run(cores, min_seconds)
+    reps1, el1 = run(1, min_seconds / 3)
     return {"value": round(reps * inp.T_total / el, 2), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"full {inp.w.name} forward (all {inp.w.HV} heads, fp64 C recurrence), "
-                      f"repeated {reps}x in {el:.1f} s"}
+                      f"repeated {reps}x in {el:.1f} s",
+            "value_1_thread": round(reps1 * inp.T_total / el1, 2)}
 
 
 def main():
@@ -396,6 +401,10 @@ def main():
     torch.cuda.synchronize()
     prep_ms = statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps))
     state_ms = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps))
+    step_ev = sorted(ev[i][0].elapsed_time(ev[i][2]) for i in range(a.steps))
+    pct = lambda f: round(step_ev[min(len(step_ev) - 1, int(f * len(step_ev)))], 5)
+    step_dist = {"p10_ms": pct(0.1), "p50_ms": pct(0.5), "p90_ms": pct(0.9),
+                 "note": "per-step durations of the event-timed pass (events add a few us)"}
 
     cold = None
     if a.cold_steps > 0:
@@ -477,7 +486,7 @@ def main():
         "roofline": roof, "roofline_path": roof_path, "kernels": kernels,
         "kernel_timing": "avg_ms: a second pass of the same steps, each stage launched alone "
                          "with HIP events around it on its stream",
-        "cold_cache": cold, "cpu_baseline": cpu,
+        "step_distribution": step_dist, "cold_cache": cold, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
