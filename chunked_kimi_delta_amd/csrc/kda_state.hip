@@ -21,7 +21,7 @@
 //   * the chunk's fragments (w, qd, kr, u, Mqk, exp(gam)) are read from the workspace in the
 //     exact lane order stage 1 wrote them, as contiguous vector loads, two chunks ahead;
 //   * the workgroups of one (sequence, value head) share an XCD, hence an L2.
-#include "kda_internal.h"
+#include "kda_chain_f32.h"
 
 namespace kda {
 
@@ -251,73 +251,17 @@ __global__ __launch_bounds__(128) void state_bf16_kernel(FwdParams p)
 }
 
 // =============================================================================== fp32 io
-// Correctness mode: one block per (sequence, value head), one thread per value column, the
-// column of S held in registers, chunk operands staged in LDS.
+// The state pass in fp32 on the fp32 matrix cores (kda_chain_f32.h, forward mode): one
+// workgroup of 4 waves per (sequence, value head, 16-column slice), the K rows split over the
+// waves, o formed by wave 0 from the waves' qd S partials and Mqk delta.
 template <int K, int V>
-__global__ __launch_bounds__(V) void state_f32_kernel(FwdParams p)
+__global__ __launch_bounds__(64 * CHAIN_WAVES) void state_f32_kernel(FwdParams p)
 {
-    using WS = WsF32<K, V>;
-    __shared__ float sw[16][K], sqd[16][K], skr[16][K], smq[16][16], seg[K];
-    const int n = threadIdx.x;
-    const int j = blockIdx.x % p.HV, s = blockIdx.x / p.HV;
-    const int64_t bos = seq_bos(p.seq, s);
-    const int64_t eos = seq_eos(p.seq, s, bos);
-    const int nc = (int)((eos - bos + CHUNK - 1) / CHUNK);
-
-    float S[K];
-    if (p.h0) {
-        const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + n;
-#pragma unroll
-        for (int d = 0; d < K; ++d) S[d] = h0[(size_t)d * V];
-    } else {
-#pragma unroll
-        for (int d = 0; d < K; ++d) S[d] = 0.f;
-    }
-    const float *base = (const float *)(p.ws + ((size_t)j * p.seq.n_slots +
-                                                (size_t)(bos / CHUNK + s)) * (size_t)WS::BYTES);
-    float *o = (float *)p.o;
-    for (int c = 0; c < nc; ++c) {
-        const float *ch = base + (size_t)c * (WS::BYTES / 4);
-        for (int idx = n; idx < 16 * K; idx += V) {
-            sw[idx / K][idx % K] = ch[WS::W / 4 + idx];
-            sqd[idx / K][idx % K] = ch[WS::QD / 4 + idx];
-            skr[idx / K][idx % K] = ch[WS::KR / 4 + idx];
-        }
-        for (int idx = n; idx < 256; idx += V) smq[idx / 16][idx % 16] = ch[WS::MQK / 4 + idx];
-        for (int idx = n; idx < K; idx += V) seg[idx] = ch[WS::EG / 4 + idx];
-        __syncthreads();
-        float d[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float acc = ch[WS::U / 4 + t * V + n];
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) acc -= sw[t][kk] * S[kk];
-            d[t] = acc;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float acc = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) acc += sqd[t][kk] * S[kk];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc += smq[t][m] * d[m];
-            const int64_t tok = bos + 16 * c + t;
-            if (tok < eos) o[(tok * p.HV + j) * V + n] = acc;
-        }
-#pragma unroll
-        for (int kk = 0; kk < K; ++kk) {
-            float acc = seg[kk] * S[kk];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) acc += skr[t][kk] * d[t];
-            S[kk] = acc;
-        }
-        __syncthreads();
-    }
-    if (p.ht) {
-        float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + n;
-#pragma unroll
-        for (int d = 0; d < K; ++d) ht[(size_t)d * V] = S[d];
-    }
+    int unit, slice;
+    if (!state_unit(blockIdx.x, V / 16, p.seq.N * p.HV, &unit, &slice)) return;
+    chain_run<K, V, float, CHAIN_FORWARD>(p, unit, slice * 16, threadIdx.x >> 6,
+                                          threadIdx.x & 63, p.h0, nullptr, p.ht, (float *)p.o,
+                                          WsF32<K, V>::BYTES, (const float *)nullptr);
 }
 
 template <int K, int V>
@@ -333,9 +277,10 @@ hipError_t launch_state_bf16(const FwdParams &p, hipStream_t st)
 template <int K, int V>
 hipError_t launch_state_f32(const FwdParams &p, hipStream_t st)
 {
-    const int64_t nblk = (int64_t)p.seq.N * p.HV;
+    const int64_t units = (int64_t)p.seq.N * p.HV;
+    const int64_t nblk = (units + 7) / 8 * 8 * (V / 16);
     if (nblk == 0) return hipSuccess;
-    state_f32_kernel<K, V><<<dim3((unsigned)nblk), dim3(V), 0, st>>>(p);
+    state_f32_kernel<K, V><<<dim3((unsigned)nblk), dim3(64 * CHAIN_WAVES), 0, st>>>(p);
     return hipGetLastError();
 }
 

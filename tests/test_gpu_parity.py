@@ -258,6 +258,16 @@ def test_full_size_sampled_parity(name, chunk):
     assert eo <= TOL[w.dtype] and ef <= TOL[w.dtype], f"rel L2 o={eo:.3e} final={ef:.3e}"
 
 
+@pytest.mark.parametrize("chunk", [1, 16])
+def test_full_size_fp32_every_unit(chunk):
+    # the fp32 mode at the benchmark's size: every (sequence, head) against the oracle
+    w = W.WORKLOADS["h16_t4096_fp32"]
+    inp = W.make_inputs(w, seed=0)
+    o, fin = gpu_run(inp, chunk=chunk)
+    o_ref, f_ref = oracle_run(inp)
+    check_all(inp, o, fin, o_ref, f_ref, TOL["fp32"])
+
+
 @pytest.mark.parametrize("chunk", [16, 32])
 def test_prepare_records_repeat_bitwise_full_size(chunk):
     # every chunk record of the h16_t4096 workload, written twice into a zeroed workspace, is

@@ -58,6 +58,9 @@ class Workload:
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", B=1, T=64, H=1, HV=1, K=64, V=64, dtype="fp32"),
     "h16_t4096": Workload("h16_t4096", B=1, T=4096, H=16, HV=16, K=128, V=128, dtype="bf16"),
+    # the same in fp32 io (the fp32 mode at the benchmark's size)
+    "h16_t4096_fp32": Workload("h16_t4096_fp32", B=1, T=4096, H=16, HV=16, K=128, V=128,
+                               dtype="fp32"),
     "varlen8_h32": Workload("varlen8_h32", B=1, T=0, H=32, HV=32, K=128, V=128, dtype="bf16",
                             h0_std=0.1, n_seqs=8, len_lo=256, len_hi=8192),
     "gva_b4_t8192": Workload("gva_b4_t8192", B=4, T=8192, H=16, HV=32, K=128, V=128,
