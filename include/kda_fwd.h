@@ -43,8 +43,10 @@ typedef enum {
                                  cu_seqlens, N != B without cu_seqlens, HV % H != 0, a gate
                                  without A_log, a bounded gate's lower bound not < 0         */
     KDA_ERR_UNSUPPORTED = 2,  /* K or V outside {64, 128}, unknown io dtype, chunk not
-                                 offered for this io dtype, unknown gate                     */
-    KDA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than kda_fwd_workspace_bytes()    */
+                                 offered for this io dtype (the backward: other than 0, 16),
+                                 unknown gate                                                */
+    KDA_ERR_WORKSPACE = 3,    /* workspace NULL, misaligned, or smaller than
+                                 kda_fwd_workspace_bytes() / kda_bwd_workspace_bytes()       */
     KDA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)                    */
 } kda_status;
 
