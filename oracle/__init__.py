@@ -22,6 +22,9 @@ Contents
                   token recurrence, derived by hand, plus torch.autograd on the fp64 forward
                   as an independent check; with the pre-stage's reverse mode (prestage.py),
                   the gradients with respect to raw inputs, A_log and dt_bias.
+  backward_chunked.py  the same gradients by the chunked reverse sweep (chunk records, the
+                  state and state-gradient chains, per-chunk local gradients): the algebra
+                  the GPU backward follows, pinned against backward.py.
   native.py       ctypes loader for the C oracle.
   build.py        compiles kda_oracle.c with gcc.
 

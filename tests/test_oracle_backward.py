@@ -125,3 +125,32 @@ def mutant(name):
 def test_planted_backward_mistakes_are_caught(name):
     with pytest.raises(AssertionError):
         pin_finite_differences(mutant(name), rand_case(**CASES["dense_gva"]))
+
+
+# --------------------------------------------------------------------------- the chunked form
+
+from oracle.backward_chunked import kda_backward_chunked  # noqa: E402
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=1, T=40, H=1, HV=1, K=6, V=5),                      # ragged last chunk
+    dict(B=2, T=16, H=1, HV=2, K=4, V=3),                      # one exact chunk, G = 2
+    dict(H=2, HV=2, K=3, V=2, cu=np.array([0, 5, 5, 37])),     # varlen with an empty sequence
+    dict(B=1, T=33, H=1, HV=1, K=5, V=4, h0=False),
+], ids=["ragged", "gva", "varlen", "no_h0"])
+def test_chunked_backward_equals_the_recurrence(kw):
+    # the chunk-level reverse sweep (records, two chains, per-chunk local gradients) that the
+    # GPU kernels follow gives the token recurrence's gradients
+    case = rand_case(**kw)
+    a = BW.kda_backward_recurrent(*case)
+    b = kda_backward_chunked(*case)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), a, b):
+        assert np.allclose(x, y, rtol=1e-10, atol=1e-12), name
+
+
+def test_chunked_backward_without_dht():
+    q, k, v, g, beta, scale, S0, cu, do, dht = rand_case(B=1, T=21, H=1, HV=1, K=4, V=3)
+    a = BW.kda_backward_recurrent(q, k, v, g, beta, scale, S0, cu, do, None)
+    b = kda_backward_chunked(q, k, v, g, beta, scale, S0, cu, do, None)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=1e-10, atol=1e-12)
