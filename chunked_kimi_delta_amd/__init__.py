@@ -6,7 +6,8 @@ pointers and the current HIP stream into that ABI and nothing else. There is no 
 the shared library is missing or cannot be loaded, every entry point raises.
 """
 from .api import KdaBwdPlan, KdaFwdPlan, kda_bwd, kda_fwd, workspace_bytes  # noqa: F401
+from .autograd import ChunkKDAFunction, chunk_kda  # noqa: F401
 from ._lib import KDA_BF16, KDA_FP32, library_path, load  # noqa: F401
 
-__all__ = ["kda_fwd", "KdaFwdPlan", "kda_bwd", "KdaBwdPlan", "workspace_bytes", "load",
-           "library_path", "KDA_BF16", "KDA_FP32"]
+__all__ = ["kda_fwd", "KdaFwdPlan", "kda_bwd", "KdaBwdPlan", "chunk_kda", "ChunkKDAFunction",
+           "workspace_bytes", "load", "library_path", "KDA_BF16", "KDA_FP32"]

@@ -256,3 +256,39 @@ def test_backward_prestage_full_size_bounded_gate():
     got = gpu_bwd_raw(raw, gr, pre)
     print("[bwd pre full] oracle", file=sys.stderr, flush=True)
     check_raw(got, oracle_bwd_raw(raw, gr, pre), pre)
+
+
+# --------------------------------------------------------------------------- torch.autograd
+
+@pytest.mark.parametrize("pre", [{}, {"l2": True, "sig": True, "gate": "bounded", "lb": -4.0}],
+                         ids=["plain", "prestage"])
+def test_chunk_kda_autograd_matches_oracle(pre):
+    # loss = sum(o * d_o) + sum(final * dht) through chunk_kda: torch.autograd drives kda_fwd
+    # and kda_bwd; the gradients (cast to the inputs' dtypes) against the fp64 oracle
+    from oracle.backward import kda_backward_raw
+    w = W.custom(B=1, T=50, H=2, HV=4, K=64, V=64, dtype="fp32", h0_std=0.3)
+    raw = W.make_raw_inputs(w, seed=11) if pre else None
+    inp = raw.inp if pre else W.make_inputs(w, seed=11)
+    gr = W.make_grads(inp, seed=11)
+    leaf = lambda x: None if x is None else dev(x).requires_grad_(True)
+    q, k, v, g, beta, h0 = map(leaf, (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0))
+    A_log = leaf(raw.A_log) if pre else None
+    dt_bias = leaf(raw.dt_bias) if pre else None
+    o, fin = kda.chunk_kda(q, k, v, g, beta, scale=inp.scale, initial_state=h0,
+                           use_qk_l2norm=pre.get("l2", False),
+                           use_beta_sigmoid=pre.get("sig", False), gate=pre.get("gate"),
+                           A_log=A_log, dt_bias=dt_bias,
+                           gate_lower_bound=pre.get("lb", -5.0))
+    loss = (o * dev(gr.d_o)).sum() + (fin * dev(gr.dht)).sum()
+    leaves = [q, k, v, g, beta, h0] + ([A_log, dt_bias] if pre else [])
+    got = torch.autograd.grad(loss, leaves)
+    f = W.as_f32_numpy
+    ref = kda_backward_raw(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.scale,
+                           inp.h0.numpy(), None, f(gr.d_o), gr.dht.numpy(),
+                           pre.get("l2", False), pre.get("sig", False), pre.get("gate"),
+                           raw.A_log.numpy() if pre else None,
+                           raw.dt_bias.numpy() if pre else None, pre.get("lb", -5.0))
+    for name, a, b in zip(PNAMES, got, ref):
+        assert a.dtype == torch.float32, name
+        e = rel_l2(a.detach().cpu().numpy(), np.asarray(b).reshape(a.shape))
+        assert e <= TOL, (name, e)
