@@ -84,6 +84,8 @@ SMALL = {
     "bf16_strong_decay": W.custom(B=1, T=200, H=2, HV=2, K=128, V=128, g_lo=0.5, g_hi=0.9999,
                                   beta_std=2.0),
     "bf16_t1": W.custom(B=3, T=1, H=1, HV=1, K=128, V=128, h0_std=0.1),
+    "bf16_g4_varlen": W.custom(H=1, HV=4, K=128, V=64, h0_std=0.2, lengths=(3, 0, 40, 17)),
+    "fp32_k64v128_b3_t31": W.custom(B=3, T=31, H=2, HV=2, K=64, V=128, dtype="fp32"),
 }
 
 
@@ -176,6 +178,8 @@ PRE_SHAPES = {
                                   lengths=(0, 1, 17, 33, 64)),
     "bf16_k64v64_t50": W.custom(B=1, T=50, H=2, HV=2, K=64, V=64),
     "fp32_k128v64_t70": W.custom(B=1, T=70, H=1, HV=2, K=128, V=64, dtype="fp32"),
+    "bf16_k64v128_g4_varlen": W.custom(H=1, HV=4, K=64, V=128, h0_std=0.1,
+                                       lengths=(20, 0, 49)),
 }
 PNAMES = NAMES + ("dA_log", "ddt_bias")
 
