@@ -59,21 +59,25 @@ struct Prep32Share {
 template <int K, int V>
 struct Prep32In {
     u32x4 q[K / 32], k[K / 32], g[K / 32], v[V / 32];
-    float beta;
+    unsigned beta;               // bf16 bits of beta of row lane % 16 (0 past the valid rows)
     int nrows;                   // valid rows of the block (the rest are zero padding)
 };
 
+// The loads go through a buffer resource whose range ends with the block's last valid row:
+// rows past it read as zero (the hardware's range check), so no load sits under a branch. A
+// branch around a load had made the compiler wait for it right there (a register copy of the
+// loaded value inside the branch), which serialised the whole load phase.
 template <int RL>
 __device__ __forceinline__ void load_rows(const uint16_t *base, int64_t row_elems, int nrows,
                                           int lane, u32x4 (&x)[RL / 32])
 {
     constexpr int CPR = RL / 8, RPI = 64 / CPR;     // 16-byte chunks per row, rows per load
+    const uint32_t row_bytes = (uint32_t)row_elems * 2u;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(base, nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + 2u * RL : 0u);
 #pragma unroll
-    for (int u = 0; u < RL / 32; ++u) {
-        const int row = RPI * u + lane / CPR, chunk = lane % CPR;
-        x[u] = row < nrows ? *(const u32x4 *)(base + row * row_elems + 8 * chunk)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < RL / 32; ++u)
+        x[u] = bload16(rs, (int)((RPI * u + lane / CPR) * row_bytes) + 16 * (lane % CPR), 0);
 }
 
 template <int K, int V>
@@ -81,8 +85,11 @@ __device__ __forceinline__ void prep32_load(const FwdParams &p, int64_t bos, int
                                             int wave, int lane, Prep32In<K, V> &in)
 {
     const int r = lane & 15;
-    const int64_t tok0 = bos + 16 * wave;
-    const int nrows = nvalid - 16 * wave;           // valid rows of this block (may be <= 0)
+    // the block index is the same in every lane: read it as a scalar so that the buffer
+    // resources below are scalar too (a per-lane one needs a loop around every load)
+    const int blk = __builtin_amdgcn_readfirstlane(wave);
+    const int64_t tok0 = bos + 16 * blk;
+    const int nrows = nvalid - 16 * blk;            // valid rows of this block (may be <= 0)
     const int h = j / p.G;
     load_rows<K>((const uint16_t *)p.g + (tok0 * p.HV + j) * K, (int64_t)p.HV * K, nrows, lane,
                  in.g);
@@ -92,9 +99,10 @@ __device__ __forceinline__ void prep32_load(const FwdParams &p, int64_t bos, int
                  in.q);
     load_rows<V>((const uint16_t *)p.v + (tok0 * p.HV + j) * V, (int64_t)p.HV * V, nrows, lane,
                  in.v);
-    in.beta = r < nrows ? bf16_bits_to_f32(((const uint16_t *)p.beta)[(tok0 + r) * p.HV + j])
-                        : 0.f;
-    if (p.pre.beta_sigmoid && r < nrows) in.beta = sigmoid_f(in.beta);   // pre-stage
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc((const uint16_t *)p.beta + tok0 * p.HV + j,
+                    nrows > 0 ? (uint32_t)((nrows - 1) * p.HV) * 2u + 2u : 0u);
+    in.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, r * p.HV * 2, 0, 0);
     in.nrows = nrows;
 }
 
@@ -157,7 +165,8 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     rows_to_tpl<K>(in.k, kr, stage, lane);
     rows_to_tpl<K>(in.q, qr, stage, lane);
     rows_to_tpl<V>(in.v, vraw, stage, lane);
-    const float beta_r = in.beta;
+    float beta_r = bf16_bits_to_f32((uint16_t)in.beta);
+    if (p.pre.beta_sigmoid && r < in.nrows) beta_r = sigmoid_f(beta_r);   // pre-stage
     // L2-norm factors of this lane's token row (its other columns are in the three other lane
     // groups); padding rows are zero and stay zero
     float rk = 1.f, rq = 1.f;

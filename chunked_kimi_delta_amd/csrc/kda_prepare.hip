@@ -269,9 +269,34 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
 // Neumann doubling product). One 256-thread block per (chunk, value head). T is the storage
 // type of the inputs (float for fp32 io; uint16_t bf16 bits for the backward of bf16 io, which
 // evaluates the chunks in fp32 from the same inputs).
-__device__ __forceinline__ float ld_in(const float *p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float ld_in(const uint16_t *p, int64_t i) {
-    return bf16_bits_to_f32(p[i]);
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+
+// out = A X for A 16 x 16 (rows 16-byte aligned) and X 16 x N in LDS, out row-major 16 x N:
+// each of the 256 threads takes one column and 16 N / 256 rows, so it reads its column of X
+// once and A's rows as broadcast 16-byte reads (the sum over m in ascending order).
+template <int N, int LD>
+__device__ __forceinline__ void rows_times_a(const float (*A)[20], const float (*X)[LD],
+                                             float *out, int tid)
+{
+    constexpr int RPT = 16 * N / 256;
+    const int d = tid % N, t0 = (tid / N) * RPT;
+    float x[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) x[m] = X[m][d];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const float4 a = *(const float4 *)&A[t0 + r][4 * m4];
+            acc += a.x * x[4 * m4];
+            acc += a.y * x[4 * m4 + 1];
+            acc += a.z * x[4 * m4 + 2];
+            acc += a.w * x[4 * m4 + 3];
+        }
+        out[(t0 + r) * N + d] = acc;
+    }
 }
 
 template <int K, int V, typename T, bool BWD>
@@ -279,8 +304,12 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
 {
     using WS = WsF32<K, V>;
     constexpr int STRIDE = BWD ? WsF32B<K, V>::BYTES : WS::BYTES;
-    __shared__ float sq[16][K + 1], sk[16][K + 1], sG[16][K + 1], sv[16][V + 1];
-    __shared__ float sb[16], sL[16][17], sI[16][17], sP[16][17], sT[16][17];
+    // rows padded to a multiple of 16 bytes (4 dims at a time in the Gram loop); a padding of
+    // 4 floats also puts the 16 rows of one dim in distinct banks
+    __shared__ __attribute__((aligned(16))) float sq[16][K + 4], sk[16][K + 4], sG[16][K + 4];
+    __shared__ float sv[16][V + 1];
+    __shared__ float sb[16], sL[16][17], sI[16][17], sT[16][17];
+    __shared__ __attribute__((aligned(16))) float sP[16][20];    // 16-byte rows
     const int tid = threadIdx.x;
     const int slot = blockIdx.x, j = blockIdx.y, h = j / p.G;
     int s;
@@ -292,24 +321,47 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     const T *v = (const T *)p.v, *g = (const T *)p.g;
     const bool gated = p.pre.gate != 0;              // pre-stage gate (valid rows only)
     const float aexp = gated ? __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E) : 0.f;
-    for (int idx = tid; idx < 16 * K; idx += 256) {
-        const int rr = idx / K, d = idx % K;
+    // Every load is issued before any value is used: rows past the sequence end read its last
+    // row (nvalid >= 1) and are zeroed when stored to LDS. A load under a branch, or arithmetic
+    // next to it, made the compiler wait for each load in turn.
+    constexpr int NE = 16 * K / 256, NEV = 16 * V / 256;   // elements per thread
+    T rq[NE], rk[NE], rg[NE], rv[NEV], rb;
+    float rdt[NE];
+    const float *dtb = gated && p.pre.dt_bias ? p.pre.dt_bias + (size_t)j * K : nullptr;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int idx = tid + 256 * e, rr = idx / K, d = idx % K;
+        const int64_t t = bos + (rr < nvalid ? rr : nvalid - 1);
+        rq[e] = q[(t * p.H + h) * K + d];
+        rk[e] = k[(t * p.H + h) * K + d];
+        rg[e] = g[(t * p.HV + j) * K + d];
+        rdt[e] = dtb ? dtb[d] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < NEV; ++e) {
+        const int idx = tid + 256 * e, rr = idx / V, d = idx % V;
+        const int64_t t = bos + (rr < nvalid ? rr : nvalid - 1);
+        rv[e] = v[(t * p.HV + j) * V + d];
+    }
+    rb = ((const T *)p.beta)[(bos + ((tid & 15) < nvalid ? (tid & 15) : nvalid - 1)) * p.HV + j];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int idx = tid + 256 * e, rr = idx / K, d = idx % K;
         const bool ok = rr < nvalid;
-        const int64_t t = bos + rr;
-        sq[rr][d] = ok ? ld_in(q, (t * p.H + h) * K + d) : 0.f;
-        sk[rr][d] = ok ? ld_in(k, (t * p.H + h) * K + d) : 0.f;
-        float gv = ok ? ld_in(g, (t * p.HV + j) * K + d) : 0.f;
+        sq[rr][d] = ok ? to_f32(rq[e]) : 0.f;
+        sk[rr][d] = ok ? to_f32(rk[e]) : 0.f;
+        float gv = ok ? to_f32(rg[e]) : 0.f;
         if (gated && ok)
-            gv = gate_activation(p.pre, gv + (p.pre.dt_bias ? p.pre.dt_bias[j * K + d] : 0.f),
-                                 aexp);
+            gv = gate_activation(p.pre, gv + rdt[e], aexp);
         sG[rr][d] = gv;
     }
-    for (int idx = tid; idx < 16 * V; idx += 256) {
-        const int rr = idx / V, d = idx % V;
-        sv[rr][d] = rr < nvalid ? ld_in(v, ((bos + rr) * p.HV + j) * V + d) : 0.f;
+#pragma unroll
+    for (int e = 0; e < NEV; ++e) {
+        const int idx = tid + 256 * e, rr = idx / V, d = idx % V;
+        sv[rr][d] = rr < nvalid ? to_f32(rv[e]) : 0.f;
     }
     if (tid < 16) {
-        float b = tid < nvalid ? ld_in((const T *)p.beta, (bos + tid) * p.HV + j) : 0.f;
+        float b = tid < nvalid ? to_f32(rb) : 0.f;
         if (p.pre.beta_sigmoid && tid < nvalid) b = sigmoid_f(b);
         sb[tid] = b;
     }
@@ -340,13 +392,37 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     __syncthreads();
 
     const int i = tid >> 4, jj = tid & 15;
+    // Gram and Mqk entries of the pairs row > col, with the exponent difference exact per pair
+    // and dim: pair (a, b) is split over two threads, (a, b) summing the first half of the key
+    // dims and (b, a) the second, which hands its part over through sT / sP. The diagonal of
+    // Mqk (no decay) is a plain dot product, reduced over the 16 threads of its row.
+    const int pa = i > jj ? i : jj, pb = i > jj ? jj : i;
+    const int dlo = i >= jj ? 0 : K / 2;
     float Lij = 0.f, Mij = 0.f;
-    if (i >= jj) {
-        for (int d = 0; d < K; ++d) {
-            const float kd = sk[jj][d] * __expf(sG[i][d] - sG[jj][d]);
-            Lij += sk[i][d] * kd;
-            Mij += sq[i][d] * kd;
-        }
+    for (int d = dlo; d < dlo + K / 2; d += 4) {
+        const float4 ga = *(const float4 *)&sG[pa][d], gb = *(const float4 *)&sG[pb][d];
+        const float4 ka = *(const float4 *)&sk[pa][d], kb = *(const float4 *)&sk[pb][d];
+        const float4 qa = *(const float4 *)&sq[pa][d];
+        const float e[4] = {__expf(ga.x - gb.x), __expf(ga.y - gb.y), __expf(ga.z - gb.z),
+                            __expf(ga.w - gb.w)};
+        const float kd[4] = {kb.x * e[0], kb.y * e[1], kb.z * e[2], kb.w * e[3]};
+        Lij += ka.x * kd[0]; Lij += ka.y * kd[1]; Lij += ka.z * kd[2]; Lij += ka.w * kd[3];
+        Mij += qa.x * kd[0]; Mij += qa.y * kd[1]; Mij += qa.z * kd[2]; Mij += qa.w * kd[3];
+    }
+    float Mdiag = 0.f;
+    for (int d = jj; d < K; d += 16) Mdiag += sq[i][d] * sk[i][d];
+    for (int m = 1; m < 16; m <<= 1) Mdiag += __shfl_xor(Mdiag, m);
+    if (i < jj) {
+        sT[i][jj] = Lij;
+        sP[i][jj] = Mij;
+    }
+    __syncthreads();
+    if (i > jj) {
+        Lij += sT[jj][i];
+        Mij += sP[jj][i];
+    } else if (i == jj) {
+        Lij = 0.f;
+        Mij = Mdiag;
     }
     const float Lv = i > jj ? sb[i] * Lij : 0.f;
     const float Mv = i >= jj ? p.scale * Mij : 0.f;
@@ -378,18 +454,8 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
         sq[t][d] = sk[t][d] * e;
     }
     __syncthreads();
-    for (int idx = tid; idx < 16 * K; idx += 256) {   // w = A KD
-        const int t = idx / K, d = idx % K;
-        float acc = 0.f;
-        for (int m = 0; m < 16; ++m) acc += sP[t][m] * sq[m][d];
-        ws[WS::W / 4 + t * K + d] = acc;
-    }
-    for (int idx = tid; idx < 16 * V; idx += 256) {
-        const int t = idx / V, d = idx % V;
-        float acc = 0.f;
-        for (int m = 0; m < 16; ++m) acc += sP[t][m] * sv[m][d];
-        ws[WS::U / 4 + t * V + d] = acc;
-    }
+    rows_times_a<K>(sP, sq, ws + WS::W / 4, tid);        // w = A KD
+    rows_times_a<V>(sP, sv, ws + WS::U / 4, tid);        // u = A v
     ws[WS::MQK / 4 + i * 16 + jj] = Mv;
     for (int d = tid; d < K; d += 256) ws[WS::EG / 4 + d] = __expf(sG[15][d]);
     if (BWD) {                        // the inverse and the Gram, for the local gradients
