@@ -254,6 +254,7 @@ kda_status kda_bwd(const kda_fwd_args *a, const void *d_o, const float *dht, voi
     p.h0 = a->initial_state;
     p.o = nullptr;
     p.ht = nullptr;
+    p.d_o = d_o;
     uint8_t *ws = (uint8_t *)workspace;
     p.ws = ws;
     p.pre.qk_l2norm = a->qk_l2norm != 0;

@@ -33,7 +33,7 @@ namespace {
 // Both chains of the backward in one launch (they are independent): per unit, sub-slices
 // 2i (states, recorded at every chunk start) and 2i + 1 (the state gradient, recorded at every
 // chunk end, then dh0) of the 16-column slice i, all on one XCD (kda_chain_f32.h).
-template <int K, int V, typename T>
+template <int K, int V>
 __global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams b)
 {
     constexpr int NSL = V / 16;
@@ -42,11 +42,11 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n0 = (sub >> 1) * 16;
     constexpr int RB = WsF32B<K, V>::BYTES;
     if (sub & 1)
-        chain_run<K, V, T, CHAIN_GRADS>(b.f, unit, n0, wave, lane, b.dht, b.ck_L, b.dh0,
-                                        nullptr, RB, (const T *)b.d_o);
+        chain_run<K, V, CHAIN_GRADS>(b.f, unit, n0, wave, lane, b.dht, b.ck_L, b.dh0, nullptr,
+                                     RB);
     else
-        chain_run<K, V, T, CHAIN_STATES>(b.f, unit, n0, wave, lane, b.f.h0, b.ck_S, nullptr,
-                                         nullptr, RB, (const T *)b.d_o);
+        chain_run<K, V, CHAIN_STATES>(b.f, unit, n0, wave, lane, b.f.h0, b.ck_S, nullptr,
+                                      nullptr, RB);
 }
 
 // One block (4 waves) per (chunk slot, value head): back-propagate O and S_next (through
@@ -150,21 +150,40 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
     auto dtb = [&](int d) { return gated && p.pre.dt_bias ? p.pre.dt_bias[j * K + d] : 0.f; };
 
     // ---- inputs of the chunk (rows past the end are zero), pre-stage, the cumsum of g
-    for (int idx = tid; idx < 16 * K; idx += 256) {
-        const int r = idx / K, d = idx % K;
-        const bool ok = r < nvalid;
-        const int64_t t = bos + r;
-        sh.q[r][d] = ok ? ldx(q, (t * p.H + h) * K + d) : 0.f;
-        sh.k[r][d] = ok ? ldx(k, (t * p.H + h) * K + d) : 0.f;
-        float gv = ok ? ldx(g, (t * p.HV + j) * K + d) : 0.f;
-        if (gated && ok) gv = gate_activation(p.pre, gv + dtb(d), aexp);
-        sh.gm[r][d] = gv;
-    }
-    if (tid < 16) {
-        float bv = tid < nvalid ? ldx(bt, (bos + tid) * p.HV + j) : 0.f;
-        if (p.pre.beta_sigmoid && tid < nvalid) bv = sigmoid_f(bv);
-        sh.beta[tid] = bv;
-        sh.dbeta[tid] = 0.f;
+    // Every load is issued before any value is used: rows past the sequence end read its last
+    // row (nvalid >= 1) and are zeroed on the way to LDS (a load under a branch, or used next
+    // to it, made the compiler wait for each load in turn).
+    {
+        constexpr int NE = 16 * K / 256;
+        T rq[NE], rk[NE], rg[NE], rb;
+        float rdt[NE];
+        const float *dtp = gated && p.pre.dt_bias ? p.pre.dt_bias + (size_t)j * K : nullptr;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int idx = tid + 256 * e, r = idx / K, d = idx % K;
+            const int64_t t = bos + (r < nvalid ? r : nvalid - 1);
+            rq[e] = q[(t * p.H + h) * K + d];
+            rk[e] = k[(t * p.H + h) * K + d];
+            rg[e] = g[(t * p.HV + j) * K + d];
+            rdt[e] = dtp ? dtp[d] : 0.f;
+        }
+        rb = bt[(bos + ((tid & 15) < nvalid ? (tid & 15) : nvalid - 1)) * p.HV + j];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int idx = tid + 256 * e, r = idx / K, d = idx % K;
+            const bool ok = r < nvalid;
+            sh.q[r][d] = ok ? to_f32(rq[e]) : 0.f;
+            sh.k[r][d] = ok ? to_f32(rk[e]) : 0.f;
+            float gv = ok ? to_f32(rg[e]) : 0.f;
+            if (gated && ok) gv = gate_activation(p.pre, gv + rdt[e], aexp);
+            sh.gm[r][d] = gv;
+        }
+        if (tid < 16) {
+            float bv = tid < nvalid ? to_f32(rb) : 0.f;
+            if (p.pre.beta_sigmoid && tid < nvalid) bv = sigmoid_f(bv);
+            sh.beta[tid] = bv;
+            sh.dbeta[tid] = 0.f;
+        }
     }
     __syncthreads();
     if (p.pre.qk_l2norm) {         // 16 threads per token row: partial sums, xor reduction
@@ -235,11 +254,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdParams b)
             o.sc[x] = __builtin_nontemporal_load((const f32x4 *)(cS + to));
             o.lc[x] = __builtin_nontemporal_load((const f32x4 *)(cL + to));
         }
+        o.doc = *(const f32x4 *)(rec + WSB::DO / 4 + (nb * 64 + lane) * 4);   // dO, C-layout
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            o.doc[i] = ldx(dout, ((bos + rq[i]) * p.HV + j) * V + n0 + r);
-            o.vc[i] = ldx(v, ((bos + rq[i]) * p.HV + j) * V + n0 + r);
-        }
+        for (int i = 0; i < 4; ++i) o.vc[i] = ldx(v, ((bos + rq[i]) * p.HV + j) * V + n0 + r);
         o.doa = ld4(dout + ((bos + rc) * p.HV + j) * V + n0 + 4 * gq);
         o.va = ld4(v + ((bos + rc) * p.HV + j) * V + n0 + 4 * gq);
     };
@@ -605,10 +622,7 @@ hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st)
     const int64_t units = (int64_t)p.seq.N * p.HV;
     if (units == 0) return hipSuccess;
     const dim3 cgrid((unsigned)((units + 7) / 8 * 8 * 2 * (V / 16)));
-    if (in_bf16)
-        bwd_chains_kernel<K, V, uint16_t><<<cgrid, dim3(64 * CHAIN_WAVES), 0, st>>>(b);
-    else
-        bwd_chains_kernel<K, V, float><<<cgrid, dim3(64 * CHAIN_WAVES), 0, st>>>(b);
+    bwd_chains_kernel<K, V><<<cgrid, dim3(64 * CHAIN_WAVES), 0, st>>>(b);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.seq.T_total > 0) {
         dim3 grid(p.seq.n_slots, p.HV);

@@ -19,9 +19,9 @@
 // the C-layout registers as they are), one 1 KB contiguous block per tile and wave, with
 // non-temporal stores.
 // The chunk records are read as they are laid out ([16][K] row-major w, qd, kr; [16][V] u;
-// [16][16] Mqk; [K] E): A-operand rows of w, qd, kr and Mqk are contiguous 16-byte loads, the
-// transposes four 4-byte loads. Records of the next chunk are loaded before the current
-// chunk's products.
+// [16][16] Mqk; [K] E; the backward's copy of dO in C-layout): A-operand rows of w, qd, kr and
+// Mqk and the dO tile are contiguous 16-byte loads, the transposes four 4-byte loads. Records
+// of the next chunk are loaded before the current chunk's products.
 #pragma once
 
 #include "kda_internal.h"
@@ -29,8 +29,6 @@
 namespace kda {
 
 namespace {
-
-typedef float f32v2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float ldx(const float *p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ldx(const uint16_t *p, int64_t i) {
@@ -52,10 +50,9 @@ struct ChainOps {
     f32x4 m;          // grads: Mqk^T;  forward: Mqk rows             (A operand; wave 0 uses it)
 };
 
-template <int K, int V, typename T, int MODE>
-__device__ __forceinline__ void chain_load(ChainOps<K> &o, const float *ch, const T *dout,
-                                           int64_t tok0, int64_t eos, int HV, int j, int n0,
-                                           int wave, int lane)
+template <int K, int V, int MODE>
+__device__ __forceinline__ void chain_load(ChainOps<K> &o, const float *ch, int n0, int wave,
+                                           int lane)
 {
     using WS = WsF32<K, V>;
     constexpr bool GRAD = MODE == CHAIN_GRADS, FWD = MODE == CHAIN_FORWARD;
@@ -80,12 +77,13 @@ __device__ __forceinline__ void chain_load(ChainOps<K> &o, const float *ch, cons
     // read its last row and are zeroed at use): any arithmetic on a value here, or a load under
     // a branch, would make the compiler wait for the load on the spot.
     if (FWD) o.m = *(const f32x4 *)(ch + WS::MQK / 4 + r * 16 + 4 * g);
+    // dO (grads) from the backward record, where the prepare kernel put it in this order: an
+    // input read straight from HBM arrived too late for a load one chunk ahead
+    if (GRAD) o.x = *(const f32x4 *)(ch + WsF32B<K, V>::DO / 4 + ((n0 / 16) * 64 + lane) * 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = 4 * g + i;
         if (GRAD) {
-            const int64_t tok = tok0 + t, tc = tok < eos ? tok : eos - 1;
-            o.x[i] = ldx(dout, (tc * HV + j) * V + n0 + r);
             o.m[i] = ch[WS::MQK / 4 + t * 16 + r];
         } else {
             o.x[i] = ch[WS::U / 4 + t * V + n0 + r];
@@ -96,11 +94,11 @@ __device__ __forceinline__ void chain_load(ChainOps<K> &o, const float *ch, cons
 // One chain of one 16-column slice (columns n0 ..) of one unit (sequence * HV + value head).
 // init: S (states, forward) or Lam (grads) at the start, [N][HV][K][V] or null (zero); ck: the
 // per-chunk records (states, grads); fin: where the last S / Lam goes (final state, dh0) or
-// null; o: the forward's output (fp32 io); rec_bytes: the chunk record's size; dout: dO.
-template <int K, int V, typename T, int MODE>
+// null; o: the forward's output (fp32 io); rec_bytes: the chunk record's size.
+template <int K, int V, int MODE>
 __device__ __forceinline__ void chain_run(const FwdParams &p, int unit, int n0, int wave,
                                           int lane, const float *init, float *ck, float *fin,
-                                          float *o, int rec_bytes, const T *dout)
+                                          float *o, int rec_bytes)
 {
     constexpr bool GRAD = MODE == CHAIN_GRADS, FWD = MODE == CHAIN_FORWARD;
     constexpr int TPW = ChainOps<K>::TPW;
@@ -196,7 +194,7 @@ __device__ __forceinline__ void chain_run(const FwdParams &p, int unit, int n0, 
     };
     auto load = [&](ChainOps<K> &op, int it) {
         const int c = GRAD ? nc - 1 - it : it;
-        chain_load<K, V, T, MODE>(op, rec(c), dout, bos + 16 * c, eos, p.HV, j, n0, wave, lane);
+        chain_load<K, V, MODE>(op, rec(c), n0, wave, lane);
     };
     // two operand sets used alternately (a copy from one to the other would wait for the loads)
     if (nc > 0) {

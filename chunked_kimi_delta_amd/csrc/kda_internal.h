@@ -66,6 +66,7 @@ struct FwdParams {
     float *ht;
     uint8_t *ws;
     Prestage pre;
+    const void *d_o = nullptr;   // backward only: d loss / d o, copied into the chunk records
 };
 
 // Arguments of the backward: the forward's (f.ws holds the fp32 chunk records), the incoming
@@ -153,12 +154,15 @@ struct WsF32 {
 };
 
 // The backward's fp32 chunk record: WsF32 followed by the inverse X = (I + L)^{-1} and the
-// strictly lower Gram G (L = diag(beta) G), both [16][16] fp32 row-major.
+// strictly lower Gram G (L = diag(beta) G), both [16][16] fp32 row-major, and the chunk's dO.
 template <int K, int V>
 struct WsF32B : WsF32<K, V> {
     static constexpr int XM = WsF32<K, V>::END;
     static constexpr int GM = XM + 1024;
-    static constexpr int END = GM + 1024;
+    // dO of the chunk's 16 rows in fp32, C-layout per 16-column slice ([V/16][64 lanes][4]:
+    // lane (g, r) holds rows 4g .. 4g + 3 of column 16 n + r), rows past the sequence end zero
+    static constexpr int DO = GM + 1024;
+    static constexpr int END = DO + 16 * V * 4;
     static constexpr int BYTES = (END + 255) / 256 * 256;
 };
 
@@ -228,6 +232,9 @@ __device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x &
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
     return __uint_as_float((uint32_t)x << 16);
 }
+// an io element as fp32 (fp32 io, or bf16 bits)
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 
 // four consecutive bf16 (8 bytes) -> fp32
 __device__ __forceinline__ void unpack_bf16x4(uint2 raw, float out[4]) {
@@ -283,6 +290,7 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // Vector loads through a buffer resource: the address is resource base (scalar) + soffset
 // (scalar) + voffset (per lane), so per-chunk address arithmetic stays on the scalar unit.
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef float f32v2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
@@ -294,6 +302,22 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int
 template <int AUX = 0>
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+}
+// One io element (fp32, or bf16 bits) through a buffer resource: loads past its range read 0.
+__device__ __forceinline__ void bload_elem(__amdgpu_buffer_rsrc_t r, int voff, float &x) {
+    x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+__device__ __forceinline__ void bload_elem(__amdgpu_buffer_rsrc_t r, int voff, uint16_t &x) {
+    x = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+// A resource over the first `rows` rows (of `row_elems` elements, `row_stride` elements apart)
+// from `base`: the rows after them read as zero.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_in(const T *base, int rows,
+                                                          int64_t row_stride, int row_elems) {
+    return buffer_rsrc(base, rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * row_stride + row_elems) *
+                                                   (int64_t)sizeof(T))
+                                      : 0u);
 }
 // Stores through a buffer resource with cache policy AUX; stores past the resource's size are
 // dropped. A 16-byte store goes out as two 8-byte stores: behind a store with 128-bit data the

@@ -269,8 +269,6 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
 // Neumann doubling product). One 256-thread block per (chunk, value head). T is the storage
 // type of the inputs (float for fp32 io; uint16_t bf16 bits for the backward of bf16 io, which
 // evaluates the chunks in fp32 from the same inputs).
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 
 // out = A X for A 16 x 16 (rows 16-byte aligned) and X 16 x N in LDS, out row-major 16 x N:
 // each of the 256 threads takes one column and 16 N / 256 rows, so it reads its column of X
@@ -284,7 +282,7 @@ __device__ __forceinline__ void rows_times_a(const float (*A)[20], const float (
     float x[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) x[m] = X[m][d];
-#pragma unroll
+#pragma unroll 2
     for (int r = 0; r < RPT; ++r) {
         float acc = 0.f;
 #pragma unroll
@@ -317,33 +315,45 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     int nvalid;
     if (!locate_slot(p.seq, slot, &s, &bos, &nvalid)) return;
 
-    const T *q = (const T *)p.q, *k = (const T *)p.k;
-    const T *v = (const T *)p.v, *g = (const T *)p.g;
     const bool gated = p.pre.gate != 0;              // pre-stage gate (valid rows only)
     const float aexp = gated ? __builtin_amdgcn_exp2f(p.pre.A_log[j] * LOG2E) : 0.f;
-    // Every load is issued before any value is used: rows past the sequence end read its last
-    // row (nvalid >= 1) and are zeroed when stored to LDS. A load under a branch, or arithmetic
-    // next to it, made the compiler wait for each load in turn.
+    // Every load is issued before any value is used, through buffer resources that end with
+    // the chunk's last valid row (later rows read as zero, with no branch: a load under a
+    // branch, or arithmetic next to it, made the compiler wait for each load in turn; scalar
+    // bases keep one 32-bit offset register per load).
     constexpr int NE = 16 * K / 256, NEV = 16 * V / 256;   // elements per thread
+    constexpr int SZ = (int)sizeof(T);
+    const int64_t sqk = (int64_t)p.H * K, sgk = (int64_t)p.HV * K, svv = (int64_t)p.HV * V;
+    const auto rs_q = rows_in((const T *)p.q + (bos * p.H + h) * K, nvalid, sqk, K);
+    const auto rs_k = rows_in((const T *)p.k + (bos * p.H + h) * K, nvalid, sqk, K);
+    const auto rs_g = rows_in((const T *)p.g + (bos * p.HV + j) * K, nvalid, sgk, K);
+    const auto rs_v = rows_in((const T *)p.v + (bos * p.HV + j) * V, nvalid, svv, V);
+    const auto rs_b = rows_in((const T *)p.beta + bos * p.HV + j, nvalid, p.HV, 1);
     T rq[NE], rk[NE], rg[NE], rv[NEV], rb;
-    float rdt[NE];
-    const float *dtb = gated && p.pre.dt_bias ? p.pre.dt_bias + (size_t)j * K : nullptr;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         const int idx = tid + 256 * e, rr = idx / K, d = idx % K;
-        const int64_t t = bos + (rr < nvalid ? rr : nvalid - 1);
-        rq[e] = q[(t * p.H + h) * K + d];
-        rk[e] = k[(t * p.H + h) * K + d];
-        rg[e] = g[(t * p.HV + j) * K + d];
-        rdt[e] = dtb ? dtb[d] : 0.f;
+        bload_elem(rs_q, (int)(rr * sqk + d) * SZ, rq[e]);
+        bload_elem(rs_k, (int)(rr * sqk + d) * SZ, rk[e]);
+        bload_elem(rs_g, (int)(rr * sgk + d) * SZ, rg[e]);
     }
 #pragma unroll
     for (int e = 0; e < NEV; ++e) {
         const int idx = tid + 256 * e, rr = idx / V, d = idx % V;
-        const int64_t t = bos + (rr < nvalid ? rr : nvalid - 1);
-        rv[e] = v[(t * p.HV + j) * V + d];
+        bload_elem(rs_v, (int)(rr * svv + d) * SZ, rv[e]);
     }
-    rb = ((const T *)p.beta)[(bos + ((tid & 15) < nvalid ? (tid & 15) : nvalid - 1)) * p.HV + j];
+    bload_elem(rs_b, (tid & 15) * p.HV * SZ, rb);
+    // the gate's dt_bias of this thread's key dim (K divides 256: the same dim for every e)
+    const float rdt = gated && p.pre.dt_bias ? p.pre.dt_bias[j * K + tid % K] : 0.f;
+    // dO (backward): column tid % V, rows do0 .. do0 + NEV - 1 of the chunk
+    const int do0 = (tid / V) * NEV;
+    T rdo[BWD ? NEV : 1];
+    if (BWD) {
+        const auto rs_o = rows_in((const T *)p.d_o + (bos * p.HV + j) * V, nvalid, svv, V);
+#pragma unroll
+        for (int e = 0; e < NEV; ++e)
+            bload_elem(rs_o, (int)((do0 + e) * svv + tid % V) * SZ, rdo[e]);
+    }
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         const int idx = tid + 256 * e, rr = idx / K, d = idx % K;
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
         sk[rr][d] = ok ? to_f32(rk[e]) : 0.f;
         float gv = ok ? to_f32(rg[e]) : 0.f;
         if (gated && ok)
-            gv = gate_activation(p.pre, gv + rdt[e], aexp);
+            gv = gate_activation(p.pre, gv + rdt, aexp);
         sG[rr][d] = gv;
     }
 #pragma unroll
@@ -399,6 +409,7 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     const int pa = i > jj ? i : jj, pb = i > jj ? jj : i;
     const int dlo = i >= jj ? 0 : K / 2;
     float Lij = 0.f, Mij = 0.f;
+#pragma unroll 2
     for (int d = dlo; d < dlo + K / 2; d += 4) {
         const float4 ga = *(const float4 *)&sG[pa][d], gb = *(const float4 *)&sG[pb][d];
         const float4 ka = *(const float4 *)&sk[pa][d], kb = *(const float4 *)&sk[pb][d];
@@ -461,6 +472,19 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(FwdParams p)
     if (BWD) {                        // the inverse and the Gram, for the local gradients
         ws[WsF32B<K, V>::XM / 4 + i * 16 + jj] = sI[i][jj];
         ws[WsF32B<K, V>::GM / 4 + i * 16 + jj] = i > jj ? Lij : 0.f;
+        // dO in the grads chain's operand order (a 16-byte load per lane): element (t, d) at
+        // [d / 16][lane (t / 4, d % 16)][t % 4]; each thread writes whole 16-byte groups (four
+        // rows of its column)
+        const __amdgpu_buffer_rsrc_t dr = buffer_rsrc(ws + WsF32B<K, V>::DO / 4, 16 * V * 4);
+        const int d = tid % V;
+#pragma unroll
+        for (int e = 0; e < NEV; e += 4) {
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = do0 + e + i < nvalid ? to_f32(rdo[e + i]) : 0.f;
+            const int off = ((d / 16) * 64 + ((do0 + e) / 4) * 16 + d % 16) * 16;
+            bstore16<0>(dr, off, 0, f32x4{x[0], x[1], x[2], x[3]});
+        }
     }
 }
 

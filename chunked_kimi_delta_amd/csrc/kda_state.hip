@@ -259,9 +259,8 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void state_f32_kernel(FwdParams p
 {
     int unit, slice;
     if (!state_unit(blockIdx.x, V / 16, p.seq.N * p.HV, &unit, &slice)) return;
-    chain_run<K, V, float, CHAIN_FORWARD>(p, unit, slice * 16, threadIdx.x >> 6,
-                                          threadIdx.x & 63, p.h0, nullptr, p.ht, (float *)p.o,
-                                          WsF32<K, V>::BYTES, (const float *)nullptr);
+    chain_run<K, V, CHAIN_FORWARD>(p, unit, slice * 16, threadIdx.x >> 6, threadIdx.x & 63,
+                                   p.h0, nullptr, p.ht, (float *)p.o, WsF32<K, V>::BYTES);
 }
 
 template <int K, int V>

@@ -171,8 +171,9 @@ def test_bwd_workspace_bytes(lib):
         B, T, N, H, HV, K, V = (getattr(a, n) for n in ("B", "T", "N", "H", "HV", "K", "V"))
         slots = B * T // 16 + N
         # the forward's fp32 record plus the inverse and the Gram (two 16 x 16 fp32 blocks)
+        # and the chunk's dO (16 x V fp32)
         rec = lib.kda_fwd_workspace_bytes(ctypes.byref(args(**dict(kw, io=1, chunk=16))))
-        rec += slots * HV * 2048
+        rec += slots * HV * (2048 + 16 * V * 4)
         part = B * T * HV * K * 4 if HV > H else 0
         assert f(a) == up(rec) + 2 * up(slots * HV * K * V * 4) + 2 * up(part), kw
     base = f(args())
