@@ -19,11 +19,6 @@ namespace kda {
 
 namespace {
 
-__device__ __forceinline__ float ld_io(const uint16_t *p, int64_t i) {
-    return bf16_bits_to_f32(p[i]);
-}
-__device__ __forceinline__ float ld_io(const float *p, int64_t i) { return p[i]; }
-
 __device__ __forceinline__ void st_io(uint16_t *p, int64_t i, float x) {
     p[i] = __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -32,6 +27,13 @@ __device__ __forceinline__ void st_io(float *p, int64_t i, float x) { p[i] = x; 
 template <int K>
 struct TokenRow {
     f32x4 qkeb[K];               // per key dim: q, k, exp(g), beta * k
+};
+
+// What one token contributes, as stored (raw io values), for lane l: key dims l, l + 64, ...
+// and its value column.
+template <int KL, typename T>
+struct TokenIn {
+    T q[KL], k[KL], g[KL], b, v;
 };
 
 }  // namespace
@@ -66,6 +68,31 @@ __global__ __launch_bounds__(64) void recurrent_kernel(FwdParams p)
     for (int u = 0; u < KL; ++u)
         dtl[u] = gated && p.pre.dt_bias ? p.pre.dt_bias[(size_t)j * K + lane + 64 * u] : 0.f;
 
+    // the inputs of token t of this sequence, through resources over its rows only (a token
+    // past the sequence end reads zeros and is never used): no load sits under a branch
+    constexpr int SZ = (int)sizeof(T);
+    auto load_token = [&](TokenIn<KL, T> &x, int64_t t) {
+        const bool in = t < eos;
+        const int64_t tc = in ? t : 0;
+        const auto rq = buffer_rsrc(q + (tc * p.H + h) * K, in ? K * SZ : 0);
+        const auto rk = buffer_rsrc(k + (tc * p.H + h) * K, in ? K * SZ : 0);
+        const auto rg = buffer_rsrc(g + (tc * p.HV + j) * K, in ? K * SZ : 0);
+        const auto rb = buffer_rsrc(beta + tc * p.HV + j, in ? SZ : 0);
+        const auto rv = buffer_rsrc(v + (tc * p.HV + j) * V, in ? V * SZ : 0);
+#pragma unroll
+        for (int u = 0; u < KL; ++u) {
+            bload_elem(rq, (lane + 64 * u) * SZ, x.q[u]);
+            bload_elem(rk, (lane + 64 * u) * SZ, x.k[u]);
+            bload_elem(rg, (lane + 64 * u) * SZ, x.g[u]);
+        }
+        bload_elem(rb, 0, x.b);
+        bload_elem(rv, col * SZ, x.v);
+    };
+    // the first token's inputs go out before the state, so their latency is covered by it;
+    // every later token's go out one token ahead
+    TokenIn<KL, T> x;
+    load_token(x, bos);
+
     float S[K];
     if (p.h0) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.h0 + st_off, st_bytes);
@@ -79,17 +106,22 @@ __global__ __launch_bounds__(64) void recurrent_kernel(FwdParams p)
     }
 
     for (int64_t t = bos; t < eos; ++t) {
-        float b = ld_io(beta, t * p.HV + j);
-        if (p.pre.beta_sigmoid) b = sigmoid_f(b);
-        // stage this token's q, k, exp(g), beta k: lane l takes key dims l, l + 64, ...
+        // this token's inputs (loaded one token earlier), then the next token's loads into the
+        // same registers
+        float b = to_f32(x.b), vt = to_f32(x.v);
         float qv[KL], kv[KL], gv[KL];
 #pragma unroll
         for (int u = 0; u < KL; ++u) {
-            const int kk = lane + 64 * u;
-            qv[u] = ld_io(q, (t * p.H + h) * K + kk);
-            kv[u] = ld_io(k, (t * p.H + h) * K + kk);
-            gv[u] = ld_io(g, (t * p.HV + j) * K + kk);
-            if (gated) gv[u] = gate_activation(p.pre, gv[u] + dtl[u], aexp);
+            qv[u] = to_f32(x.q[u]);
+            kv[u] = to_f32(x.k[u]);
+            gv[u] = to_f32(x.g[u]);
+        }
+        load_token(x, t + 1);
+        if (p.pre.beta_sigmoid) b = sigmoid_f(b);
+        // stage this token's q, k, exp(g), beta k: lane l takes key dims l, l + 64, ...
+        if (gated) {
+#pragma unroll
+            for (int u = 0; u < KL; ++u) gv[u] = gate_activation(p.pre, gv[u] + dtl[u], aexp);
         }
         if (p.pre.qk_l2norm) {          // pre-stage: the token's q and k over all K dims
             float sq = 0.f, sk = 0.f;
@@ -122,7 +154,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(FwdParams p)
             kS += e[1] * S[kk];
             if (kk % 8 == 7) __builtin_amdgcn_sched_barrier(0);
         }
-        const float r = ld_io(v, (t * p.HV + j) * V + col) - kS;
+        const float r = vt - kS;
         float os = 0.f;
 #pragma unroll
         for (int kk = 0; kk < K; ++kk) {
