@@ -550,6 +550,7 @@ __global__ __launch_bounds__(256) void bwd_qk_finalize_kernel(BwdParams b)
 #pragma unroll
             for (int e = 0; e < PL; ++e) {
                 float acc = 0.f;
+#pragma unroll 4
                 for (int jj = 0; jj < p.G; ++jj)
                     acc += part[(tok * p.HV + h * p.G + jj) * K + lane + 64 * e];
                 dy[e] = acc;
@@ -632,10 +633,14 @@ hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st)
             bwd_local_kernel<K, V, float><<<grid, dim3(256), 0, st>>>(b);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (p.G > 1 || p.pre.qk_l2norm) {
+            // one wave per (token, q/k head) row up to 2^20 waves (the loads of a row are
+            // waited for where they are used, so the latency is covered by other waves)
+            const int64_t rows = p.seq.T_total * p.H;
+            const unsigned fg = (unsigned)((rows + 3) / 4 < (1 << 18) ? (rows + 3) / 4 : (1 << 18));
             if (in_bf16)
-                bwd_qk_finalize_kernel<K, uint16_t><<<dim3(1024), dim3(256), 0, st>>>(b);
+                bwd_qk_finalize_kernel<K, uint16_t><<<dim3(fg), dim3(256), 0, st>>>(b);
             else
-                bwd_qk_finalize_kernel<K, float><<<dim3(1024), dim3(256), 0, st>>>(b);
+                bwd_qk_finalize_kernel<K, float><<<dim3(fg), dim3(256), 0, st>>>(b);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
