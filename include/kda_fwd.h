@@ -171,8 +171,9 @@ kda_status kda_fwd_state(const kda_fwd_args *args, void *workspace, size_t ws_by
    dq, dk, dg, dbeta are the gradients of the arguments as passed: with the pre-stage on, of
    the raw q, k, g, beta.
    `workspace`: at least kda_bwd_workspace_bytes(args) bytes, 256-byte aligned, contents on
-   entry irrelevant: the fp32 chunk records, the state at every chunk start and the state
-   gradient at every chunk end (about 2 * (B*T/16 + N) * HV * K * V * 4 bytes), plus
+   entry irrelevant: the fp32 chunk records (each with a copy of its chunk's d_o), the state
+   at every chunk start and the state gradient at every chunk end (about
+   2 * (B*T/16 + N) * HV * K * V * 4 bytes), plus
    2 * B*T * HV * K * 4 bytes when HV > H or the q/k L2 norm is on, plus (B*T/16 + N) * HV *
    (K + 1) * 4 bytes with a gate. Status codes as for kda_fwd; KDA_ERR_UNSUPPORTED also for a
    chunk other than 0 or 16; KDA_ERR_INVALID_ARG also for a missing or misaligned dA_log with
