@@ -7,6 +7,9 @@ per instruction. The compiler merges plain 8-byte stores to adjacent addresses i
 store, so the kernels use the buffer-store intrinsics, which it leaves alone; these tests keep
 any wide store, and in particular one followed closely by a write of its data registers, out of
 the library.
+
+The forward kernels are also checked for a wait on all outstanding loads right behind a load,
+the pattern a load under a branch or a conversion next to a load produces.
 """
 from __future__ import annotations
 
@@ -111,3 +114,44 @@ def test_no_wide_stores_at_all():
         if n:
             bad[os.path.basename(s)] = n
     assert not bad, f"stores wider than 8 bytes: {bad}"
+
+
+def load_then_full_wait(asm: str, window: int = 3):
+    """(line, load) pairs where `s_waitcnt vmcnt(0)` follows a vector-memory load within
+    `window` instructions: the wave waits for every load it has in flight right after issuing
+    one, which serialises a load phase into memory round trips."""
+    lines = [l.split(";")[0].strip() for l in asm.splitlines()]
+    ins = [(i, l) for i, l in enumerate(lines) if l and not l.startswith(".") and not l.endswith(":")]
+    out = []
+    for n, (i, l) in enumerate(ins):
+        if l.startswith("s_waitcnt") and "vmcnt(0)" in l:
+            for _, p in ins[max(0, n - window):n]:
+                if re.match(r"(global|buffer|flat)_load", p):
+                    out.append((i, p))
+                    break
+    return out
+
+
+def test_detector_finds_a_load_then_full_wait():
+    asm = "\n".join(["global_load_ushort v1, v[2:3], off", "v_mov_b32 v5, 0",
+                     "s_waitcnt vmcnt(0)", "v_lshlrev_b32_e32 v1, 16, v1"])
+    assert len(load_then_full_wait(asm)) == 1
+    assert load_then_full_wait(asm.replace("vmcnt(0)", "vmcnt(3)")) == []
+
+
+# Forward kernels: their loads are issued unconditionally and converted where they are used,
+# so no load is waited for on the spot (a load under a per-row branch, or a conversion next to
+# it, had serialised the prepare and token-recurrence load phases).
+FORWARD_SOURCES = ("kda_prepare32.hip", "kda_state32.hip", "kda_recurrent.hip", "kda_prepare.hip",
+                   "kda_state.hip")
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="hipcc not available")
+def test_forward_kernels_do_not_wait_on_each_load():
+    bad = {}
+    for s, a in kernel_asms().items():
+        if os.path.basename(s) in FORWARD_SOURCES:
+            hits = load_then_full_wait(a)
+            if hits:
+                bad[os.path.basename(s)] = hits[:3]
+    assert not bad, bad
