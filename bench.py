@@ -3,12 +3,13 @@
 
 A step is one full forward (prepare kernel + state kernel, i.e. one kda_fwd call) over one
 synthetic batch already resident in HBM. Default workload: B=1, T=4096, H=HV=16, K=V=128, bf16
-io ("h16_t4096"). The timed region is exactly --steps back-to-back kda_fwd calls bracketed by
-torch.cuda.synchronize(), with nothing else enqueued between them (an event record between two
-launches costs several microseconds of GPU time here). Each kernel's average duration for the
-roofline figures comes from a second pass of --steps steps, the two stages launched separately
-(kda_fwd_prepare, kda_fwd_state: the same kernels) with HIP events around each launch on the
-stream it runs on.
+io ("h16_t4096"). The timed region is exactly --steps kda_fwd calls bracketed by
+torch.cuda.synchronize(); before each step a 1 GiB device copy (a write of 1 GiB) evicts L2 and
+the 256 MB MALL, and each step is timed alone with HIP events on its stream, so the step reads
+its inputs from HBM; the reported time is the median step. Each kernel's average duration for
+the roofline figures comes from a second pass of --steps flushed steps, the two stages launched
+separately (kda_fwd_prepare, kda_fwd_state: the same kernels) with HIP events around each
+launch on the stream it runs on.
 
 With --backward the step is one kda_bwd call instead (gradients of every input from seeded
 d_o and dht), reported under its own metric; the default line is the forward.
@@ -17,7 +18,8 @@ Extra fields beyond the driver contract:
   roofline        dominant kernel: achieved algorithmic throughput / MI355X peak
   roofline_path   the whole forward against the HBM roof (algorithmic bytes / step time)
   kernels         per-kernel average durations and algorithmic work
-  cold_cache      per-step time when a 1 GiB copy evicts the caches between steps
+  warm_cache      back-to-back steps without flushes (the working set stays in the MALL)
+  chunk16_run     the same workload with 16-token chunks, timed the same way
   cpu_baseline    the fp64 C oracle on the host cores over a bounded sample
 """
 from __future__ import annotations
@@ -261,6 +263,23 @@ def summarize_mfma(d: str, command: str) -> str:
     return "\n".join(out)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Host threads the oracle runs on: the CPU share of a one-GPU machine (16 CPUs), or fewer when the
+# process may run on fewer. The affinity mask of a box can list every CPU of the host, which
+# the other GPUs' jobs share.
+BOX_CPU_SHARE = 16
+
+
 def cpu_baseline(inp, min_seconds: float):
     """The fp64 C oracle (unchanged) on the host cores: the whole workload, repeated until at
     least `min_seconds` of wall time have passed (bounded at 1000 repetitions); then the same
@@ -268,10 +287,10 @@ def cpu_baseline(inp, min_seconds: float):
     import workloads as W
     from oracle.native import kda_oracle_c
     try:
-        cores = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))        # a one-GPU machine's CPU share
+        affinity = os.cpu_count() or 1
+    cores = max(1, min(affinity, BOX_CPU_SHARE))
     f = W.as_f32_numpy
     args = [f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta)]
     h0 = None if inp.h0 is None else inp.h0.numpy()
@@ -290,7 +309,10 @@ def cpu_baseline(inp, min_seconds: float):
             "kind": "oracle",
             "sample": f"full {inp.w.name} forward (all {inp.w.HV} heads, fp64 C recurrence), "
                       f"repeated {reps}x in {el:.1f} s",
-            "value_1_thread": round(reps1 * inp.T_total / el1, 2)}
+            "value_1_thread": round(reps1 * inp.T_total / el1, 2),
+            "cpu_model": cpu_model(), "affinity_cpus": affinity,
+            "threads_note": f"{cores} threads: the CPU share of a one-GPU box "
+                            f"(min of the affinity mask and {BOX_CPU_SHARE})"}
 
 
 def main():
@@ -304,8 +326,10 @@ def main():
                          "this gate activation) inside the kernels")
     ap.add_argument("--chunk", type=int, default=0,
                     help="tokens per serial state step (16, 32; 0 = library default)")
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="steps timed with a cache-evicting copy between them (0: skip)")
+    ap.add_argument("--warm-steps", type=int, default=50,
+                    help="extra back-to-back steps without flushes, reported as warm (0: skip)")
+    ap.add_argument("--compare-chunk16", type=int, default=1,
+                    help="also time the 16-token chunk path of the same workload (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -378,21 +402,49 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Every timed step starts with the caches flushed: a 1 GiB device copy (a write of 1 GiB)
+    # evicts L2 and the 256 MB MALL, so the step reads its inputs from HBM. Each step is timed
+    # alone with HIP events on the stream it runs on; the flush lies outside the events.
+    flush_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+
+    def flush():
+        flush_dst.copy_(flush_src)
+
+    def flushed_steps(call, n):
+        evs = []
+        for _ in range(n):
+            flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(stream)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
     for _ in range(a.warmup):
+        flush()
         plan(stream)
     torch.cuda.synchronize()
 
-    # the timed region: exactly --steps forwards
+    # the timed region: exactly --steps forwards, each after a cache flush
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        plan(stream)
-    torch.cuda.synchronize()
+    step_ms = flushed_steps(plan, a.steps)
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    ms_per_step = statistics.median(step_ms)
+    srt = sorted(step_ms)
+    pct = lambda f: round(srt[min(len(srt) - 1, int(f * len(srt)))], 5)
+    step_dist = {"p10_ms": pct(0.1), "p50_ms": pct(0.5), "p90_ms": pct(0.9),
+                 "wall_s_with_flushes": round(t1 - t0, 4),
+                 "note": "per-step HIP-event durations of the timed (flushed) steps"}
 
-    # per-kernel durations: the same kernels, one launch per stage, HIP events around each
+    # per-kernel durations: the same kernels, one launch per stage, each step after a flush,
+    # HIP events around each launch on its stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
     for i in range(a.steps):
+        flush()
         ev[i][0].record(stream)
         plan.prepare(stream)
         ev[i][1].record(stream)
@@ -401,44 +453,54 @@ def main():
     torch.cuda.synchronize()
     prep_ms = statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps))
     state_ms = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps))
-    step_ev = sorted(ev[i][0].elapsed_time(ev[i][2]) for i in range(a.steps))
-    pct = lambda f: round(step_ev[min(len(step_ev) - 1, int(f * len(step_ev)))], 5)
-    step_dist = {"p10_ms": pct(0.1), "p50_ms": pct(0.5), "p90_ms": pct(0.9),
-                 "note": "per-step durations of the event-timed pass (events add a few us)"}
 
-    cold = None
-    if a.cold_steps > 0:
-        fa = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        fb = torch.empty_like(fa)
-        cs = []
-        for _ in range(a.cold_steps):
-            fb.copy_(fa)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+    # warm cache, labelled as such: --warm-steps back-to-back forwards with the working set
+    # (inputs, workspace, outputs) left in the MALL, timed by the host clock
+    warm = None
+    if a.warm_steps > 0:
+        torch.cuda.synchronize()
+        tw0 = time.perf_counter()
+        for _ in range(a.warm_steps):
             plan(stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cs.append(e0.elapsed_time(e1))
-        cold_ms = statistics.median(cs)
-        cold = {"ms_per_step_median": round(cold_ms, 5),
-                "tokens_per_s": round(inp.T_total / (cold_ms * 1e-3), 1),
-                "steps": a.cold_steps,
-                "note": "1 GiB device copy between steps evicts L2 and the 256 MB MALL; "
-                        "each step timed alone with HIP events"}
-        del fa, fb
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - tw0) * 1e3 / a.warm_steps
+        warm = {"ms_per_step": round(warm_ms, 5),
+                "tokens_per_s": round(inp.T_total / (warm_ms * 1e-3), 1),
+                "steps": a.warm_steps,
+                "note": "warm cache: back-to-back steps, no flush, host clock around all of them"}
+
+    # the chunk-16 run of the same workload (the FlashKDA tile), timed the same way
+    c16 = None
+    if a.compare_chunk16 and chunk == 32:
+        plan16 = kda.KdaFwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta),
+                                cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0),
+                                chunk=16, **pre)
+        for _ in range(3):
+            plan16(stream)
+        ms16 = statistics.median(flushed_steps(plan16, a.steps))
+        c16 = {"chunk": 16, "ms_per_step": round(ms16, 5),
+               "tokens_per_s": round(inp.T_total / (ms16 * 1e-3), 1),
+               "note": "same workload and timing (flushed, median), 16-token chunks"}
+        del plan16
+    del flush_src, flush_dst
 
     work = algorithmic_work(inp, chunk)
+    # The method's algorithmic FLOPs are counted with 16-token chunks, the chunk length the
+    # pages' kernels use; longer chunks issue more (the 2 C^2 V term) for the same result.
+    work16 = algorithmic_work(inp, 16)
     es = "bf16" if w.dtype == "bf16" else "fp32"
     if chunk != 1:
         kernels = {
             "kda_prepare": {"avg_ms": round(prep_ms, 5), "bound": "hbm",
-                            "alg_bytes": work["prep_bytes"], "alg_flops": work["prep_flops"],
+                            "alg_bytes": work["prep_bytes"], "alg_flops": work16["prep_flops"],
+                            "issued_flops_this_chunk": work["prep_flops"],
                             "achieved_GBs": round(work["prep_bytes"] / (prep_ms * 1e-3) / 1e9,
                                                   1)},
             "kda_state": {"avg_ms": round(state_ms, 5), "bound": "mfma",
-                          "alg_bytes": work["state_bytes"], "alg_flops": work["state_flops"],
-                          "achieved_TFLOPs": round(work["state_flops"] / (state_ms * 1e-3) / 1e12,
-                                                   2)},
+                          "alg_bytes": work["state_bytes"], "alg_flops": work16["state_flops"],
+                          "issued_flops_this_chunk": work["state_flops"],
+                          "achieved_TFLOPs": round(work16["state_flops"] / (state_ms * 1e-3)
+                                                   / 1e12, 2)},
         }
     if chunk == 1:
         # the token recurrence is one kernel (the prepare launch is empty): everything it reads
@@ -452,21 +514,27 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 5),
                 "traffic": committed_traffic("kda_recurrent", w.name)}
     elif state_ms >= prep_ms:
-        ach = work["state_flops"] / (state_ms * 1e-3) / 1e12
+        ach = work16["state_flops"] / (state_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[es]
         roof = {"kernel": "kda_state", "bound": "mfma", "achieved": round(ach, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 5),
-                "traffic": committed_traffic("kda_state", w.name)}
+                "traffic": committed_traffic("kda_state", w.name),
+                "alg_flops_per_launch": work16["state_flops"]}
     else:
         ach = work["prep_bytes"] / (prep_ms * 1e-3) / 1e9
         roof = {"kernel": "kda_prepare", "bound": "hbm", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 5),
-                "traffic": committed_traffic("kda_prepare", w.name)}
+                "traffic": committed_traffic("kda_prepare", w.name),
+                "alg_bytes_per_launch": work["prep_bytes"]}
     path_bytes = work["prep_bytes"] + work["state_bytes"]
     path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
     roof_path = {"bound": "hbm", "achieved": round(path_gbs, 1), "peak": HBM_PEAK_GBS,
                  "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 5),
-                 "alg_bytes_per_step": path_bytes}
+                 "alg_bytes_per_step": path_bytes,
+                 "note": "whole forward, algorithmic bytes / flushed median step time"}
+    if c16 is not None:
+        c16["roofline_path_frac"] = round(path_bytes / (c16["ms_per_step"] * 1e-3) / 1e9
+                                          / HBM_PEAK_GBS, 5)
 
     cpu = None
     if a.cpu_seconds > 0 and not pre:
@@ -481,12 +549,18 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": inp.q.shape[1], "H": w.H, "HV": w.HV,
                    "K": w.K, "V": w.V, "chunk": chunk, "tokens_per_step": inp.T_total,
                    "parallelism": "single-gpu", "prestage": a.prestage,
+                   "timing": "median of per-step HIP-event times, each step after a 1 GiB "
+                             "cache-flushing copy",
+                   "chunk_note": ("the library's default chunk for bf16 io (32 tokens); the "
+                                  "16-token run of the same workload is in chunk16_run"
+                                  if chunk == 32 else ""),
                    "arithmetic": ("fp32 VALU token recurrence" if chunk == 1 else
                                   "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse")},
         "roofline": roof, "roofline_path": roof_path, "kernels": kernels,
-        "kernel_timing": "avg_ms: a second pass of the same steps, each stage launched alone "
-                         "with HIP events around it on its stream",
-        "step_distribution": step_dist, "cold_cache": cold, "cpu_baseline": cpu,
+        "kernel_timing": "avg_ms: a second pass of the same steps, each after a cache flush, "
+                         "each stage launched alone with HIP events around it on its stream",
+        "step_distribution": step_dist, "warm_cache": warm, "chunk16_run": c16,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

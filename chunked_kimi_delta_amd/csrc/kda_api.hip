@@ -8,8 +8,31 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kda_fwd.h"
 #include "kda_internal.h"
+
+namespace kda {
+
+// The compute-unit count only changes with the device, so it is queried once per device
+// ordinal; hipGetDevice is a thread-local read.
+int current_device_cus()
+{
+    constexpr int MAX_DEV = 64, FALLBACK = 256;
+    static std::atomic<int> cached[MAX_DEV];   // 0: not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FALLBACK;
+    int c = dev < MAX_DEV ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (c > 0) return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c <= 0)
+        c = FALLBACK;
+    if (dev < MAX_DEV) cached[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+}  // namespace kda
 
 namespace {
 

@@ -431,6 +431,9 @@ __device__ __forceinline__ void vm_drain() {
 
 // Host-side launchers (defined next to their kernels).
 namespace kda {
+// Compute units of the calling thread's current device, read once per device and cached
+// (kda_api.hip).
+int current_device_cus();
 template <int K, int V> hipError_t launch_prepare_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state_bf16(const FwdParams &p, hipStream_t st);
 // fp32 chunk records from fp32 or (in_bf16) bf16 inputs: WsF32, or WsF32B for the backward

@@ -40,9 +40,7 @@ static hipError_t launch_state32_spw(const FwdParams &p, hipStream_t st)
 template <int K, int V>
 hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int cus = current_device_cus();
     const int64_t slice_wgs = (int64_t)p.seq.N * p.HV * (V / 16);
     if (slice_wgs >= 4LL * cus) return launch_state32_spw<K, V, 4>(p, st);
     if (slice_wgs >= 2LL * cus) return launch_state32_spw<K, V, 2>(p, st);
