@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace kda {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -404,6 +406,130 @@ __device__ __forceinline__ float gate_activation(const Prestage &pre, float x, f
 // 1 / sqrt(sum of squares + eps): the L2-norm factor of a q or k row.
 __device__ __forceinline__ float l2norm_factor(float sumsq) {
     return __builtin_amdgcn_rsqf(sumsq + L2NORM_EPS);
+}
+
+// ----------------------------------------------------------------------------- exact Gram
+
+// The bf16 prepare kernels factor e^{Gam_i - Gam_j} = e^{Gam_i - ref} e^{ref - Gam_j} around a
+// reference token of the chunk. The factors of a block's diagonal Gram products then span
+// e^{+-(decay between the reference and the block's far end)}; beyond 2^{+-FACTOR_SPAN_MAX} (log2
+// units) their fp32 / bf16 hi-lo representation loses the small factor's low bits or
+// overflows, and the block's diagonal products are formed by exact_block_gram instead.
+constexpr float FACTOR_SPAN_MAX = 64.f;
+
+// Lane I of each 16-lane DPP row, broadcast to the whole row (row_newbcast).
+template <int I>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_amdgcn_update_dpp(0.f, x, 0x150 + I, 0xf, 0xf, false);
+}
+
+// One 16-token block's rows of q, k, g as stored in the inputs.
+struct BlockRows {
+    const uint16_t *q, *k, *g;    // element 0 of the block's first token (this head)
+    int64_t qk_stride, g_stride;  // elements between consecutive tokens
+    int nrows;                    // valid rows; later rows read as zero (k = q = 0, g = 0)
+};
+
+// Column step I of exact_block_gram: this lane is column r (its own token) of the block; E
+// carries e^{Gam_I - Gam_r} for I >= r (0 above the diagonal) along the lane's key dims, as the
+// running product of the per-token decays e^{g} of tokens r+1 .. I, broadcast from lane I.
+template <int I>
+__device__ __forceinline__ void exact_gram_step(float (&E)[4], const float (&a)[4],
+                                                const float (&kk)[4], const float (&qq)[4],
+                                                int r, float (&Lp)[16], float (&Mp)[16]) {
+    const float ind = r == I ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        E[e] = fmaf(E[e], row_bcast<I>(a[e]), ind);
+        const float t = E[e] * kk[e];
+        Lp[I] = fmaf(t, row_bcast<I>(kk[e]), Lp[I]);
+        Mp[I] = fmaf(t, row_bcast<I>(qq[e]), Mp[I]);
+    }
+}
+
+template <int... I>
+__device__ __forceinline__ void exact_gram_steps(float (&E)[4], const float (&a)[4],
+                                                 const float (&kk)[4], const float (&qq)[4],
+                                                 int r, float (&Lp)[16], float (&Mp)[16],
+                                                 std::integer_sequence<int, I...>) {
+    (exact_gram_step<I>(E, a, kk, qq, r, Lp, Mp), ...);
+}
+
+// Sums x[4g + i] over the four lane groups g' of a lane's column, keeping rows 4g .. 4g + 3 on
+// lane group g: a reduce-scatter whose result is the C-layout of the 16 x 16 matrix whose
+// column n lane (g', n) holds partial sums of in x[0..15].
+__device__ __forceinline__ f32x4 reduce_scatter_rows(const float (&x)[16], int grp) {
+    const bool hi = grp >= 2, lo = grp & 1;
+    float kept[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float mine = hi ? x[8 + k] : x[k];
+        const float send = hi ? x[k] : x[8 + k];
+        kept[k] = mine + __shfl_xor(send, 32);
+    }
+    f32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float mine = lo ? kept[4 + i] : kept[i];
+        const float send = lo ? kept[i] : kept[4 + i];
+        out[i] = mine + __shfl_xor(send, 16);
+    }
+    return out;
+}
+
+// The diagonal Gram products of one 16-token block, with every decay an exact product of
+// per-token decays (no factorisation, so no exponent range limit): in C-layout,
+//     Lc  = [ sum_d k_i k_j e^{Gam_i - Gam_j} ]_{i >= j}      (the caller keeps i > j, scales by
+//                                                            beta_i)
+//     Mc  = [ sum_d sq_i q_i k_j e^{Gam_i - Gam_j} ]_{i >= j}
+// with i the row (token of the block), j the column, k and q of each token multiplied by rk
+// and sq of that token (the L2-norm factor and, for q, the output scale), and g the activated
+// per-token log decay (the pre-stage gate, when on, applied as in the kernels). Entries above
+// the diagonal are zero. Each lane reloads its own token's q, k, g (TPL, rows past nrows read
+// as zero) one 16-dim tile at a time, so nothing the caller keeps in registers is needed.
+// "手撕KDA" section 1 (naive_chunk_kda) forms the same products with exponents of differences.
+template <int K>
+__device__ __forceinline__ void exact_block_gram(const BlockRows &br, const Prestage &pre, int j,
+                                                 float aexp, float rk, float sq, int lane,
+                                                 f32x4 &Lc, f32x4 &Mc) {
+    const int grp = lane >> 4, r = lane & 15;
+    float Lp[16], Mp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { Lp[i] = 0.f; Mp[i] = 0.f; }
+    auto rows = [&](const uint16_t *base, int64_t stride) {
+        return buffer_rsrc(base, br.nrows > 0 ? (uint32_t)(((int64_t)(br.nrows - 1) * stride +
+                                                             K) * 2)
+                                              : 0u);
+    };
+    const __amdgpu_buffer_rsrc_t rq = rows(br.q, br.qk_stride), rkk = rows(br.k, br.qk_stride),
+                                 rg = rows(br.g, br.g_stride);
+    const bool live = r < br.nrows;
+    const bool gated = pre.gate != 0;
+#pragma unroll 1
+    for (int c = 0; c < K / 16; ++c) {
+        const int col = 16 * c + 4 * grp;
+        const u32x2 qw = bload8(rq, (int)((r * br.qk_stride + col) * 2), 0);
+        const u32x2 kw = bload8(rkk, (int)((r * br.qk_stride + col) * 2), 0);
+        const u32x2 gw = bload8(rg, (int)((r * br.g_stride + col) * 2), 0);
+        float kk[4], qq[4], gv[4], a[4];
+        unpack_bf16x4(make_uint2(kw[0], kw[1]), kk);
+        unpack_bf16x4(make_uint2(qw[0], qw[1]), qq);
+        unpack_bf16x4(make_uint2(gw[0], gw[1]), gv);
+        f32x4 dt = zero4();
+        if (gated && pre.dt_bias) dt = *(const f32x4 *)(pre.dt_bias + (size_t)j * K + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kk[e] *= rk;
+            qq[e] *= sq;
+            float g = gv[e];
+            if (gated) g = live ? gate_activation(pre, g + dt[e], aexp) : 0.f;
+            a[e] = __builtin_amdgcn_exp2f(g * LOG2E);
+        }
+        float E[4] = {0.f, 0.f, 0.f, 0.f};
+        exact_gram_steps(E, a, kk, qq, r, Lp, Mp, std::make_integer_sequence<int, 16>{});
+    }
+    Lc = reduce_scatter_rows(Lp, grp);
+    Mc = reduce_scatter_rows(Mp, grp);
 }
 
 // Workgroup fences that order LDS accesses only. Around s_barrier they make LDS writes visible

@@ -61,6 +61,7 @@ struct Prep32In {
     u32x4 q[K / 32], k[K / 32], g[K / 32], v[V / 32];
     unsigned beta;               // bf16 bits of beta of row lane % 16 (0 past the valid rows)
     int nrows;                   // valid rows of the block (the rest are zero padding)
+    int64_t tok0;                // packed-axis index of the block's first token
 };
 
 // The loads go through a buffer resource whose range ends with the block's last valid row:
@@ -104,6 +105,7 @@ __device__ __forceinline__ void prep32_load(const FwdParams &p, int64_t bos, int
                     nrows > 0 ? (uint32_t)((nrows - 1) * p.HV) * 2u + 2u : 0u);
     in.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, r * p.HV * 2, 0, 0);
     in.nrows = nrows;
+    in.tok0 = tok0;
 }
 
 // Row-contiguous input rows -> TPL (lane (g, r): row r, columns 16c + 4g .. + 3) through this
@@ -298,6 +300,7 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     // lo hi), one 32-column slab at a time. Block a publishes its KI factors; block b also
     // contracts its rows against them (the off-diagonal blocks L_ba, Mqk_ba).
     auto gram_phase = [&]() {
+        float span = 0.f;                    // largest |exponent| of this block's factors
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             bf16x8 kdh, kdl, kih, kil, qdh, qdl;
@@ -317,6 +320,7 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float d1 = gc[i] - ref[i];
+                    span = fmaxf(span, fabsf(d1));
                     const float e1 = __builtin_amdgcn_exp2f(d1);
                     const float e2 = __builtin_amdgcn_exp2f(-d1);
                     const float xd = kk[i] * e1, xi = kk[i] * e2, xq = sc * qq[i] * e1;
@@ -345,6 +349,19 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
                 Lba = mfma32(kdl, ah, Lba);
                 Mba = mfma32(qdl, ah, Mba);
             }
+        }
+        // The factors above are centred on the chunk middle, which bounds every factor of the
+        // off-diagonal block (rows after, columns before the middle) by 1 whatever the decay;
+        // the diagonal block's factors span the decay between the middle and the block's far
+        // end. Beyond FACTOR_SPAN_MAX that block's products are formed from exact per-token
+        // decay products instead (wave-uniform branch; no barrier inside).
+        if (__builtin_amdgcn_ballot_w64(span > FACTOR_SPAN_MAX) != 0) {
+            const int h = j / p.G;
+            const BlockRows br{(const uint16_t *)p.q + (in.tok0 * p.H + h) * K,
+                               (const uint16_t *)p.k + (in.tok0 * p.H + h) * K,
+                               (const uint16_t *)p.g + (in.tok0 * p.HV + j) * K,
+                               (int64_t)p.H * K, (int64_t)p.HV * K, in.nrows};
+            exact_block_gram<K>(br, p.pre, j, aexp, rk, sc, lane, Lacc, Macc);
         }
     };
 

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
                     gl[c][i] = gate_activation(p.pre, gl[c][i] + dtv[c][i], aexp);
         }
     }
+    float rq = 1.f, rk = 1.f;                       // L2-norm factors of this lane's row
     if (p.pre.qk_l2norm) {
         // L2 norm of each token's q and k row: this lane holds a quarter of row r, the three
         // other lane groups the rest
@@ -115,8 +116,8 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
                 sq += qf[c][i] * qf[c][i];
                 sk += kf[c][i] * kf[c][i];
             }
-        const float rq = l2norm_factor(sum_lane_groups(sq));
-        const float rk = l2norm_factor(sum_lane_groups(sk));
+        rq = l2norm_factor(sum_lane_groups(sq));
+        rk = l2norm_factor(sum_lane_groups(sk));
 #pragma unroll
         for (int c = 0; c < NK; ++c)
 #pragma unroll
@@ -145,11 +146,13 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
     const float sc = p.scale;
     float KD[NK][4], QD[NK][4], KRv[NK][4];
     bf16x8 kdh[NS], kdl[NS], kih[NS], kil[NS], qdh[NS], qdl[NS];
+    float span = 0.f;                               // largest |exponent| of a Gram factor
 #pragma unroll
     for (int c = 0; c < NK; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float d1 = G2[c][i] - ref[c][i];
+            span = fmaxf(span, fabsf(d1));
             const float e1 = __builtin_amdgcn_exp2f(d1);
             const float e2 = __builtin_amdgcn_exp2f(-d1);
             const float eA = __builtin_amdgcn_exp2f(G2[c][i]);
@@ -176,6 +179,16 @@ __global__ __launch_bounds__(64) void prepare_bf16_kernel(FwdParams p)
         Macc = mfma32(qdh[st], kil[st], Macc);
         Lacc = mfma32(kdl[st], kih[st], Lacc);
         Macc = mfma32(qdl[st], kih[st], Macc);
+    }
+    // Decays too strong for the centred factors (their exponents span more than
+    // FACTOR_SPAN_MAX): the chunk's Gram products are formed from exact per-token decay
+    // products instead (wave-uniform branch).
+    if (__builtin_amdgcn_ballot_w64(span > FACTOR_SPAN_MAX) != 0) {
+        const BlockRows br{(const uint16_t *)p.q + (bos * p.H + h) * K,
+                           (const uint16_t *)p.k + (bos * p.H + h) * K,
+                           (const uint16_t *)p.g + (bos * p.HV + j) * K,
+                           (int64_t)p.H * K, (int64_t)p.HV * K, nvalid};
+        exact_block_gram<K>(br, p.pre, j, aexp, rk, sc * rq, lane, Lacc, Macc);
     }
     float b4[4], Mq[4];
     f32x4 L, eye;

@@ -84,11 +84,14 @@ typedef struct {
     const void *k;            /* [B, T, H, K]   io dtype                                    */
     const void *v;            /* [B, T, HV, V]  io dtype                                    */
     const void *g;            /* [B, T, HV, K]  io dtype; per-key-dim decay in natural-log
-                                 units (exp(g) multiplies the state). The chunked
-                                 factorisation needs the sum of g over any 8 (chunk 16) or 16
-                                 (chunk 32) consecutive tokens of a chunk to stay above about
-                                 -88 per key dim (fp32 exponent range); chunk 1 and fp32 io have
-                                 no such limit. g <= 0 is expected but not enforced.         */
+                                 units (exp(g) multiplies the state). Any g <= 0 is exact to
+                                 rounding at every chunk length: where a chunk's decay is too
+                                 strong for the bf16 prepare kernels' factorised decay products
+                                 (exponents spanning more than 2^64 between a chunk's
+                                 reference token and its far end, e.g. below about -5.5 per
+                                 token over 8 tokens), they form that chunk's diagonal Gram
+                                 blocks from exact products of per-token decays instead.
+                                 g <= 0 is expected but not enforced.                       */
     const void *beta;         /* [B, T, HV]     io dtype; used as given (no sigmoid)        */
     float scale;              /* output scale; <= 0 or NaN selects K^-0.5                   */
     const int64_t *cu_seqlens;/* device [N + 1] token offsets (cu[0] = 0, nondecreasing,
@@ -108,7 +111,7 @@ typedef struct {
                                  to rounding.                                                */
     /* Pre-stage, fused into the kernels that read the inputs (all zero: inputs used as given;
        "KDA源码剖析之FlashKDA（上）" parts 6, 7 and 10; "手撕KDA" section 2.1). The activated
-       values replace q, k, g, beta everywhere above, including the g limit of `g`.           */
+       values replace q, k, g, beta everywhere above.                                          */
     int32_t qk_l2norm;        /* nonzero: q and k of every token and q/k head are divided by
                                  sqrt(sum over the K dims of the squares + 1e-6)             */
     int32_t beta_sigmoid;     /* nonzero: beta <- 1 / (1 + exp(-beta))                       */
@@ -177,8 +180,8 @@ kda_status kda_fwd_state(const kda_fwd_args *args, void *workspace, size_t ws_by
    2 * B*T * HV * K * 4 bytes when HV > H or the q/k L2 norm is on, plus (B*T/16 + N) * HV *
    (K + 1) * 4 bytes with a gate. Status codes as for kda_fwd; KDA_ERR_UNSUPPORTED also for a
    chunk other than 0 or 16; KDA_ERR_INVALID_ARG also for a missing or misaligned dA_log with
-   a gate. The g limit of fp32 io of the forward applies (none in practice: every exponent the
-   kernels form is a difference of in-chunk cumsums with the later one first). Deterministic
+   a gate. Any g <= 0 is exact to rounding: every exponent the kernels form is a difference
+   of in-chunk cumsums with the later one first. Deterministic
    (fixed-order sums, no atomics). With N = 0 nothing is written.                          */
 size_t kda_bwd_workspace_bytes(const kda_fwd_args *args);
 

@@ -311,7 +311,8 @@ def raw_oracle(raw, pre, units=None):
     cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
     if units is None:
         return kda_recurrent(q, k, f(inp.v), g, beta, inp.scale, h0, cu)
-    return kda_oracle_c(q, k, f(inp.v), g, beta, inp.scale, h0, cu, units=units)
+    return kda_oracle_c(q, k, f(inp.v), g, beta, inp.scale, h0, cu, units=units,
+                        n_threads=ORACLE_THREADS)
 
 
 PRE_SHAPES = {
@@ -374,3 +375,69 @@ def test_prestage_full_size_bounded_gate():
     o_ref, f_ref = raw_oracle(raw, pre, units=units)
     check_all(raw.inp, o.float().cpu().numpy(), fin.cpu().numpy().astype(np.float64), o_ref,
               f_ref, "bf16", units=units)
+
+
+# --------------------------------------------------------------------------- strong gates
+# Decays far beyond what factors centred on a reference token can hold (their exponents
+# would span more than 2^64 within a 16- or 32-token chunk). The kernels then form the
+# diagonal Gram blocks from exact per-token decay products; the result must meet the same bars.
+
+STRONG_G = {
+    # plain log decays of -6.9 .. -18.4 per token and key dim
+    "strong_g": W.custom(B=1, T=100, H=2, HV=2, K=128, V=128, h0_std=0.1, g_lo=1e-8,
+                         g_hi=1e-3),
+    # per-dim decays from almost none to -13.8 per token: chunks and blocks of both kinds
+    "mixed_g": W.custom(B=2, T=77, H=1, HV=2, K=128, V=128, g_lo=1e-6, g_hi=0.999),
+    "strong_g_k64_varlen": W.custom(H=1, HV=2, K=64, V=64, h0_std=0.1, g_lo=1e-8, g_hi=1e-3,
+                                    lengths=(0, 5, 16, 33, 70)),
+}
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("name", list(STRONG_G))
+def test_strong_decay_parity(name, chunk):
+    w = STRONG_G[name]
+    inp = W.make_inputs(w, seed=31)
+    o, fin = gpu_run(inp, chunk=chunk)
+    o_ref, f_ref = oracle_run(inp)
+    check_all(inp, o, fin, o_ref, f_ref, w.dtype, what=f"{name} chunk {chunk}")
+
+
+# gate parameters for strong activated decays: the softplus gate with exp(A_log) = 8 and raw
+# gate inputs ~ N(2, 1) (about -17 per token); the bounded gate at lower bound -5 with raw
+# inputs ~ N(3, 1) (close to -5 per token, -80 over 16 tokens)
+STRONG_PRE = {
+    "softplus_A8": (dict(g_mean=2.0, A_lo=7.99, A_hi=8.01), {"gate": "softplus"}),
+    "bounded_lb5": (dict(g_mean=3.0), {"gate": "bounded", "lb": -5.0}),
+}
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("case", list(STRONG_PRE))
+def test_strong_gate_parity(case, chunk):
+    kw, gate = STRONG_PRE[case]
+    w = W.custom(B=2, T=90, H=2, HV=4, K=128, V=128, h0_std=0.1)
+    raw = W.make_raw_inputs(w, seed=32, **kw)
+    pre = {"l2": True, "sig": True, **gate}
+    o, fin = raw_plan(raw, chunk, pre)()
+    torch.cuda.synchronize()
+    o_ref, f_ref = raw_oracle(raw, pre)
+    check_all(raw.inp, o.float().cpu().numpy(), fin.cpu().numpy().astype(np.float64), o_ref,
+              f_ref, "bf16", what=f"{case} chunk {chunk}")
+
+
+@pytest.mark.parametrize("chunk", [32, 16])
+@pytest.mark.parametrize("case", list(STRONG_PRE))
+def test_strong_gate_full_size_every_unit(case, chunk):
+    # the throughput shape with raw inputs and a strong gate: every chunk takes the exact
+    # diagonal path; every unit and row against the oracle
+    kw, gate = STRONG_PRE[case]
+    w = W.WORKLOADS["h16_t4096"]
+    raw = W.make_raw_inputs(w, seed=0, **kw)
+    pre = {"l2": True, "sig": True, **gate}
+    o, fin = raw_plan(raw, chunk, pre)()
+    torch.cuda.synchronize()
+    units = [(0, j) for j in range(w.HV)]
+    o_ref, f_ref = raw_oracle(raw, pre, units=units)
+    check_all(raw.inp, o.float().cpu().numpy(), fin.cpu().numpy().astype(np.float64), o_ref,
+              f_ref, "bf16", units=units, what=f"{case} chunk {chunk}")
