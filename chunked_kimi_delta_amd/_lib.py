@@ -7,7 +7,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libkda_fwd.so"
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+(KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP,
+ KDA_ERR_NOALLOC_TOO_LARGE) = range(6)
+KDA_NOALLOC_WORKSPACE_BYTES = 128 << 20
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_GATE_NONE, KDA_GATE_SOFTPLUS, KDA_GATE_BOUNDED = 0, 1, 2
 
@@ -57,6 +59,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes = lib.kda_fwd.argtypes
         f.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = [ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_bwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaFwdArgs)]
     lib.kda_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_bwd.argtypes = ([ctypes.POINTER(KdaFwdArgs), ctypes.c_void_p, ctypes.c_void_p,

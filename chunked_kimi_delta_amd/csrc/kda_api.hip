@@ -349,10 +349,13 @@ const char *kda_strerror(int status)
                "gate 0, 1 or 2; the backward: chunk 16)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
+    case KDA_ERR_NOALLOC_TOO_LARGE:
+        return "shapes need more workspace than kda_fwd_noalloc's static device array "
+               "(KDA_NOALLOC_WORKSPACE_BYTES = 128 MiB)";
     default: return "unknown status";
     }
 }
 
-int kda_version(void) { return 104; }
+int kda_version(void) { return 105; }
 
 }  // extern "C"

@@ -47,7 +47,9 @@ typedef enum {
                                  unknown gate                                                */
     KDA_ERR_WORKSPACE = 3,    /* workspace NULL, misaligned, or smaller than
                                  kda_fwd_workspace_bytes() / kda_bwd_workspace_bytes()       */
-    KDA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError)                    */
+    KDA_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError)                    */
+    KDA_ERR_NOALLOC_TOO_LARGE = 5  /* kda_fwd_noalloc: these shapes need more workspace than
+                                      KDA_NOALLOC_WORKSPACE_BYTES                             */
 } kda_status;
 
 typedef enum {
@@ -188,6 +190,21 @@ size_t kda_bwd_workspace_bytes(const kda_fwd_args *args);
 kda_status kda_bwd(const kda_fwd_args *args, const void *d_o, const float *dht,
                    void *workspace, size_t ws_bytes, float *dq, float *dk, float *dv, float *dg,
                    float *dbeta, float *dh0, float *dA_log, float *ddt_bias, void *stream);
+
+/* ---------------------------------------------------------------------------- no allocation
+   For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc. kda_fwd_noalloc is kda_fwd
+   with the workspace taken from a static device array of KDA_NOALLOC_WORKSPACE_BYTES that the
+   library holds on every device it runs on until the process ends; it calls no allocating
+   routine. Same arguments (no workspace), checks, results and status codes as kda_fwd, plus
+   KDA_ERR_NOALLOC_TOO_LARGE when kda_fwd_workspace_bytes(args) exceeds the array (128 MiB:
+   for example 16 value heads of up to about 7,700 tokens at bf16 io; chunk 1 needs none, so
+   decoding steps have no limit). The work runs on the calling thread's current device and
+   uses that device's array. Every call on one device shares that array: calls whose work
+   overlaps on one device (several streams or threads) race on it, so the caller serialises
+   them (one stream, or events between them). The array's contents on entry do not matter. */
+#define KDA_NOALLOC_WORKSPACE_BYTES ((size_t)128 << 20)
+kda_status kda_fwd_noalloc(const kda_fwd_args *args, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_strerror(int status);

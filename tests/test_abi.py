@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["kda_bwd", "kda_bwd_workspace_bytes", "kda_fwd",
-                                    "kda_fwd_prepare", "kda_fwd_state",
+                                    "kda_fwd_noalloc", "kda_fwd_prepare", "kda_fwd_state",
                                     "kda_fwd_workspace_bytes", "kda_strerror", "kda_version"]
 
 
@@ -118,7 +118,7 @@ def test_strerror_and_version(lib):
     for st in range(5):
         assert kda._lib.strerror(st)
     assert "unknown" in kda._lib.strerror(99)
-    assert lib.kda_version() == 104
+    assert lib.kda_version() == 105
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):
@@ -216,3 +216,15 @@ def test_kda_bwd_rejects_bad_arguments(lib):
     assert call(args(T=32, N=2), do=fake) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_bwd(None, None, None, None, 0, *([None] * 8), None) == \
         _lib.KDA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_before_any_device_work(lib):
+    # both rejections return before the entry point touches a device
+    assert lib.kda_fwd_noalloc(None, None) == _lib.KDA_ERR_INVALID_ARG
+    big = args(B=1, T=131072, N=1, H=32, HV=32, chunk=32)
+    assert lib.kda_fwd_workspace_bytes(ctypes.byref(big)) > _lib.KDA_NOALLOC_WORKSPACE_BYTES
+    assert lib.kda_fwd_noalloc(ctypes.byref(big), None) == _lib.KDA_ERR_NOALLOC_TOO_LARGE
+    assert "static device array" in lib.kda_strerror(_lib.KDA_ERR_NOALLOC_TOO_LARGE).decode()
+    # the array holds the throughput workload's records (16 heads x 4096 tokens, chunk 32)
+    assert lib.kda_fwd_workspace_bytes(ctypes.byref(args(chunk=32))) <= \
+        _lib.KDA_NOALLOC_WORKSPACE_BYTES
