@@ -487,7 +487,7 @@ def main():
 
     # the chunk-16 run of the same workload (the FlashKDA tile), timed the same way
     c16 = None
-    if a.compare_chunk16 and chunk == 32:
+    if a.compare_chunk16 and chunk in (32, 64):
         plan16 = kda.KdaFwdPlan(d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta),
                                 cu_seqlens=d(inp.cu_seqlens), initial_state=d(inp.h0),
                                 chunk=16, **pre)

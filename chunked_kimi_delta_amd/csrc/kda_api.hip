@@ -66,13 +66,16 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     int ct = a->chunk;
     if (ct == 0)            // default: the token recurrence for short dense batches (decode)
         ct = (!a->cu_seqlens && a->T <= 16) ? 1 : (a->io == KDA_BF16 ? 32 : 16);
-    if (ct != 1 && ct != 16 && !(ct == 32 && a->io == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if (ct != 1 && ct != 16 && !((ct == 32 || ct == 64) && a->io == KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
     const int64_t tt = (int64_t)a->B * a->T;
-    const int64_t ns = tt / ct + a->N;
-    if (ns > INT32_MAX || (int64_t)a->HV > 65535) return KDA_ERR_UNSUPPORTED;
+    const int64_t ns = tt / ct + a->N;    // chunk slots (for chunk 64: pairs of 32-token chunks)
+    if (2 * ns > INT32_MAX || (int64_t)a->HV > 65535) return KDA_ERR_UNSUPPORTED;
     size_t cb;
     if (ct == 1)
         cb = 0;                      // the token-recurrent kernel needs no workspace
+    else if (a->io == KDA_BF16 && ct == 64)
+        cb = 2 * record_bytes<WsPair>(a->K, a->V);      // two 32-token records per slot
     else if (a->io == KDA_BF16)
         cb = ct == 32 ? record_bytes<WsBf16x32>(a->K, a->V) : record_bytes<WsBf16>(a->K, a->V);
     else
@@ -108,6 +111,10 @@ hipError_t dispatch(const FwdParams &p, int io, int chunk, int stages, hipStream
     if (chunk == 1)     // token-recurrent: no prepare stage
         return (stages & STAGE_STATE) ? launch_recurrent<K, V>(p, io, st) : hipSuccess;
     const bool prep = (stages & STAGE_PREPARE) && p.seq.T_total > 0;
+    if (io == KDA_BF16 && chunk == 64) {
+        if (prep && (e = launch_prepare64_bf16<K, V>(p, st)) != hipSuccess) return e;
+        return (stages & STAGE_STATE) ? launch_state64_bf16<K, V>(p, st) : hipSuccess;
+    }
     if (io == KDA_BF16 && chunk == 32) {
         if (prep && (e = launch_prepare32_bf16<K, V>(p, st)) != hipSuccess) return e;
         return (stages & STAGE_STATE) ? launch_state32_bf16<K, V>(p, st) : hipSuccess;
@@ -345,8 +352,8 @@ const char *kda_strerror(int status)
     case KDA_OK: return "ok";
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED:
-        return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 with bf16 io; "
-               "gate 0, 1 or 2; the backward: chunk 16)";
+        return "unsupported configuration (K, V in {64, 128}; chunk 1, 16, or 32 / 64 with bf16 "
+               "io; gate 0, 1 or 2; the backward: chunk 16)";
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
     case KDA_ERR_NOALLOC_TOO_LARGE:

@@ -141,6 +141,21 @@ struct WsBf16x32 {
     static constexpr int BYTES = (END + 255) / 256 * 256;
 };
 
+// The 64-token step of the state kernel reads the records of two consecutive 32-token chunks
+// (c, c + 1) of one sequence, stored side by side, each a WsBf16x32 record followed by
+//   PT   [2 blocks][64][8] fp16   (second chunk only) P = W_{c+1} KR_c^T (32 x 32) as the
+//                                 16x16x32 A operand of each row block, the reduction pairing
+//                                 chunk c's blocks as in WsBf16x32
+// and the second chunk's W is stored scaled by e^{gam_c} per key dim, so that
+//     delta_{c+1} = U_{c+1} - (W_{c+1} diag(e^{gam_c})) S_c - P delta_c
+// needs only the state at the start of the pair.
+template <int K, int V>
+struct WsPair {
+    static constexpr int PT = WsBf16x32<K, V>::END;
+    static constexpr int END = PT + 2048;
+    static constexpr int BYTES = (END + 255) / 256 * 256;
+};
+
 // Workspace of one chunk, fp32 io: plain row-major fp32 arrays.
 //   W [16][K], QD [16][K], KR [16][K], U [16][V], MQK [16][16], EG [K]
 template <int K, int V>
@@ -423,6 +438,23 @@ __device__ __forceinline__ float row_bcast(float x) {
     return __builtin_amdgcn_update_dpp(0.f, x, 0x150 + I, 0xf, 0xf, false);
 }
 
+// e^{gam} of the state rows a lane holds, for NT 16-row tiles: `raw` is one 16-byte load in
+// which lane (g, n) read the four values of tile n % NT for its lane group g (rows
+// 16 t + 4 g .. + 3); tile t's values are then broadcast from lane (g, t) to the row. One
+// load of 256 distinct bytes per NT tiles instead of NT loads that each fetch 64 lanes x 16 B
+// for 64 distinct bytes.
+template <int... T>
+__device__ __forceinline__ void expand_rows_impl(u32x4 raw, f32x4 (&eg)[sizeof...(T)],
+                                                 std::integer_sequence<int, T...>) {
+    const f32x4 x = __builtin_bit_cast(f32x4, raw);
+    ((eg[T] = f32x4{row_bcast<T>(x[0]), row_bcast<T>(x[1]), row_bcast<T>(x[2]),
+                    row_bcast<T>(x[3])}), ...);
+}
+template <int NT>
+__device__ __forceinline__ void expand_rows(u32x4 raw, f32x4 (&eg)[NT]) {
+    expand_rows_impl(raw, eg, std::make_integer_sequence<int, NT>{});
+}
+
 // One 16-token block's rows of q, k, g as stored in the inputs.
 struct BlockRows {
     const uint16_t *q, *k, *g;    // element 0 of the block's first token (this head)
@@ -505,28 +537,39 @@ __device__ __forceinline__ void exact_block_gram(const BlockRows &br, const Pres
                                  rg = rows(br.g, br.g_stride);
     const bool live = r < br.nrows;
     const bool gated = pre.gate != 0;
+    // this lane's q, k, g (bf16 pairs) and dt_bias of one 16-dim tile; the next tile's are
+    // loaded while the current one is consumed (the index is clamped to the last tile, so every
+    // load stays inside its row and dt_bias stays inside its array)
+    struct Tile { u32x2 q, k, g; f32x4 dt; };
+    auto load = [&](int c) {
+        const int col = 16 * c + 4 * grp;
+        Tile t;
+        t.q = bload8(rq, (int)((r * br.qk_stride + col) * 2), 0);
+        t.k = bload8(rkk, (int)((r * br.qk_stride + col) * 2), 0);
+        t.g = bload8(rg, (int)((r * br.g_stride + col) * 2), 0);
+        t.dt = gated && pre.dt_bias ? *(const f32x4 *)(pre.dt_bias + (size_t)j * K + col)
+                                    : zero4();
+        return t;
+    };
+    Tile cur = load(0);
 #pragma unroll 1
     for (int c = 0; c < K / 16; ++c) {
-        const int col = 16 * c + 4 * grp;
-        const u32x2 qw = bload8(rq, (int)((r * br.qk_stride + col) * 2), 0);
-        const u32x2 kw = bload8(rkk, (int)((r * br.qk_stride + col) * 2), 0);
-        const u32x2 gw = bload8(rg, (int)((r * br.g_stride + col) * 2), 0);
+        const Tile nxt = load(c + 1 < K / 16 ? c + 1 : c);
         float kk[4], qq[4], gv[4], a[4];
-        unpack_bf16x4(make_uint2(kw[0], kw[1]), kk);
-        unpack_bf16x4(make_uint2(qw[0], qw[1]), qq);
-        unpack_bf16x4(make_uint2(gw[0], gw[1]), gv);
-        f32x4 dt = zero4();
-        if (gated && pre.dt_bias) dt = *(const f32x4 *)(pre.dt_bias + (size_t)j * K + col);
+        unpack_bf16x4(make_uint2(cur.k[0], cur.k[1]), kk);
+        unpack_bf16x4(make_uint2(cur.q[0], cur.q[1]), qq);
+        unpack_bf16x4(make_uint2(cur.g[0], cur.g[1]), gv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             kk[e] *= rk;
             qq[e] *= sq;
             float g = gv[e];
-            if (gated) g = live ? gate_activation(pre, g + dt[e], aexp) : 0.f;
+            if (gated) g = live ? gate_activation(pre, g + cur.dt[e], aexp) : 0.f;
             a[e] = __builtin_amdgcn_exp2f(g * LOG2E);
         }
         float E[4] = {0.f, 0.f, 0.f, 0.f};
         exact_gram_steps(E, a, kk, qq, r, Lp, Mp, std::make_integer_sequence<int, 16>{});
+        cur = nxt;
     }
     Lc = reduce_scatter_rows(Lp, grp);
     Mc = reduce_scatter_rows(Mp, grp);
@@ -569,6 +612,8 @@ hipError_t launch_prepare_f32(const FwdParams &p, hipStream_t st, bool in_bf16 =
 template <int K, int V> hipError_t launch_state_f32(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_state32_bf16(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_prepare64_bf16(const FwdParams &p, hipStream_t st);
+template <int K, int V> hipError_t launch_state64_bf16(const FwdParams &p, hipStream_t st);
 template <int K, int V> hipError_t launch_recurrent(const FwdParams &p, int io, hipStream_t st);
 template <int K, int V>
 hipError_t launch_backward(const BwdParams &b, bool in_bf16, hipStream_t st);

@@ -53,6 +53,15 @@ struct Prep32Share {
     }
 };
 
+// Carried from the first to the second chunk of a 64-token pair (one workgroup processes both,
+// in order): the first chunk's KR in TPL (fp16, one 16x16x32 operand per 32-dim slab and block)
+// and its e^{gam}.
+template <int K>
+struct PairStash {
+    f16x8 kr0[2][K / 32][64];
+    float eg0[K];
+};
+
 // Inputs of one 32-token chunk as each lane loads them: the 16 rows of its block (wave)
 // row-contiguously, 16 bytes per lane (row RPI u + lane / CPR, 8 columns from 8 (lane % CPR)),
 // so that every quarter-wave reads one or two whole cache lines.
@@ -134,11 +143,25 @@ __device__ __forceinline__ void rows_to_tpl(const u32x4 (&x)[RL / 32], uint2 (&o
 // their L2 norms (pre-stage); the factor of each token's row is applied in fp32 wherever q or
 // k is unpacked, so the bf16 inputs are not rounded again. A gate activation (pre-stage) is
 // applied to g before the cumsum, to valid rows only (padding rows keep g = 0).
-template <int K, int V, bool NORM = false, int AUX = 0>
+//
+// PAIR: 0 for a stand-alone 32-token record; 1 and 2 for the first and second chunk of a
+// 64-token pair (WsPair records, the state kernel's 64-token step). The first chunk also leaves
+// its KR (TPL) and e^{gam} in `ps`; the second stores its W scaled by the first chunk's e^{gam}
+// per key dim and the 32 x 32 product P = W KR_first^T as the A operand of the state kernel's
+// delta correction (WsPair::PT).
+//
+// `after_inputs` runs as soon as this chunk's inputs have arrived (the caller issues the next
+// chunk's loads there, so they stream in while this chunk is processed instead of competing
+// with this chunk's own loads).
+struct NoOp {
+    __device__ void operator()() const {}
+};
+
+template <int K, int V, bool NORM = false, int AUX = 0, int PAIR = 0, class AFTER = NoOp>
 __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, V> &sh,
-                                             const Prep32In<K, V> &in,
+                                             PairStash<K> *ps, const Prep32In<K, V> &in,
                                              __amdgpu_buffer_rsrc_t wr, int j, int wave,
-                                             int lane)
+                                             int lane, AFTER after_inputs = NoOp())
 {
     constexpr int NK = K / 16, NV = V / 16, NS = K / 32;
     using WS = WsBf16x32<K, V>;
@@ -167,6 +190,7 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     rows_to_tpl<K>(in.k, kr, stage, lane);
     rows_to_tpl<K>(in.q, qr, stage, lane);
     rows_to_tpl<V>(in.v, vraw, stage, lane);
+    after_inputs();
     float beta_r = bf16_bits_to_f32((uint16_t)in.beta);
     if (p.pre.beta_sigmoid && r < in.nrows) beta_r = sigmoid_f(beta_r);   // pre-stage
     // L2-norm factors of this lane's token row (its other columns are in the three other lane
@@ -255,6 +279,7 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             float QD[2][4];
+            f16x4 krh[2];                    // this slab's KR tiles in TPL (fp16)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int c = 2 * st + u;
@@ -277,9 +302,11 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
                     KRv[i] = kk[i] * eR;
                 }
                 kdC[c] = to_bf16x4(mfma16(to_bf16x4(KD), Ib, zero4()));
+                krh[u] = to_f16x4(KRv);
                 bstore8<AUX>(wr, lane * 16 + wave * 8, WS::KR + c * 1024,
-                             to_f16x4(mfma16(to_f16x4(KRv), Ih, zero4())));
+                             to_f16x4(mfma16(krh[u], Ih, zero4())));
             }
+            if constexpr (PAIR == 1) ps->kr0[wave][st][lane] = cat(krh[0], krh[1]);
             bstore16<AUX>(wr, lane * 16, WS::QD + (wave * NS + st) * 1024,
                           cat(to_f16x4(QD[0]), to_f16x4(QD[1])));
         }
@@ -291,6 +318,7 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(gc[i]);
                 bstore16<AUX>(wr, grp * 16, WS::EG + 64 * c, e);
+                if constexpr (PAIR == 1) *(f32x4 *)&ps->eg0[16 * c + 4 * grp] = e;
             }
         }
     };
@@ -419,12 +447,27 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
     for (int i = 0; i < 4; ++i) AT[i] = INV[i] * b4[i];     // C(A_xx^T) = diag(beta) X_xx^T
     const bf16x4 ATb = to_bf16x4(AT);
     const f16x4 MqT = to_f16x4(mfma16(to_f16x4(Mq), Ih, zero4()));   // C(Mqk_xx^T)
+    // W rows of this block, slab st, from the two TPL tiles t0, t1 (fp32). The second chunk of
+    // a pair also contracts them against the first chunk's KR (C(P^T) for both of its blocks)
+    // and stores them scaled by the first chunk's e^{gam} per key dim.
+    f32x4 Pa = zero4(), Pb = zero4();
+    auto store_w = [&](int st, f32x4 t0, f32x4 t1) {
+        const f16x8 wf = cat(to_f16x4(t0), to_f16x4(t1));
+        if constexpr (PAIR == 2) {
+            Pa = mfma32(ps->kr0[0][st][lane], wf, Pa);
+            Pb = mfma32(ps->kr0[1][st][lane], wf, Pb);
+            const f32x4 e0 = *(const f32x4 *)&ps->eg0[32 * st + 4 * grp];
+            const f32x4 e1 = *(const f32x4 *)&ps->eg0[32 * st + 16 + 4 * grp];
+            bstore16<AUX>(wr, lane * 16, WS::W + (wave * NS + st) * 1024,
+                          cat(to_f16x4(t0 * e0), to_f16x4(t1 * e1)));
+        } else {
+            bstore16<AUX>(wr, lane * 16, WS::W + (wave * NS + st) * 1024, wf);
+        }
+    };
     if (wave == 0) {
 #pragma unroll
         for (int st = 0; st < NS; ++st)
-            bstore16<AUX>(wr, lane * 16, WS::W + st * 1024,
-                          cat(to_f16x4(mfma16(kdC[2 * st], ATb, zero4())),
-                              to_f16x4(mfma16(kdC[2 * st + 1], ATb, zero4()))));
+            store_w(st, mfma16(kdC[2 * st], ATb, zero4()), mfma16(kdC[2 * st + 1], ATb, zero4()));
 #pragma unroll
         for (int c = 0; c < NV; ++c)
             bstore8<AUX>(wr, lane * 16, WS::NU + c * 1024,
@@ -443,12 +486,10 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
         const bf16x8 Arow = cat(ABTb, ATb);                  // [A_ba | A_bb] as A (16 x 32)
 #pragma unroll
         for (int st = 0; st < NS; ++st)
-            bstore16<AUX>(
-                wr, lane * 16, WS::W + (NS + st) * 1024,
-                cat(to_f16x4(mfma32(cat(sh.u.ph.a.cols.kdc[2 * st][lane], kdC[2 * st]), Arow,
-                                    zero4())),
-                    to_f16x4(mfma32(cat(sh.u.ph.a.cols.kdc[2 * st + 1][lane], kdC[2 * st + 1]),
-                                    Arow, zero4()))));
+            store_w(st,
+                    mfma32(cat(sh.u.ph.a.cols.kdc[2 * st][lane], kdC[2 * st]), Arow, zero4()),
+                    mfma32(cat(sh.u.ph.a.cols.kdc[2 * st + 1][lane], kdC[2 * st + 1]), Arow,
+                           zero4()));
 #pragma unroll
         for (int c = 0; c < NV; ++c)
             bstore8<AUX>(wr, lane * 16 + 8, WS::NU + c * 1024,
@@ -456,6 +497,12 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
         const f16x4 MqbaT = to_f16x4(mfma16(to_f16x4(Mba), Ih, zero4()));  // C(Mqk_ba^T)
         bstore16<AUX>(wr, lane * 16, WS::MQKB, cat(MqbaT, MqT));
     }
+    // C(P_{x,a}^T), C(P_{x,b}^T) side by side: lane (g, n) holds row n of this block's P
+    // against tokens 4g .. 4g + 3 of the first chunk's blocks a and b, the 16x16x32 A operand
+    // that pairs with the first chunk's delta in the state kernel
+    if constexpr (PAIR == 2)
+        bstore16<AUX>(wr, lane * 16, WsPair<K, V>::PT + wave * 1024,
+                      cat(to_f16x4(Pa), to_f16x4(Pb)));
 }
 
 }  // namespace kda

@@ -67,7 +67,9 @@ def test_workspace_bytes(lib):
     assert f(args(io=1, chunk=32)) == 0                   # fp32 io: 16-token chunks only
     assert f(args(chunk=1)) == 0 and f(args(io=1, chunk=1)) == 0   # recurrent: no workspace
     assert f(args(T=16, chunk=0)) == 0 and f(args(T=17, chunk=0)) > 0   # default, short batch
-    assert f(args(chunk=64)) == 0
+    assert f(args(chunk=64)) == (4096 // 64 + 1) * 16 * 2 * 36864   # pairs of 32-token records
+    assert f(args(io=1, chunk=64)) == 0                   # fp32 io: 16-token chunks only
+    assert f(args(chunk=128)) == 0
     assert f(args(K=96)) == 0          # unsupported head dim
     assert f(args(HV=24, H=16)) == 0   # HV % H != 0
     assert f(args(N=2)) == 0           # dense batch needs N == B

@@ -142,8 +142,8 @@ def test_detector_finds_a_load_then_full_wait():
 # Forward kernels: their loads are issued unconditionally and converted where they are used,
 # so no load is waited for on the spot (a load under a per-row branch, or a conversion next to
 # it, had serialised the prepare and token-recurrence load phases).
-FORWARD_SOURCES = ("kda_prepare32.hip", "kda_state32.hip", "kda_recurrent.hip", "kda_prepare.hip",
-                   "kda_state.hip")
+FORWARD_SOURCES = ("kda_prepare32.hip", "kda_state32.hip", "kda_state64.hip",
+                   "kda_recurrent.hip", "kda_prepare.hip", "kda_state.hip")
 
 
 @pytest.mark.skipif(not HAVE_HIPCC, reason="hipcc not available")

@@ -22,7 +22,8 @@ from oracle.chunked import chunk_prepare
 from oracle.native import kda_oracle_c
 from errlog import report_named
 from parity_check import TOL, check_outputs, rel_l2
-from ws_decode import chunk_bytes, chunk_bytes32, decode_chunk, decode_chunk32
+from ws_decode import (chunk_bytes, chunk_bytes32, decode_chunk, decode_chunk32,
+                       decode_pair, pair_bytes)
 
 import chunked_kimi_delta_amd as kda
 
@@ -95,7 +96,7 @@ SMALL = {
 
 
 # chunk lengths the library offers per io dtype (0 = its default)
-CHUNKS = {"bf16": [1, 16, 32], "fp32": [1, 16]}
+CHUNKS = {"bf16": [1, 16, 32, 64], "fp32": [1, 16]}
 SMALL_CASES = [(n, c) for n in SMALL for c in CHUNKS[SMALL[n].dtype]]
 
 
@@ -108,8 +109,8 @@ def test_small_parity(name, chunk):
     check_all(inp, o, fin, o_ref, f_ref, w.dtype, what=f"{name} chunk {chunk}")
 
 
-@pytest.mark.parametrize("io,chunk", [("bf16", 1), ("bf16", 16), ("bf16", 32), ("fp32", 1),
-                                      ("fp32", 16)])
+@pytest.mark.parametrize("io,chunk", [("bf16", 1), ("bf16", 16), ("bf16", 32), ("bf16", 64),
+                                      ("fp32", 1), ("fp32", 16)])
 def test_empty_sequences_carry_initial_state(io, chunk):
     w = W.custom(B=2, T=0, H=1, HV=2, K=128, V=64, dtype=io, h0_std=1.0)
     inp = W.make_inputs(w, seed=3)
@@ -118,7 +119,7 @@ def test_empty_sequences_carry_initial_state(io, chunk):
     assert np.array_equal(fin, inp.h0.numpy().astype(np.float64))
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 @pytest.mark.parametrize("case", ["beta0", "g0"])
 def test_degenerate_gates(case, chunk):
     w = W.custom(B=1, T=90, H=2, HV=2, K=128, V=128, h0_std=0.5)
@@ -133,7 +134,7 @@ def test_degenerate_gates(case, chunk):
         assert rel_l2(fin[0], np.exp(cum)[:, :, None] * S0[0]) <= 1e-3
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 def test_deltanet_retrieval_property(chunk):
     # g = 0, beta = 1 and one fixed unit key shared by all tokens with q = k: each output
     # returns scale * v_t (the plain delta rule overwrites the memory slot every token)
@@ -155,7 +156,7 @@ def test_deltanet_retrieval_property(chunk):
     assert rel_l2(o[0, :, 0], 0.5 * nk2 * inp.v.float().numpy()[0, :, 0]) <= 2e-2
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 def test_no_final_state_and_explicit_scale(chunk):
     w = W.custom(B=1, T=64, H=1, HV=2, K=128, V=128)
     inp = W.make_inputs(w, seed=2)
@@ -165,7 +166,7 @@ def test_no_final_state_and_explicit_scale(chunk):
     assert rel_l2(o, o_ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 def test_deterministic_and_repeatable(chunk):
     w = W.custom(B=1, T=300, H=2, HV=2, K=128, V=128, h0_std=0.1)
     inp = W.make_inputs(w, seed=4)
@@ -222,6 +223,44 @@ def test_prepare32_workspace_matches_chunk_oracle():
                 assert err <= 1e-2, f"head {j} chunk {c} {key}: rel L2 {err:.2e}"
 
 
+def test_prepare64_workspace_matches_chunk_oracle():
+    # stage-1 diagnostics of the 64-token pair records: the first record of each pair is the
+    # 32-token record of its chunk; the second holds its chunk's record with W scaled by the
+    # first chunk's e^{gam} per key dim and P = W_second KR_first^T; a pair whose second chunk
+    # is empty carries the identity step there
+    w = W.custom(B=1, T=150, H=1, HV=2, K=128, V=128)
+    inp = W.make_inputs(w, seed=9)
+    plan = gpu_plan(inp, chunk=64)
+    plan()
+    torch.cuda.synchronize()
+    ws = plan.workspace.cpu().numpy()
+    pb = pair_bytes(128, 128)
+    n_pairs = 150 // 64 + 1
+    f = W.as_f32_numpy
+    for j in range(2):
+        prep = chunk_prepare(f(inp.q)[0, :, 0], f(inp.k)[0, :, 0], f(inp.v)[0, :, j],
+                             f(inp.g)[0, :, j], f(inp.beta)[0, :, j], inp.scale, 32)
+        nch = len(prep["w"])                       # 5 chunks of 32 tokens, the last ragged
+        for m in range(n_pairs):
+            off = (j * n_pairs + m) * 2 * pb
+            first, second = decode_pair(ws[off:off + 2 * pb], 128, 128)
+            c0, c1 = 2 * m, 2 * m + 1
+            for key in ("w", "qd", "kr", "u", "Mqk", "eg"):
+                err = rel_l2(first[key], prep[key][c0])
+                assert err <= 1e-2, f"head {j} chunk {c0} {key}: rel L2 {err:.2e}"
+            if c1 >= nch:                          # empty second chunk: the identity step
+                for key in ("w", "qd", "kr", "u", "Mqk", "P"):
+                    assert not np.any(second[key]), key
+                assert np.all(second["eg"] == 1.0)
+                continue
+            ref = {k: prep[k][c1] for k in prep}
+            ref["w"] = prep["w"][c1] * prep["eg"][c0][None, :]
+            ref["P"] = prep["w"][c1] @ prep["kr"][c0].T
+            for key in ("w", "qd", "kr", "u", "Mqk", "eg", "P"):
+                err = rel_l2(second[key], ref[key])
+                assert err <= 1e-2, f"head {j} chunk {c1} {key}: rel L2 {err:.2e}"
+
+
 FULL = ["h16_t4096", "varlen8_h32", "gva_b4_t8192", "long_t131072"]
 _FULL_CACHE: dict = {}
 
@@ -237,7 +276,7 @@ def full_case(name):
     return _FULL_CACHE[name]
 
 
-@pytest.mark.parametrize("chunk", [32, 16, 1])
+@pytest.mark.parametrize("chunk", [64, 32, 16, 1])
 @pytest.mark.parametrize("name", FULL)          # outermost: one oracle run per workload
 def test_full_size_every_unit(name, chunk):
     inp, (o_ref, f_ref) = full_case(name)
@@ -256,7 +295,7 @@ def test_full_size_fp32_every_unit(chunk):
     check_all(inp, o, fin, o_ref, f_ref, "fp32", what=f"h16_t4096_fp32 chunk {chunk}")
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_prepare_records_repeat_bitwise_full_size(chunk):
     # every chunk record of the h16_t4096 workload, written twice into a zeroed workspace, is
     # the same bits both times (a lost or torn record store shows up as a difference)
@@ -341,7 +380,7 @@ def test_prestage_parity(name, chunk, gate):
     check_all(raw.inp, o, fin, o_ref, f_ref, w.dtype)
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 @pytest.mark.parametrize("pre", [{"l2": True}, {"sig": True}, {"gate": "softplus"},
                                  {"gate": "bounded", "lb": -2.5}],
                          ids=["l2norm", "beta_sigmoid", "softplus_gate", "bounded_gate"])
@@ -393,7 +432,7 @@ STRONG_G = {
 }
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 @pytest.mark.parametrize("name", list(STRONG_G))
 def test_strong_decay_parity(name, chunk):
     w = STRONG_G[name]
@@ -412,7 +451,7 @@ STRONG_PRE = {
 }
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 32])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 @pytest.mark.parametrize("case", list(STRONG_PRE))
 def test_strong_gate_parity(case, chunk):
     kw, gate = STRONG_PRE[case]
@@ -426,7 +465,7 @@ def test_strong_gate_parity(case, chunk):
               f_ref, "bf16", what=f"{case} chunk {chunk}")
 
 
-@pytest.mark.parametrize("chunk", [32, 16])
+@pytest.mark.parametrize("chunk", [64, 32, 16])
 @pytest.mark.parametrize("case", list(STRONG_PRE))
 def test_strong_gate_full_size_every_unit(case, chunk):
     # the throughput shape with raw inputs and a strong gate: every chunk takes the exact

@@ -49,7 +49,7 @@ def oracle(inp):
                         n_threads=16)
 
 
-@pytest.mark.parametrize("chunk", [32, 16, 1])
+@pytest.mark.parametrize("chunk", [64, 32, 16, 1])
 def test_noalloc_matches_kda_fwd_on_consecutive_calls(chunk):
     cases = [W.WORKLOADS["h16_t4096"],                                  # 72 MB of records
              W.custom(B=2, T=100, H=2, HV=4, K=128, V=128, h0_std=0.1),  # then a smaller one

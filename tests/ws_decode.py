@@ -109,3 +109,28 @@ def decode_chunk32(raw: np.ndarray, K: int, V: int):
     off += 1024
     out["eg"] = raw[off:off + 4 * K].view(np.float32).astype(np.float64)
     return out
+
+
+def pair_bytes(K, V):
+    end = 64 * K * 3 + 64 * V + 512 + 1024 + 4 * K + 2048
+    return (end + 255) // 256 * 256
+
+
+def decode_pair(raw: np.ndarray, K: int, V: int):
+    """Decode the two records of one 64-token pair (chunk-64 workspace): returns
+    (first, second), each as decode_chunk32 returns it; second["P"] [32,32] is the product the
+    second record carries in its PT field (rows: its tokens; columns: the first chunk's)."""
+    rb = pair_bytes(K, V)
+    first = decode_chunk32(raw[:rb], K, V)
+    second = decode_chunk32(raw[rb:2 * rb], K, V)
+    end32 = 64 * K * 3 + 64 * V + 512 + 1024 + 4 * K
+    pt = raw[rb + end32:rb + end32 + 2048].view(np.float16).astype(np.float64).reshape(2, 64, 8)
+    lanes = np.arange(64)
+    g, n = lanes // 16, lanes % 16
+    P = np.full((32, 32), np.nan)
+    for x in range(2):
+        for e in range(8):
+            colv = 4 * g + e if e < 4 else 16 + 4 * g + e - 4
+            P[16 * x + n, colv] = pt[x, :, e]
+    second["P"] = P
+    return first, second
