@@ -95,7 +95,10 @@ def committed_traffic(kernel: str, workload: str):
 
 
 def summarize_trace(d: str, command: str) -> str:
-    """Markdown summary of a rocprofv3 --kernel-trace --stats run (run_kernel_stats.csv)."""
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run (CSV output): per kernel the
+    statistics of every dispatch, and, for this script's forward kernels, the average over the
+    dispatches of cache-flushed steps (a step whose first kernel follows the flush's copy and
+    read kernels) next to the warm ones, which is what the timed steps' HIP events measure."""
     import csv
     rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
     out = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
@@ -104,6 +107,29 @@ def summarize_trace(d: str, command: str) -> str:
         out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
+    tp = os.path.join(d, "run_kernel_trace.csv")
+    if os.path.exists(tp):
+        tr = sorted(csv.DictReader(open(tp)), key=lambda r: int(r["Start_Timestamp"]))
+        flushed, warm = {}, {}
+        after_flush = False
+        for r in tr:
+            name = r["Kernel_Name"]
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            if "kda::" not in name:
+                after_flush = True            # the flush's copy and read kernels
+                continue
+            (flushed if after_flush else warm).setdefault(name, []).append(dur)
+            if "state" in name or "recurrent" in name:
+                after_flush = False           # a step ends with its state pass
+        out += ["", "Forward kernels by step kind (a flushed step's kernels run after the "
+                    "flush's copy and read kernels):", "",
+                "| kernel | flushed calls | flushed avg (us) | warm calls | warm avg (us) |",
+                "|---|---|---|---|---|"]
+        for name in sorted(set(flushed) | set(warm)):
+            f, w = flushed.get(name, []), warm.get(name, [])
+            fa = f"{statistics.mean(f):.2f}" if f else "-"
+            wa = f"{statistics.mean(w):.2f}" if w else "-"
+            out.append(f"| `{name}` | {len(f)} | {fa} | {len(w)} | {wa} |")
     out += ["", f"kernel sources digest: `{source_digest()}`", ""]
     return "\n".join(out)
 
@@ -111,9 +137,11 @@ def summarize_trace(d: str, command: str) -> str:
 def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: str) -> dict:
     """Per-launch HBM bytes of each libkda_fwd kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
-    for the 256 MiB device copy (__amd_rocclr_copyBuffer) that `--copy-calibration` runs."""
+    for a device copy of known size (__amd_rocclr_copyBuffer): the 1 GiB cache-flushing copies
+    the timed steps run between them (their source does not fit any cache, so the copy reads
+    and writes 1 GiB of HBM)."""
     import csv
-    copy_bytes = 256 << 20
+    copy_bytes = 1 << 30
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
@@ -122,12 +150,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
             if r["Counter_Name"] != counter:
                 continue
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024)
-        # the calibration copy is the largest copy dispatch (inputs uploaded to the device
-        # show up as smaller ones)
-        copy = [x for k, v in vals.items() if "copyBuffer" in k for x in v]
+        # the flush copies are the largest copy dispatches (inputs uploaded to the device show
+        # up as smaller ones); their median calibrates the counter
+        copy = sorted(x for k, v in vals.items() if "copyBuffer" in k for x in v)
+        copy = [x for x in copy if x > 0.25 * copy[-1]] if copy else []
         if not copy:
             raise SystemExit(f"no calibration copy kernel in {d}")
-        scale = copy_bytes / max(copy)
+        scale = copy_bytes / statistics.median(copy)
         for k, v in vals.items():
             m = re.search(r"kda::(prepare|state|recurrent)(?:32)?_", k)
             if m:
@@ -265,6 +294,33 @@ def summarize_mfma(d: str, command: str) -> str:
     return "\n".join(out)
 
 
+def summarize_counters(dirs, command: str) -> str:
+    """Markdown summary of rocprofv3 --pmc runs of SQ_* instruction and cycle counters (one or
+    more passes, CSV output): per libkda_fwd kernel the mean per dispatch and, for counts, the
+    mean per wave (SQ_WAVES). Cycle counters in the SQ_*_CYCLES / SQ_WAIT / SQ_ACTIVE family
+    count in units of four cycles (quad cycles); they are shown as read."""
+    import csv
+    per = {}
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if "kda::" not in r["Kernel_Name"]:
+                continue
+            e = per.setdefault(r["Kernel_Name"], {})
+            e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = ["# rocprofv3 instruction and cycle counters", "", "Command (one run per pass):", "",
+           "```", command, "```", ""]
+    for k, e in per.items():
+        waves = statistics.mean(e["SQ_WAVES"]) if "SQ_WAVES" in e else None
+        out += [f"## `{k}`", "", "| counter | mean per dispatch | per wave |", "|---|---|---|"]
+        for c in sorted(e):
+            m = statistics.mean(e[c])
+            pw = f"{m / waves:.1f}" if waves and c != "SQ_WAVES" and c != "GRBM_GUI_ACTIVE" else ""
+            out.append(f"| {c} | {m:.6g} | {pw} |")
+        out.append("")
+    out += [f"kernel sources digest: `{source_digest()}`", ""]
+    return "\n".join(out)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -334,8 +390,6 @@ def main():
                     help="also time the 16-token chunk path of the same workload (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle CPU baseline (0: skip)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run one 256 MiB device copy first (a counter calibration kernel)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 --stats output dir and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -343,12 +397,17 @@ def main():
     ap.add_argument("--command", default="", help="the profiling command, for the summaries")
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 --pmc matrix-core run and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print a markdown summary of rocprofv3 --pmc SQ counter runs and exit")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (kda_bwd) instead of the forward")
     a = ap.parse_args()
 
     if a.summarize_trace:
         print(summarize_trace(a.summarize_trace, a.command))
+        return
+    if a.summarize_counters:
+        print(summarize_counters(a.summarize_counters, a.command))
         return
     if a.summarize_mfma:
         print(summarize_mfma(a.summarize_mfma, a.command))
@@ -396,13 +455,6 @@ def main():
     chunk = a.chunk or (1 if inp.cu_seqlens is None and inp.q.shape[1] <= 16 else
                         32 if w.dtype == "bf16" else 16)
     stream = torch.cuda.current_stream(dev)
-
-    if a.copy_calibration:
-        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     # Every timed step starts with the caches flushed: a 1 GiB device copy (a write of 1 GiB)
     # evicts every line of the step's working set from L2 and the 256 MB MALL; a 512 MiB read
