@@ -8,9 +8,9 @@ torch.cuda.synchronize(); before each step a 1 GiB device copy (a write of 1 GiB
 the 256 MB MALL and a 512 MiB read leaves clean lines there, and each step is timed alone with
 HIP events on its stream, so the step reads its inputs from HBM; the reported time is the
 median step. Each kernel's average duration for
-the roofline figures comes from a second pass of --steps flushed steps, the two stages launched
-separately (kda_fwd_prepare, kda_fwd_state: the same kernels) with HIP events around each
-launch on the stream it runs on.
+the roofline figures comes from a second pass of --steps flushed rounds, the two stages
+launched separately (kda_fwd_prepare, kda_fwd_state: the same kernels), --kernel-reps launches
+of each back to back between HIP events on the stream they run on.
 
 With --backward the step is one kda_bwd call instead (gradients of every input from seeded
 d_o and dht), reported under its own metric; the default line is the forward.
@@ -384,6 +384,8 @@ def main():
                          "this gate activation) inside the kernels")
     ap.add_argument("--chunk", type=int, default=0,
                     help="tokens per serial state step (16, 32; 0 = library default)")
+    ap.add_argument("--kernel-reps", type=int, default=8,
+                    help="launches of each stage per event span in the per-kernel timing pass")
     ap.add_argument("--warm-steps", type=int, default=50,
                     help="extra back-to-back steps without flushes, reported as warm (0: skip)")
     ap.add_argument("--compare-chunk16", type=int, default=1,
@@ -501,19 +503,25 @@ def main():
                  "wall_s_with_flushes": round(t1 - t0, 4),
                  "note": "per-step HIP-event durations of the timed (flushed) steps"}
 
-    # per-kernel durations: the same kernels, one launch per stage, each step after a flush,
-    # HIP events around each launch on its stream
+    # per-kernel durations: after each flush, --kernel-reps launches of the prepare stage, then
+    # as many of the state stage, back to back between HIP events on their stream (both stages
+    # are idempotent: the same inputs give the same workspace, the same workspace the same o
+    # and final state). An event recorded between two kernels adds several microseconds of GPU
+    # time, so a span of one launch would overstate the kernel; over R launches it adds 1/R.
+    R = max(1, a.kernel_reps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
     for i in range(a.steps):
         flush()
         ev[i][0].record(stream)
-        plan.prepare(stream)
+        for _ in range(R):
+            plan.prepare(stream)
         ev[i][1].record(stream)
-        plan.state(stream)
+        for _ in range(R):
+            plan.state(stream)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    prep_ms = statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps))
-    state_ms = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps))
+    prep_ms = statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps)) / R
+    state_ms = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps)) / R
 
     # warm cache, labelled as such: --warm-steps back-to-back forwards with the working set
     # (inputs, workspace, outputs) left in the MALL, timed by the host clock
@@ -626,8 +634,9 @@ def main():
                    "arithmetic": ("fp32 VALU token recurrence" if chunk == 1 else
                                   "bf16/fp16 MFMA with fp32 accumulation, fp32 inverse")},
         "roofline": roof, "roofline_path": roof_path, "kernels": kernels,
-        "kernel_timing": "avg_ms: a second pass of the same steps, each after a cache flush, "
-                         "each stage launched alone with HIP events around it on its stream",
+        "kernel_timing": f"avg_ms: a second pass of --steps rounds, each after a cache flush: "
+                         f"{R} back-to-back launches of one stage between HIP events on its "
+                         f"stream, then {R} of the other; span / {R}",
         "step_distribution": step_dist, "warm_cache": warm, "flush_dirty": dirty,
         "chunk16_run": c16,
         "cpu_baseline": cpu,

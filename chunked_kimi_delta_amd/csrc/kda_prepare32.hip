@@ -9,6 +9,11 @@ namespace kda {
 // slot's have arrived, so they stream in while the first slot is processed (requested at the
 // kernel start they had competed with every workgroup's first-slot loads, and every wave
 // waited for the whole input read before computing).
+//
+// Grid: x enumerates (slot pair, member of the value-head group), y the q/k head. The G value
+// heads of a group read the same q and k rows; blockIdx.x -> (pair, member) is the XCD map of
+// state_unit (workgroups go to the 8 XCDs round-robin), so the G workgroups of one slot pair
+// run on one XCD, eight dispatches apart, and the later ones find q and k in that XCD's L2.
 template <int K, int V, bool NORM>
 __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
 {
@@ -16,8 +21,10 @@ __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
     __shared__ Prep32Share<K, V> sh;
     const int wave = threadIdx.x >> 6;      // row block: 0 = a, 1 = b
     const int lane = threadIdx.x & 63;
-    const int j = blockIdx.y;
-    const int slot0 = 2 * blockIdx.x, slot1 = slot0 + 1;
+    int pair = 0, member = 0;
+    if (!state_unit(blockIdx.x, p.G, (p.seq.n_slots + 1) / 2, &pair, &member)) return;
+    const int j = blockIdx.y * p.G + member;
+    const int slot0 = 2 * pair, slot1 = slot0 + 1;
     int s0 = 0, s1 = 0, nv0 = 0, nv1 = 0;
     int64_t bos0 = 0, bos1 = 0;
     // workgroup-uniform: every wave takes the same branches and barriers
@@ -75,7 +82,8 @@ __global__ __launch_bounds__(128) void prepare64_bf16_kernel(FwdParams p)
 template <int K, int V>
 hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st)
 {
-    dim3 grid((p.seq.n_slots + 1) / 2, p.HV);
+    const int pairs = (p.seq.n_slots + 1) / 2;
+    dim3 grid((pairs + 7) / 8 * 8 * p.G, p.H);
     if (p.pre.qk_l2norm)
         prepare32_bf16_kernel<K, V, true><<<grid, dim3(128), 0, st>>>(p);
     else
