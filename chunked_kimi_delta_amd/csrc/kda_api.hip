@@ -71,8 +71,8 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     const int64_t tt = (int64_t)a->B * a->T;
     const int64_t ns = tt / ct + a->N;    // chunk slots (for chunk 64: pairs of 32-token chunks)
     if (2 * ns > INT32_MAX || (int64_t)a->HV > 65535) return KDA_ERR_UNSUPPORTED;
-    // the 32-token prepare grid is ((ns + 1) / 2 rounded up to 8) x (HV / H) workgroups wide
-    if (ct == 32 && ((ns + 1) / 2 + 8) * (int64_t)(a->HV / a->H) > INT32_MAX)
+    // the 32-token prepare grid is up to (ns rounded up to 8) x (HV / H) workgroups wide
+    if (ct == 32 && (ns + 8) * (int64_t)(a->HV / a->H) > INT32_MAX)
         return KDA_ERR_UNSUPPORTED;
     size_t cb;
     if (ct == 1)

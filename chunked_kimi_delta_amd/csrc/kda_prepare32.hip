@@ -5,26 +5,32 @@
 
 namespace kda {
 
-// Two chunk slots per workgroup: the second slot's inputs are requested as soon as the first
-// slot's have arrived, so they stream in while the first slot is processed (requested at the
-// kernel start they had competed with every workgroup's first-slot loads, and every wave
-// waited for the whole input read before computing).
+// SLOTS (1 or 2) chunk slots per workgroup. With two, the second slot's inputs are requested
+// as soon as the first slot's have arrived, so they stream in while the first slot is
+// processed (requested at the kernel start they had competed with every workgroup's first-slot
+// loads, and every wave waited for the whole input read before computing). Two slots pay when
+// the whole grid is resident at once (every wave would otherwise wait for its inputs at the
+// same moment); with several rounds of workgroups one slot each is faster, because the rounds
+// overlap one workgroup's loads with others' arithmetic by themselves.
 //
-// Grid: x enumerates (slot pair, member of the value-head group), y the q/k head. The G value
-// heads of a group read the same q and k rows; blockIdx.x -> (pair, member) is the XCD map of
-// state_unit (workgroups go to the 8 XCDs round-robin), so the G workgroups of one slot pair
+// Grid: x enumerates (slot group, member of the value-head group), y the q/k head. The G value
+// heads of a group read the same q and k rows; blockIdx.x -> (group, member) is the XCD map of
+// state_unit (workgroups go to the 8 XCDs round-robin), so the G workgroups of one slot group
 // run on one XCD, eight dispatches apart, and the later ones find q and k in that XCD's L2.
-template <int K, int V, bool NORM>
+template <int K, int V, bool NORM, int SLOTS>
 __global__ __launch_bounds__(128) void prepare32_bf16_kernel(FwdParams p)
 {
+    static_assert(SLOTS == 1 || SLOTS == 2, "one or two chunk slots per workgroup");
     using WS = WsBf16x32<K, V>;
     __shared__ Prep32Share<K, V> sh;
     const int wave = threadIdx.x >> 6;      // row block: 0 = a, 1 = b
     const int lane = threadIdx.x & 63;
-    int pair = 0, member = 0;
-    if (!state_unit(blockIdx.x, p.G, (p.seq.n_slots + 1) / 2, &pair, &member)) return;
+    int grp = 0, member = 0;
+    if (!state_unit(blockIdx.x, p.G, (p.seq.n_slots + SLOTS - 1) / SLOTS, &grp, &member))
+        return;
     const int j = blockIdx.y * p.G + member;
-    const int slot0 = 2 * pair, slot1 = slot0 + 1;
+    const int slot0 = SLOTS * grp;
+    const int slot1 = SLOTS == 2 ? slot0 + 1 : p.seq.n_slots;    // one slot: no second
     int s0 = 0, s1 = 0, nv0 = 0, nv1 = 0;
     int64_t bos0 = 0, bos1 = 0;
     // workgroup-uniform: every wave takes the same branches and barriers
@@ -79,16 +85,32 @@ __global__ __launch_bounds__(128) void prepare64_bf16_kernel(FwdParams p)
                                    wave, lane);
 }
 
+template <int K, int V, int SLOTS>
+static hipError_t launch_prepare32_slots(const FwdParams &p, hipStream_t st)
+{
+    const int groups = (p.seq.n_slots + SLOTS - 1) / SLOTS;
+    dim3 grid((groups + 7) / 8 * 8 * p.G, p.H);
+    if (p.pre.qk_l2norm)
+        prepare32_bf16_kernel<K, V, true, SLOTS><<<grid, dim3(128), 0, st>>>(p);
+    else
+        prepare32_bf16_kernel<K, V, false, SLOTS><<<grid, dim3(128), 0, st>>>(p);
+    return hipGetLastError();
+}
+
+// Two slots per workgroup while the two-slot workgroups that hold chunks fit on the chip in
+// one round (four two-wave workgroups per CU: the kernel's register use allows two waves per
+// SIMD), else one. Workgroups of empty slots exit at once and are not counted: a dense batch
+// has ceil(ceil(T / 32) / 2) two-slot groups per sequence; packed sequences at most
+// T_total / 64 + N. Measured with the 16 x 4096 grid (1,024 two-slot workgroups, one round):
+// 37.5 us with two slots, 39.4 with one; at 4 x 8192 tokens x 32 heads (16 rounds): 488 us
+// with two, 464 with one.
 template <int K, int V>
 hipError_t launch_prepare32_bf16(const FwdParams &p, hipStream_t st)
 {
-    const int pairs = (p.seq.n_slots + 1) / 2;
-    dim3 grid((pairs + 7) / 8 * 8 * p.G, p.H);
-    if (p.pre.qk_l2norm)
-        prepare32_bf16_kernel<K, V, true><<<grid, dim3(128), 0, st>>>(p);
-    else
-        prepare32_bf16_kernel<K, V, false><<<grid, dim3(128), 0, st>>>(p);
-    return hipGetLastError();
+    const int64_t groups = p.seq.cu ? (p.seq.T_total + 63) / 64 + p.seq.N
+                                    : p.seq.N * (((p.seq.T + 31) / 32 + 1) / 2);
+    if (groups * p.HV <= 4LL * current_device_cus()) return launch_prepare32_slots<K, V, 2>(p, st);
+    return launch_prepare32_slots<K, V, 1>(p, st);
 }
 
 template <int K, int V>
