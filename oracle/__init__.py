@@ -25,8 +25,11 @@ Contents
   backward_chunked.py  the same gradients by the chunked reverse sweep (chunk records, the
                   state and state-gradient chains, per-chunk local gradients): the algebra
                   the GPU backward follows, pinned against backward.py.
+  kda_oracle_bwd.c  the fp64 reverse token recurrence of backward.py in plain C (states
+                  rebuilt from checkpoints every 256 tokens), threaded over (sequence, q/k
+                  head) tasks; the fast backward oracle for full-size workloads.
   native.py       ctypes loader for the C oracle.
-  build.py        compiles kda_oracle.c with gcc.
+  build.py        compiles kda_oracle.c and kda_oracle_bwd.c with gcc.
 
 Sources (pages, by title): the KDA definition is read off the chunked listing in "手撕KDA"
 ("KDA by hand"), section 1 (the FLA naive_chunk_kda routine): a one-token chunk of that

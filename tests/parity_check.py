@@ -151,3 +151,43 @@ def check_outputs(o, fin, o_ref, f_ref, bounds, dtype, units=None, what=""):
             f"{len(bad_rows)} row(s), first (s, j, key row) = {tuple(int(i) for i in bad_rows[0])}: "
             f"{fr[tuple(bad_rows[0])]:.3e}")
     return worst
+
+
+# ----------------------------------------------------------------------------- gradients
+
+GRAD_TOL = 1e-4          # the backward computes in fp32 from the exact inputs (either io)
+GRAD_NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def check_grads(got, ref, bounds, what=""):
+    """Both bars on every gradient tensor, per unit and per row, as for o and the final state:
+    dq and dk per (sequence, q/k head) with token rows of K values; dv and dg per (sequence,
+    value head) with token rows; dbeta per (sequence, value head) with one value per token;
+    dh0 per (sequence, value head) with its K key rows. got and ref are (dq, dk, dv, dg, dbeta,
+    dh0) in the layouts of the inputs ([B, T, heads, D], [B, T, HV], [N, HV, K, V]). Returns
+    the worst unit and row values per tensor."""
+    worst = {}
+    for name, a, b in zip(GRAD_NAMES, got, ref):
+        if name == "dh0":
+            if a is None:
+                continue
+            assert np.isfinite(a).all(), f"{what}: non-finite {name}"
+            ue, ratio = state_errors(a, np.asarray(b).reshape(a.shape))
+        else:
+            a = np.asarray(a)
+            b = np.asarray(b).reshape(a.shape)
+            if name == "dbeta":
+                a, b = a[..., None], b[..., None]
+            assert np.isfinite(a).all(), f"{what}: non-finite {name}"
+            ue, ratio, _ = o_errors(a, b, bounds)
+        worst[name + "_unit"] = float(np.nanmax(ue)) if np.isfinite(ue).any() else 0.0
+        worst[name + "_row"] = float(ratio.max()) if ratio.size else 0.0
+        bad = np.argwhere(np.nan_to_num(ue, nan=0.0) > GRAD_TOL)
+        assert bad.size == 0, (
+            f"{what}: {name} rel L2 above {GRAD_TOL} in {len(bad)} unit(s), first "
+            f"{tuple(int(i) for i in bad[0])}: {ue[tuple(bad[0])]:.3e}")
+        bad = np.argwhere(ratio > GRAD_TOL)
+        assert bad.size == 0, (
+            f"{what}: {name} row error above {GRAD_TOL} x (row norm + unit rms) in {len(bad)} "
+            f"row(s), first {tuple(int(i) for i in bad[0])}: {ratio[tuple(bad[0])]:.3e}")
+    return worst

@@ -4,9 +4,9 @@ oracle/backward.py, element by element.
 Bar: relative L2 error ||x_gpu - x_ref|| / ||x_ref|| of each gradient tensor (dq, dk, dv, dg,
 dbeta, dh0), computed in fp64, <= 1e-4 for bf16 and fp32 io alike: the kernels compute in fp32
 from exactly the values the oracle reads (bf16 -> fp32 is exact), so the only error is fp32
-rounding, as for the forward's fp32 io. Small cases compare every element; the full-size
-workloads compare a seeded sample of whole units (all tokens of one sequence and one q/k head
-with its value heads) and check finiteness everywhere.
+rounding, as for the forward's fp32 io. Small cases compare every element. The full-size
+workloads compare every unit against the C backward oracle (oracle/kda_oracle_bwd.c), with the
+bar applied per (sequence, head) unit and per token row of every tensor (tests/parity_check.py).
 """
 from __future__ import annotations
 
@@ -25,6 +25,7 @@ import chunked_kimi_delta_amd as kda
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
 DEV = "cuda:0"
+ORACLE_THREADS = 16             # the CPU share of a one-GPU machine
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 
 
@@ -133,41 +134,39 @@ def test_backward_g0_matches_oracle():
     check_grads(gpu_bwd(inp, gr), oracle_bwd(inp, gr))
 
 
-def _unit_slice(inp: W.Inputs, gr: W.Grads, s: int, h: int):
-    """The inputs of sequence s and q/k head h with its G value heads, as a 1-sequence batch."""
-    bos, eos = inp.seq_bounds()[s]
-    G = inp.w.G
-    js = slice(h * G, (h + 1) * G)
-    tok = lambda x: x.reshape(-1, *x.shape[2:])[bos:eos].unsqueeze(0)
-    sub = W.Inputs(inp.w, tok(inp.q)[:, :, h:h + 1], tok(inp.k)[:, :, h:h + 1],
-                   tok(inp.v)[:, :, js], tok(inp.g)[:, :, js], tok(inp.beta)[:, :, js],
-                   None if inp.h0 is None else inp.h0[s:s + 1, js], None, inp.scale)
-    sgr = W.Grads(tok(gr.d_o)[:, :, js], None if gr.dht is None else gr.dht[s:s + 1, js])
-    return sub, sgr, (bos, eos, js)
+def gpu_bwd_f32(inp: W.Inputs, gr: W.Grads):
+    """The GPU gradients as float32 numpy arrays (full-size workloads: half the memory of
+    float64 copies; the checks convert one head at a time)."""
+    plan = kda.KdaBwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                          dev(gr.d_o), dev(gr.dht), scale=inp.scale,
+                          cu_seqlens=dev(inp.cu_seqlens), initial_state=dev(inp.h0))
+    out = plan()
+    torch.cuda.synchronize()
+    res = tuple(None if x is None else x.float().cpu().numpy() for x in out[:6])
+    del plan, out
+    return res
 
 
-@pytest.mark.parametrize("name,n_units", [("h16_t4096", 3), ("varlen8_h32", 3),
-                                          ("gva_b4_t8192", 2)])
-def test_backward_full_size_sampled(name, n_units):
+@pytest.mark.parametrize("name", ["h16_t4096", "varlen8_h32", "gva_b4_t8192", "long_t131072"])
+def test_backward_full_size_every_unit(name):
+    # every unit of the workload against the C backward oracle, both bars on every tensor
+    from oracle.native import kda_oracle_bwd_c
+    from parity_check import check_grads as check_every_unit
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, seed=0)
     gr = W.make_grads(inp, seed=0)
     print(f"[bwd full] {name}: GPU backward", file=sys.stderr, flush=True)
-    got = gpu_bwd(inp, gr)
-    for x in got[:6]:
-        assert np.isfinite(x).all()
-    dq, dk, dv, dg, db, dh0 = got[:6]
-    flat = lambda x: x.reshape(-1, *x.shape[2:])
-    units = W.sample_units(inp.N, w.H, n_units, seed=7)
-    for s, h in units:
-        sub, sgr, (bos, eos, js) = _unit_slice(inp, gr, s, h)
-        print(f"[bwd full] {name}: oracle unit s={s} h={h} ({eos - bos} tokens)",
-              file=sys.stderr, flush=True)
-        ref = oracle_bwd(sub, sgr)
-        mine = (flat(dq)[bos:eos, h:h + 1][None], flat(dk)[bos:eos, h:h + 1][None],
-                flat(dv)[bos:eos, js][None], flat(dg)[bos:eos, js][None],
-                flat(db)[bos:eos, js][None], dh0[s:s + 1, js])
-        check_grads(mine, ref)
+    got = gpu_bwd_f32(inp, gr)
+    print(f"[bwd full] {name}: oracle over every unit", file=sys.stderr, flush=True)
+    f = W.as_f32_numpy
+    ref = kda_oracle_bwd_c(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.scale,
+                           None if inp.h0 is None else inp.h0.numpy(),
+                           None if inp.cu_seqlens is None else inp.cu_seqlens.numpy(),
+                           f(gr.d_o), None if gr.dht is None else gr.dht.numpy(),
+                           n_threads=ORACLE_THREADS)
+    print(f"[bwd full] {name}: compare", file=sys.stderr, flush=True)
+    worst = check_every_unit(got, ref, inp.seq_bounds(), what=name)
+    report_named(**worst)
 
 
 # --------------------------------------------------------------------------- with the pre-stage
@@ -259,7 +258,21 @@ def test_backward_prestage_full_size_bounded_gate():
     print("[bwd pre full] GPU backward", file=sys.stderr, flush=True)
     got = gpu_bwd_raw(raw, gr, pre)
     print("[bwd pre full] oracle", file=sys.stderr, flush=True)
-    check_raw(got, oracle_bwd_raw(raw, gr, pre), pre)
+    ref = oracle_bwd_raw(raw, gr, pre)
+    check_raw(got, ref, pre)
+    # and per unit / per row on the six input gradients, per value head on the parameters
+    from parity_check import check_grads as check_every_unit
+    worst = check_every_unit(got[:6], ref[:6], raw.inp.seq_bounds(), what="prestage h16_t4096")
+    report_named(**worst)
+    # each head's parameter gradient within TOL x (its norm + the rms over heads), the row
+    # bar's form: a sum over every token can cancel to a small value in one head
+    dA, dA_ref = got[6], np.asarray(ref[6]).reshape(got[6].shape)
+    rms = np.sqrt(np.mean(dA_ref ** 2))
+    assert np.all(np.abs(dA - dA_ref) <= TOL * (np.abs(dA_ref) + rms)), "dA_log off in a head"
+    ddt, ddt_ref = got[7], np.asarray(ref[7]).reshape(got[7].shape)
+    nrm = np.linalg.norm(ddt_ref, axis=-1)
+    bad = np.linalg.norm(ddt - ddt_ref, axis=-1) > TOL * (nrm + np.sqrt(np.mean(nrm ** 2)))
+    assert not bad.any(), f"ddt_bias off in head {int(np.argmax(bad))}"
 
 
 # --------------------------------------------------------------------------- torch.autograd

@@ -8,6 +8,11 @@
   decay only   beta = 0: dh0 = exp(sum of g) * dht elementwise (final = exp(sum g) h0)
 Planted mistakes (copies of the reverse recurrence with one line changed) must each fail the
 finite-difference pin.
+
+The C backward (oracle/kda_oracle_bwd.c, the fast oracle of the full-size GPU tests) is pinned
+the same way: central differences of the fp64 forward, including sequences that span several
+of its 256-token checkpoint segments; the decay-only and zero-loss cases; and agreement with
+the Python reverse recurrence to 1e-12 on fp32-valued inputs.
 """
 from __future__ import annotations
 
@@ -154,3 +159,51 @@ def test_chunked_backward_without_dht():
     b = kda_backward_chunked(q, k, v, g, beta, scale, S0, cu, do, None)
     for x, y in zip(a, b):
         assert np.allclose(x, y, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- the C backward
+
+def _c_bwd(q, k, v, g, beta, scale, S0, cu, do, dht):
+    from oracle.native import kda_oracle_bwd_c
+    return kda_oracle_bwd_c(q, k, v, g, beta, scale, S0, cu, do, dht, n_threads=2)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_c_backward_matches_finite_differences(name):
+    # the C reverse recurrence against central differences of the fp64 forward (recurrent.py)
+    pin_finite_differences(_c_bwd, rand_case(**CASES[name]))
+
+
+def test_c_backward_checkpoint_segments_match_finite_differences():
+    # 600 tokens: three 256-token checkpoint segments, the last one partial, and a sequence
+    # boundary inside a segment
+    cu = np.array([0, 300, 300, 600])
+    pin_finite_differences(_c_bwd, rand_case(H=1, HV=2, K=3, V=2, cu=cu))
+
+
+def _f32_case(case):
+    # the C oracle reads fp32 carriers: round every input to fp32 first, so both oracles see
+    # the same values
+    r = lambda x: x if x is None or np.isscalar(x) else np.asarray(x, np.float32).astype(np.float64)
+    q, k, v, g, beta, scale, S0, cu, do, dht = case
+    return (r(q), r(k), r(v), r(g), r(beta), scale, r(S0), cu, r(do), r(dht))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_c_backward_agrees_with_python_backward(name):
+    case = _f32_case(rand_case(**CASES[name]))
+    a = _c_bwd(*case)
+    b = BW.kda_backward_recurrent(*case)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, np.asarray(y).reshape(x.shape), rtol=1e-12, atol=1e-13)
+
+
+def test_c_backward_decay_only_and_zero_loss():
+    q, k, v, g, beta, scale, S0, cu, do, dht = _f32_case(rand_case(B=1, T=300, H=1, HV=1, K=3,
+                                                                   V=2))
+    beta0 = np.zeros_like(beta)
+    *_, dh0 = _c_bwd(q, k, v, g, beta0, scale, S0, cu, np.zeros_like(do), dht)
+    # beta = 0: final = exp(sum g) h0 per key row, so dh0 = exp(sum g) dht
+    np.testing.assert_allclose(dh0, np.exp(g.sum(axis=1))[..., None] * dht, rtol=1e-12)
+    grads = _c_bwd(q, k, v, g, beta, scale, S0, cu, np.zeros_like(do), np.zeros_like(dht))
+    assert all(np.count_nonzero(x) == 0 for x in grads)

@@ -88,3 +88,48 @@ def test_varlen_units_and_empty_sequences():
     bad[0, 40 + 5, 1, :] *= 1.001             # sequence 3 (tokens 40..56), head 1
     with pytest.raises(AssertionError, match=r"first \(s, j\) = \(3, 1\)"):
         check_outputs(bad, f_ref, o_ref, f_ref, inp.seq_bounds(), "fp32")
+
+
+# --------------------------------------------------------------------------- gradient bars
+
+@pytest.fixture(scope="module")
+def grads_small():
+    # packed sequences with grouped value heads; the C backward oracle's gradients
+    from oracle.native import kda_oracle_bwd_c
+    w = W.custom(H=2, HV=4, K=64, V=64, h0_std=0.2, lengths=(40, 0, 300, 17))
+    inp = W.make_inputs(w, seed=4)
+    gr = W.make_grads(inp, seed=4)
+    f = W.as_f32_numpy
+    ref = kda_oracle_bwd_c(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.scale,
+                           inp.h0.numpy(), inp.cu_seqlens.numpy(), f(gr.d_o), gr.dht.numpy(),
+                           n_threads=2)
+    return inp, ref
+
+
+def test_fp32_rounded_gradients_pass(grads_small):
+    from parity_check import check_grads
+    inp, ref = grads_small
+    got = tuple(x.astype(np.float32) for x in ref)
+    worst = check_grads(got, ref, inp.seq_bounds())
+    assert max(worst.values()) < 1e-6
+
+
+@pytest.mark.parametrize("name,where", [("dk", (0, 320, 1)), ("dg", (0, 5, 2)),
+                                        ("dbeta", (0, 100, 3)), ("dv", (0, 341, 0))])
+def test_planted_gradient_row_is_caught(grads_small, name, where):
+    from parity_check import GRAD_NAMES, check_grads
+    inp, ref = grads_small
+    got = [x.copy() for x in ref]
+    i = GRAD_NAMES.index(name)
+    got[i][where] = 0.0                        # one token row (one value for dbeta) unwritten
+    with pytest.raises(AssertionError, match=f"{name} (rel L2 above|row error)"):
+        check_grads(got, ref, inp.seq_bounds())
+
+
+def test_planted_dh0_row_is_caught(grads_small):
+    from parity_check import check_grads
+    inp, ref = grads_small
+    got = [x.copy() for x in ref]
+    got[5][2, 1, 7, :] *= 1.001                # one key row of one unit's dh0, 0.1% off
+    with pytest.raises(AssertionError, match="dh0 (rel L2 above|row error)"):
+        check_grads(got, ref, inp.seq_bounds())

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Optional, Sequence
+from typing import Optional
 
 import torch
 
@@ -220,17 +220,3 @@ def as_f32_numpy(x: Optional[torch.Tensor]):
     if x is None:
         return None
     return x.float().contiguous().numpy()
-
-
-def sample_units(N: int, HV: int, n: int, seed: int = 1) -> Sequence[tuple]:
-    """A seeded sample of n distinct (sequence, value head) units for spot checks at full
-    size. Always includes the first and last unit."""
-    total = N * HV
-    gen = torch.Generator().manual_seed(seed)
-    idx = set([0, total - 1])
-    perm = torch.randperm(total, generator=gen).tolist()
-    for p in perm:
-        if len(idx) >= min(n, total):
-            break
-        idx.add(p)
-    return sorted((i // HV, i % HV) for i in idx)
