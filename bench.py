@@ -97,8 +97,8 @@ def committed_traffic(kernel: str, workload: str):
 def summarize_trace(d: str, command: str) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run (CSV output): per kernel the
     statistics of every dispatch, and, for this script's forward kernels, the average over the
-    dispatches of cache-flushed steps (a step whose first kernel follows the flush's copy and
-    read kernels) next to the warm ones, which is what the timed steps' HIP events measure."""
+    first launch of each stage after a cache flush next to the average over the launches that
+    follow it back to back."""
     import csv
     rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
     out = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
@@ -110,23 +110,25 @@ def summarize_trace(d: str, command: str) -> str:
     tp = os.path.join(d, "run_kernel_trace.csv")
     if os.path.exists(tp):
         tr = sorted(csv.DictReader(open(tp)), key=lambda r: int(r["Start_Timestamp"]))
-        flushed, warm = {}, {}
-        after_flush = False
+        first, again = {}, {}
+        seen = set()
         for r in tr:
             name = r["Kernel_Name"]
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             if "kda::" not in name:
-                after_flush = True            # the flush's copy and read kernels
+                seen = set()                  # the flush's copy and read kernels
                 continue
-            (flushed if after_flush else warm).setdefault(name, []).append(dur)
-            if "state" in name or "recurrent" in name:
-                after_flush = False           # a step ends with its state pass
-        out += ["", "Forward kernels by step kind (a flushed step's kernels run after the "
-                    "flush's copy and read kernels):", "",
-                "| kernel | flushed calls | flushed avg (us) | warm calls | warm avg (us) |",
+            kind = "prepare" if "prepare" in name else "state"
+            (again if kind in seen else first).setdefault(name, []).append(dur)
+            seen.add(kind)
+        out += ["", "Forward kernels by launch kind: the first launch of each stage after a "
+                    "cache flush (the timed steps' kernels), and the launches that follow it "
+                    "back to back before the next flush (warm steps and the per-kernel timing "
+                    "pass's repeats):", "",
+                "| kernel | first after a flush: calls | avg (us) | repeats: calls | avg (us) |",
                 "|---|---|---|---|---|"]
-        for name in sorted(set(flushed) | set(warm)):
-            f, w = flushed.get(name, []), warm.get(name, [])
+        for name in sorted(set(first) | set(again)):
+            f, w = first.get(name, []), again.get(name, [])
             fa = f"{statistics.mean(f):.2f}" if f else "-"
             wa = f"{statistics.mean(w):.2f}" if w else "-"
             out.append(f"| `{name}` | {len(f)} | {fa} | {len(w)} | {wa} |")
@@ -492,6 +494,22 @@ def main():
         plan(stream)
     torch.cuda.synchronize()
 
+    # the box's own copy bandwidth, for context next to the 8 TB/s peak: the flush's 1 GiB
+    # device copy (reads and writes 1 GiB of HBM; neither buffer fits any cache), HIP events
+    # around each of five copies, median
+    cps = []
+    for _ in range(5):
+        flush_clean.max()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        flush_dst.copy_(flush_src)
+        c1.record(stream)
+        cps.append((c0, c1))
+    torch.cuda.synchronize()
+    copy_ms = statistics.median(c0.elapsed_time(c1) for c0, c1 in cps)
+    copy_gbs = 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+
     # the timed region: exactly --steps forwards, each after a cache flush
     t0 = time.perf_counter()
     step_ms = flushed_steps(plan, a.steps)
@@ -607,7 +625,9 @@ def main():
     roof_path = {"bound": "hbm", "achieved": round(path_gbs, 1), "peak": HBM_PEAK_GBS,
                  "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 5),
                  "alg_bytes_per_step": path_bytes,
-                 "note": "whole forward, algorithmic bytes / flushed median step time"}
+                 "copy_GBs": round(copy_gbs, 1), "frac_of_copy": round(path_gbs / copy_gbs, 5),
+                 "note": "whole forward, algorithmic bytes / flushed median step time; copy_GBs "
+                         "is a 1 GiB device copy on the same GPU (read + write bytes / time)"}
     if c16 is not None:
         c16["roofline_path_frac"] = round(path_bytes / (c16["ms_per_step"] * 1e-3) / 1e9
                                           / HBM_PEAK_GBS, 5)
