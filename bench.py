@@ -200,28 +200,40 @@ def backward_flops(inp):
 
 
 def cpu_baseline_bwd(inp, gr, min_seconds: float):
-    """The fp64 oracle backward (numpy reverse recurrence, unchanged) on one (sequence, value
-    head) slice of up to 512 tokens, repeated for at least `min_seconds`; scaled to the
-    workload's tokens/s (all heads)."""
+    """The fp64 C backward oracle (unchanged) on the host cores: the whole workload's gradients
+    (every unit), repeated until at least `min_seconds` of wall time have passed (bounded at
+    1000 repetitions); then the same on one thread for a third of that time."""
     import workloads as W
-    from oracle.backward import kda_backward_recurrent
-    T = min(512, inp.q.shape[1])
-    f = lambda x: W.as_f32_numpy(x)[:1, :T]
-    args = [f(inp.q)[:, :, :1], f(inp.k)[:, :, :1], f(inp.v)[:, :, :1], f(inp.g)[:, :, :1],
-            f(inp.beta)[:, :, :1]]
-    do = f(gr.d_o)[:, :, :1]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        kda_backward_recurrent(*args, inp.scale, None, None, do, None)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or reps >= 1000:
-            break
-    return {"value": round(reps * T / inp.w.HV / el, 2), "unit": "tokens/s", "cores": 1,
+    from oracle.native import kda_oracle_bwd_c
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    cores = max(1, min(affinity, BOX_CPU_SHARE))
+    f = W.as_f32_numpy
+    args = [f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.scale,
+            None if inp.h0 is None else inp.h0.numpy(),
+            None if inp.cu_seqlens is None else inp.cu_seqlens.numpy(),
+            f(gr.d_o), None if gr.dht is None else gr.dht.numpy()]
+    def run(threads, seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            kda_oracle_bwd_c(*args, n_threads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                return reps, el
+    reps, el = run(cores, min_seconds)
+    reps1, el1 = run(1, min_seconds / 3)
+    return {"value": round(reps * inp.T_total / el, 2), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"oracle backward (fp64 numpy reverse recurrence) of {T} tokens of one "
-                      f"value head, repeated {reps}x in {el:.1f} s; tokens/s of all "
-                      f"{inp.w.HV} heads = head-tokens/s / {inp.w.HV}"}
+            "sample": f"full {inp.w.name} backward (all {inp.w.HV} heads, fp64 C reverse "
+                      f"recurrence), repeated {reps}x in {el:.1f} s",
+            "value_1_thread": round(reps1 * inp.T_total / el1, 2),
+            "cpu_model": cpu_model(), "affinity_cpus": affinity,
+            "threads_note": f"{cores} threads: the CPU share of a one-GPU box "
+                            f"(min of the affinity mask and {BOX_CPU_SHARE}); the tasks are "
+                            f"(sequence, q/k head) pairs"}
 
 
 def run_backward(a, torch, W, kda):
