@@ -11,7 +11,7 @@
  *     S <- S + beta[t, j] k[t, h, :] r^T;   o[t, j, :] = scale * S^T q[t, h, :]
  *
  * and final_state[s, j] is S after the last token. The library evaluates it in the chunked
- * form of the same section with chunks of 16 or 32 tokens: a token-parallel prepare kernel
+ * form of the same section with chunks of 16, 32 or 64 tokens: a token-parallel prepare kernel
  * (in-chunk cumsum of g, decayed q/k, the strictly lower triangular L and the masked Mqk, the
  * inverse of (I + L) by the Neumann doubling product of "KDA源码剖析之FlashKDA（上）" part 12,
  * and w = A (exp(G) k), u = A v) followed by a chunk-sequential state kernel; or token by token
@@ -105,7 +105,10 @@ typedef struct {
     float *final_state;       /* [N, HV, K, V] fp32, or NULL to skip                        */
     int32_t chunk;            /* tokens per serial step of the state kernel: 16 (the FlashKDA
                                  tile of "KDA源码剖析之FlashKDA（上）"), 32 (two 16-token blocks
-                                 joined by block forward substitution; bf16 io only), 1 (the
+                                 joined by block forward substitution; bf16 io only), 64 (pairs
+                                 of 32-token chunks per serial step, the second chunk's delta
+                                 written in the pair's starting state and the first chunk's
+                                 delta; bf16 io only), 1 (the
                                  token recurrence itself, fp32 arithmetic, no workspace: for
                                  decoding and other short sequences, where a chunk's fixed cost
                                  dominates), or 0 for the default: 1 for a dense batch with
@@ -126,8 +129,9 @@ typedef struct {
 /* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
    Returns 0 for arguments kda_fwd would reject. The workspace holds the prepare kernel's
    per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma)) for ceil-bounded chunk slots of every
-   value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16) or 34,816 B (chunk 32) at
-   bf16 io and K = V = 128. Chunk 1 needs none (0; kda_fwd then accepts a NULL workspace). */
+   value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16), 34,816 B (chunk 32) or
+   2 x 36,864 B (chunk 64: two 32-token records per slot) at bf16 io and K = V = 128. Chunk 1
+   needs none (0; kda_fwd then accepts a NULL workspace). */
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
 
 /* Enqueue the forward: prepare kernel, then state kernel, on `stream` (hipStream_t or NULL).
