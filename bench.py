@@ -108,7 +108,8 @@ def summarize_trace(d: str, command: str) -> str:
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
     tp = os.path.join(d, "run_kernel_trace.csv")
-    if os.path.exists(tp):
+    # the backward's runs have no cache-flushed steps: no split for them
+    if os.path.exists(tp) and not any("bwd_" in r["Name"] for r in rows):
         tr = sorted(csv.DictReader(open(tp)), key=lambda r: int(r["Start_Timestamp"]))
         first, again = {}, {}
         seen = set()
