@@ -126,11 +126,15 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, f32x4 (&S)
 {
     constexpr int NSH = K / 64;
     if constexpr (h == 0) {
+        // -U of both blocks is stored in the B layout of a 16x16x16 product (lane (n, g): rows
+        // 4g .. 4g + 3 of column n), so the identity times it is -U in C layout, exactly: two
+        // matrix-core products instead of eight conversions in this wave's stream
+        const int n = lane & 15, g = lane >> 4;
+        f16x4 ih;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Xa[i] = (float)f.nu[i];
-            Xb[i] = (float)f.nu[4 + i];
-        }
+        for (int i = 0; i < 4; ++i) ih[i] = (_Float16)(4 * g + i == n ? 1.f : 0.f);
+        Xa = mfma16(ih, __builtin_shufflevector(f.nu, f.nu, 0, 1, 2, 3), zero4());
+        Xb = mfma16(ih, __builtin_shufflevector(f.nu, f.nu, 4, 5, 6, 7), zero4());
     } else {
         Xa = zero4();
         Xb = zero4();
