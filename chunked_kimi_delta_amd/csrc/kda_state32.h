@@ -53,6 +53,8 @@ struct HalfFrag {
     f16x8 w[2][NSH];          // W rows of blocks a and b, this half's columns
     f16x8 kr[NKH];            // KR^T tiles of this half over the 32 tokens
     f32x4 eg[NKH];            // exp(gam) of the four rows 16t + 4g + i each lane holds
+    float e1;                 // exp(gam) of row K/2 h + lane % (K/2) as loaded; it reaches eg
+                              // through this wave's LDS stage one step later (stage_eg)
     f16x8 nu;                 // -U of blocks a (0..3) and b (4..7), this slice (half 0 only)
 };
 
@@ -75,17 +77,16 @@ struct Chunk32 {
     int lane, slice;
     template <int h>
     __device__ __forceinline__ void load_w(HalfFrag<K, V> &f) const {
+        // first, so that waiting for it (one step later) waits for no load issued after it
+        f.e1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rs, (lane % (K / 2)) * 4, WS::EG + h * (K / 2) * 4,
+                                             AUX));
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int j = 0; j < NSH; ++j)
                 f.w[b][j] = __builtin_bit_cast(
                     f16x8, bload16<AUX>(rs, lane * 16, WS::W + (b * NS + h * NSH + j) * 1024));
-        const int grp = lane >> 4;
-#pragma unroll
-        for (int t = 0; t < NKH; ++t)
-            f.eg[t] = __builtin_bit_cast(
-                f32x4, bload16<AUX>(rs, grp * 16, WS::EG + (h * NKH + t) * 64));
         if constexpr (h == 0)
             f.nu = __builtin_bit_cast(f16x8, bload16<AUX>(rs, lane * 16, WS::NU + slice * 1024));
     }
@@ -113,7 +114,24 @@ struct Handoff32 {
     f16x8 sh[3][K / 32][64];     // S (fp16) of chunk c in slot c % 3
     f32x4 xp[2][2][2][64];       // [chunk parity][half][block] partial W S (half 0: + (-U))
     f16x4 dh[2][2][64];          // [chunk parity][block] delta
+    float egs[2][64];            // [half] exp(gam) of the chain wave's rows, on their way from
+                                 // one value per lane to the four-rows-per-lane tiles of eg
 };
+
+// exp(gam) of the fragment `o` from one value per lane (o.e1, row K/2 h + lane) to the C-layout
+// rows each lane decays (rows 16t + 4g .. + 3 of tile t, the same for the 16 lanes of a group):
+// through this wave's own LDS stage, whose write and reads are ordered by the wave's LDS queue.
+// A 16-byte load per tile had fetched every value 16 times through the CU's vector-memory path,
+// a quarter of the chain waves' operand traffic (46.4 -> 45.5 us at 16 heads x 4096 tokens,
+// 0.465 -> 0.428 ms at 4 x 8192 tokens x 32 value heads).
+template <int K, int V, int h>
+__device__ __forceinline__ void stage_eg(HalfFrag<K, V> &o, Handoff32<K> &ho, int lane)
+{
+    ho.egs[h][lane] = o.e1;
+#pragma unroll
+    for (int t = 0; t < K / 32; ++t)
+        o.eg[t] = *(const f32x4 *)&ho.egs[h][16 * t + 4 * (lane >> 4)];
+}
 
 // Chain wave h, one 32-token chunk c (S = its rows of the state at the chunk start), up to
 // and including barrier c: fp16 rows to the hand-off and the partial of W S to the other half;
@@ -158,11 +176,13 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, f32x4 (&S)
 // Chain wave h after barrier c: the other half's partial is read first, and the refill of the
 // W / exp(gam) / -U group from `nxt` (two chunks ahead) is issued in its LDS latency; then
 // delta = -(own partial + other partial) (half 0 hands it to the output wave) and the update of
-// its rows; the KR^T group is refilled last. The scheduling barriers keep the compiler from
+// its rows; the KR^T group is refilled last, and the other fragment `o` (the next chunk's) gets
+// its exp(gam) tiles from its staged value. The scheduling barriers keep the compiler from
 // moving the refills between the update products, where their issue delayed the next step
 // (48.8 -> 46.3 us per launch at 16 x 4096, 0.474 -> 0.461 ms at 4 x 8192 x 32 heads).
 template <int K, int V, int h, int AUX>
-__device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, const Chunk32<K, V, AUX> &nxt,
+__device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, HalfFrag<K, V> &o,
+                                             const Chunk32<K, V, AUX> &nxt,
                                              f32x4 (&S)[K / 32], f32x4 Xa, f32x4 Xb,
                                              Handoff32<K> &ho, int par, int lane)
 {
@@ -189,16 +209,18 @@ __device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, const Chunk32<K,
     __builtin_amdgcn_sched_barrier(0);
     nxt.template load_kreg<h>(f);
     __builtin_amdgcn_sched_barrier(0);
+    stage_eg<K, V, h>(o, ho, lane);     // the next chunk's exp(gam), loaded one step ago
 }
 
 template <int K, int V, int h, int AUX>
-__device__ __forceinline__ void chain_step(HalfFrag<K, V> &f, const Chunk32<K, V, AUX> &nxt,
+__device__ __forceinline__ void chain_step(HalfFrag<K, V> &f, HalfFrag<K, V> &o,
+                                           const Chunk32<K, V, AUX> &nxt,
                                            f32x4 (&S)[K / 32], Handoff32<K> &ho, int c,
                                            int par, int lane)
 {
     f32x4 Xa, Xb;
     chain_half_a<K, V, h>(f, S, Xa, Xb, ho, c % 3, par, lane);
-    chain_half_b<K, V, h, AUX>(f, nxt, S, Xa, Xb, ho, par, lane);
+    chain_half_b<K, V, h, AUX>(f, o, nxt, S, Xa, Xb, ho, par, lane);
 }
 
 // Chain wave h over the whole sequence: S rows [K/2 h, K/2 (h + 1)) from initial_state (or 0),
@@ -235,14 +257,15 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
         // drain the prologue loads: the loop header then carries only the loop's own pending
         // loads, and the waits inside the loop count back to the right group
         vm_drain();
+        stage_eg<K, V, h>(fa, ho, lane);    // chunk 1's is staged by step 0
         // no exit between the loop body's two steps: an exit there would merge a half-step
         // state into the loop header and make every iteration wait for the loads just issued
         int c = 0;
         for (; c + 2 <= nc; c += 2) {
-            chain_step<K, V, h, AUX>(fa, at(c + 2), S, ho, c, 0, lane);
-            chain_step<K, V, h, AUX>(fb, at(c + 3), S, ho, c + 1, 1, lane);
+            chain_step<K, V, h, AUX>(fa, fb, at(c + 2), S, ho, c, 0, lane);
+            chain_step<K, V, h, AUX>(fb, fa, at(c + 3), S, ho, c + 1, 1, lane);
         }
-        if (c < nc) chain_step<K, V, h, AUX>(fa, at(c + 2), S, ho, c, 0, lane);
+        if (c < nc) chain_step<K, V, h, AUX>(fa, fb, at(c + 2), S, ho, c, 0, lane);
         lds_barrier();    // barrier nc: delta of the last chunk is in the hand-off
     }
     if (p.ht) {
