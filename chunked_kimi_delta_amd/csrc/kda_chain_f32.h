@@ -45,7 +45,8 @@ struct ChainOps {
     f32x4 a[TPW];     // states, forward: w rows;  grads: kr rows     (A operand, 16 x 16)
     f32x4 at[TPW];    // states, forward: kr^T;    grads: qd^T        (A operand)
     f32x4 bt[TPW];    // grads: w^T;  forward: qd rows                (A operand)
-    f32x4 e[TPW];     // exp(gam) of the tile rows this lane holds
+    f32x4 e[TPW];     // exp(gam) of the tile rows this lane holds (staged from e1)
+    float e1;         // exp(gam) of row 16 TPW wave + lane % (16 TPW), as loaded
     f32x4 x;          // states, forward: u (C-layout);  grads: dO (C-layout)
     f32x4 m;          // grads: Mqk^T;  forward: Mqk rows             (A operand; wave 0 uses it)
 };
@@ -59,12 +60,12 @@ __device__ __forceinline__ void chain_load(ChainOps<K> &o, const float *ch, int 
     constexpr int TPW = ChainOps<K>::TPW;
     const int r = lane & 15, g = lane >> 4;
     const float *W = ch + WS::W / 4, *QD = ch + WS::QD / 4, *KR = ch + WS::KR / 4;
+    o.e1 = ch[WS::EG / 4 + wave * TPW * 16 + lane % (TPW * 16)];
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
         const int k0 = (wave * TPW + x) * 16;
         const float *ra = (GRAD ? KR : W) + r * K + k0 + 4 * g;
         o.a[x] = *(const f32x4 *)ra;
-        o.e[x] = *(const f32x4 *)(ch + WS::EG / 4 + k0 + 4 * g);
         if (FWD) o.bt[x] = *(const f32x4 *)(QD + r * K + k0 + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -103,6 +104,7 @@ __device__ __forceinline__ void chain_run(const FwdParams &p, int unit, int n0, 
     constexpr bool GRAD = MODE == CHAIN_GRADS, FWD = MODE == CHAIN_FORWARD;
     constexpr int TPW = ChainOps<K>::TPW;
     __shared__ f32x4 part[2][CHAIN_WAVES][FWD ? 2 : 1][64];
+    __shared__ float estage[CHAIN_WAVES][64];
     const int r = lane & 15, g = lane >> 4;
     const int j = unit % p.HV, s = unit / p.HV;
     const int64_t bos = seq_bos(p.seq, s), eos = seq_eos(p.seq, s, bos);
@@ -120,8 +122,18 @@ __device__ __forceinline__ void chain_run(const FwdParams &p, int unit, int n0, 
     for (int x = 0; x < TPW; ++x)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[x][i] = init ? init[unit_off + at(x, i)] : 0.f;
+    // exp(gam) of `op` from one value per lane to the C-layout rows of its tiles, through this
+    // wave's own LDS stage (its write and reads are ordered by the wave's LDS queue). A 16-byte
+    // load per tile fetched each value 16 times through the CU's vector-memory path (backward
+    // at 16 heads x 4096 tokens 0.62 -> 0.595 ms, fp32 forward state pass 257 -> 251 us).
+    auto stage_e = [&](ChainOps<K> &op) {
+        estage[wave][lane] = op.e1;
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) op.e[x] = *(const f32x4 *)&estage[wave][16 * x + 4 * g];
+    };
     // one chunk with the operands in `o` (loaded one chunk earlier)
-    auto step = [&](const ChainOps<K> &op, int it) {
+    auto step = [&](ChainOps<K> &op, int it) {
+        stage_e(op);
         const int c = GRAD ? nc - 1 - it : it;
         if (!FWD) {
             // the record of this chunk, tile order: [V/16 slice][K/16 tile][64 lanes][4], as
