@@ -146,13 +146,18 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, f32x4 (&S)
     if constexpr (h == 0) {
         // -U of both blocks is stored in the B layout of a 16x16x16 product (lane (n, g): rows
         // 4g .. 4g + 3 of column n), so the identity times it is -U in C layout, exactly: two
-        // matrix-core products instead of eight conversions in this wave's stream
+        // matrix-core products instead of eight conversions in this wave's stream. They are
+        // 16x16x32 products (the four upper k of each lane zero), the W S products' own shape:
+        // copies that fed a 16x16x16 result into a 16x16x32 accumulator four or five
+        // instructions later computed wrong sums (the compiler's wait for that pair is too
+        // short on this part); tests/test_codegen.py keeps the pair out of the library.
         const int n = lane & 15, g = lane >> 4;
-        f16x4 ih;
+        f16x8 ih;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ih[i] = (_Float16)(4 * g + i == n ? 1.f : 0.f);
-        Xa = mfma16(ih, __builtin_shufflevector(f.nu, f.nu, 0, 1, 2, 3), zero4());
-        Xb = mfma16(ih, __builtin_shufflevector(f.nu, f.nu, 4, 5, 6, 7), zero4());
+        for (int i = 0; i < 8; ++i) ih[i] = (_Float16)(i < 4 && 4 * g + i == n ? 1.f : 0.f);
+        const f16x4 z = {0, 0, 0, 0};
+        Xa = mfma32(ih, cat(__builtin_shufflevector(f.nu, f.nu, 0, 1, 2, 3), z), zero4());
+        Xb = mfma32(ih, cat(__builtin_shufflevector(f.nu, f.nu, 4, 5, 6, 7), z), zero4());
     } else {
         Xa = zero4();
         Xb = zero4();
