@@ -21,8 +21,11 @@
  *
  * Conventions
  *  - All tensor pointers are DEVICE pointers, caller-owned, contiguous (row-major), and
- *    16-byte aligned. The library allocates nothing, keeps no global state and is re-entrant
- *    (concurrent calls must use distinct workspaces and outputs).
+ *    16-byte aligned. The library allocates nothing (kda_fwd_noalloc's workspace is a static
+ *    device array of the library, see there); its only host-side state is a per-device cache
+ *    of the compute-unit count, read once and thread-safe. Calls are re-entrant: concurrent
+ *    calls must use distinct workspaces and outputs, and kda_fwd_noalloc calls that overlap on
+ *    one device race on its array.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream). Nothing
  *    synchronises; the caller owns synchronisation. Results are deterministic (no atomics).
  *  - Errors are reported only through the return value; nothing aborts or throws.
