@@ -303,8 +303,12 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
         Y0 = mfma32(f.qd[0][st], Sh[st], Y0);
         Y1 = mfma32(f.qd[1][st], Sh[st], Y1);
     }
-    const f32x4 O0 = mfma16(f.mqa, dh0, Y0);
-    const f32x4 O1 = mfma32(f.mqb, cat(dh0, dh1), Y1);
+    // both blocks accumulate onto the 16x16x32 products with a 16x16x32 product (block a's
+    // Mqk in the lower four k of each lane, zeros above): a 16x16x16 product taking a
+    // 16x16x32 result as its accumulator a few instructions later read it too early
+    const f16x8 d32 = cat(dh0, dh1);
+    const f32x4 O0 = mfma32(cat(f.mqa, f16x4{0, 0, 0, 0}), d32, Y0);
+    const f32x4 O1 = mfma32(f.mqb, d32, Y1);
     nxt.load_out(f);
     // C(O) holds four rows of one column per lane; the identity product C(O^T) holds four
     // consecutive columns of one row, so each block goes out as one 8-byte store per lane (the

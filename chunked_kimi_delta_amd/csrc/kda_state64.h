@@ -334,8 +334,11 @@ __device__ __forceinline__ void out_step64(PairOutFrag<K, V> &f, const Pair64<K,
         Y0 = mfma32(f.qd[0][st], Sh[st], Y0);
         Y1 = mfma32(f.qd[1][st], Sh[st], Y1);
     }
-    const f32x4 O0 = mfma16(f.mqa, da, Y0);
-    const f32x4 O1 = mfma32(f.mqb, cat(da, db), Y1);
+    // block a's Mqk product in the 16x16x32 shape of the products it accumulates onto (see
+    // the output step of kda_state32.h)
+    const f16x8 d32 = cat(da, db);
+    const f32x4 O0 = mfma32(cat(f.mqa, f16x4{0, 0, 0, 0}), d32, Y0);
+    const f32x4 O1 = mfma32(f.mqb, d32, Y1);
     nxt.template load_out<k>(f);
     const bf16x4 T0 = to_bf16x4(mfma16(to_bf16x4(O0), Ib, zero4()));
     const bf16x4 T1 = to_bf16x4(mfma16(to_bf16x4(O1), Ib, zero4()));

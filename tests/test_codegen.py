@@ -157,29 +157,32 @@ def test_forward_kernels_do_not_wait_on_each_load():
     assert not bad, bad
 
 
-# A 16x16x16 product whose result a 16x16x32 product takes as its accumulator (SrcC) a few
-# instructions later: copies of the state kernel with that pair four or five instructions
-# apart computed wrong sums for every such accumulator (parity failed by 0.14-0.5 relative),
-# while the same pair eight or more instructions apart, and pairs of one shape, were right. The
-# compiler's wait for it is too short on gfx950, so the library keeps the pair out entirely
-# (the state kernel forms -U with a 16x16x32 identity product instead).
+# One matrix-core product taking the result of a product of another shape as its accumulator
+# (SrcC) a few instructions later. Copies of the state kernel with a 16x16x16 result feeding a
+# 16x16x32 accumulator 3-8 instructions later, or a 16x16x32 result feeding a 16x16x16
+# accumulator in place 4-6 instructions later, computed wrong sums for those accumulators (o
+# off by 0.14-0.8 relative), while products of one shape chained back to back were always
+# right. The compiler's wait between two shapes is evidently too short on gfx950, so the
+# library keeps such pairs out (the state kernels form -U and the Mqk term with 16x16x32
+# products, zero-padded).
 MFMA = re.compile(r"^(v_mfma_\S+)\s+(.*)")
 
 
-def mfma_16_to_32_accumulator(asm: str, window: int = 12):
-    """(line, producer, consumer) for every v_mfma_*16x16x16* whose destination a
-    v_mfma_*16x16x32* reads as SrcC within `window` instructions."""
+def mfma_cross_shape_accumulator(asm: str, window: int = 12):
+    """(line, producer, consumer) for every v_mfma whose destination a v_mfma of another
+    opcode reads as SrcC within `window` instructions (registers rewritten in between end the
+    dependence)."""
     lines = [l.split(";")[0].strip() for l in asm.splitlines()]
     ins = [(i, l) for i, l in enumerate(lines) if l and not l.startswith(".") and not l.endswith(":")]
     hits = []
     for k, (i, l) in enumerate(ins):
         m = MFMA.match(l)
-        if not m or "16x16x16" not in m.group(1):
+        if not m:
             continue
         live = vregs(m.group(2).split(",")[0])      # registers still holding the product
         for _, nxt in ins[k + 1:k + 1 + window]:
             m2 = MFMA.match(nxt)
-            if m2 and "16x16x32" in m2.group(1):
+            if m2 and m2.group(1) != m.group(1):
                 ops = [x.strip() for x in m2.group(2).split(",")]
                 if len(ops) > 3 and vregs(ops[3]) & live:
                     hits.append((i, l, nxt))
@@ -192,20 +195,27 @@ def mfma_16_to_32_accumulator(asm: str, window: int = 12):
     return hits
 
 
-def test_detector_finds_a_16_to_32_accumulator():
+def test_detector_finds_a_cross_shape_accumulator():
     asm = "\n".join(["v_mfma_f32_16x16x16_f16 v[24:27], v[20:21], v[66:67], 0",
                      "s_add_i32 s0, s23, s0",
                      "v_mfma_f32_16x16x32_f16 v[24:27], v[42:45], v[28:31], v[24:27]",
                      "v_mfma_f32_16x16x32_f16 v[4:7], v[8:11], v[12:15], v[4:7]"])
-    assert len(mfma_16_to_32_accumulator(asm)) == 1
-    assert mfma_16_to_32_accumulator(asm.replace("16x16x16_f16", "16x16x32_f16")) == []
-    # the product's registers rewritten before the 16x16x32 reads them: no dependence
+    assert len(mfma_cross_shape_accumulator(asm)) == 1
+    # one shape chained: no hit
+    assert mfma_cross_shape_accumulator(asm.replace("16x16x16_f16", "16x16x32_f16")) == []
+    # the other direction, in place
+    rev = "\n".join(["v_mfma_f32_16x16x32_f16 v[10:13], v[10:13], v[46:49], v[18:21]",
+                      "v_cvt_pk_bf16_f32 v22, v38, s0",
+                      "v_mfma_f32_16x16x16_f16 v[10:13], v[76:77], v[50:51], v[10:13]"])
+    assert len(mfma_cross_shape_accumulator(rev)) == 1
+    # the product's registers rewritten before the other shape reads them: no dependence
     rewritten = asm.replace("s_add_i32 s0, s23, s0", "v_mov_b32_e32 v[24:27], 0")
-    assert mfma_16_to_32_accumulator(rewritten) == []
+    assert mfma_cross_shape_accumulator(rewritten) == []
 
 
 @pytest.mark.skipif(not HAVE_HIPCC, reason="hipcc not available")
-def test_no_16_to_32_mfma_accumulator_in_kernels():
-    bad = {os.path.basename(s): mfma_16_to_32_accumulator(a)[:3] for s, a in kernel_asms().items()}
+def test_no_cross_shape_mfma_accumulator_in_kernels():
+    bad = {os.path.basename(s): mfma_cross_shape_accumulator(a)[:3]
+           for s, a in kernel_asms().items()}
     bad = {k: v for k, v in bad.items() if v}
     assert not bad, bad
