@@ -7,8 +7,9 @@
 //     o     = QD S + Mqk delta             (32 x V), rows past the sequence end not stored
 //     S    <- diag(e^{gam}) S + KR^T delta
 //
-// One workgroup per (sequence, value head, 16-column slice of V), three waves on three SIMDs:
-// two chain waves that each own half of the key rows of S (fp32 registers) and one output wave.
+// Per (sequence, value head, 16-column slice of V) two chain waves that each own half of the
+// key rows of S (fp32 registers), and an output wave for the slice (or for two slices of the
+// unit in one workgroup, kda_state32.hip).
 // A chain step is split where the contraction over the key dimension allows it: each chain
 // wave forms its half of W S from its fp16 rows and hands the 32 x 16 fp32 partial to the
 // other through LDS; after the step's barrier both add the two partials (in the same order of
@@ -283,42 +284,6 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
     }
 }
 
-// Output wave, chunk c, after barrier c + 1: o = QD S + Mqk delta, stored as bf16. `nxt` is
-// the record two chunks ahead.
-template <int K, int V, int AUX>
-__device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V, AUX> &nxt,
-                                           const Handoff32<K> &ho, int slot, int par, int lane,
-                                           __amdgpu_buffer_rsrc_t orows, const int (&ooff)[2],
-                                           bf16x4 Ib)
-{
-    constexpr int NS = K / 32;
-    lds_barrier();
-    f16x8 Sh[NS];
-#pragma unroll
-    for (int st = 0; st < NS; ++st) Sh[st] = ho.sh[slot][st][lane];
-    const f16x4 dh0 = ho.dh[par][0][lane], dh1 = ho.dh[par][1][lane];
-    f32x4 Y0 = zero4(), Y1 = zero4();
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        Y0 = mfma32(f.qd[0][st], Sh[st], Y0);
-        Y1 = mfma32(f.qd[1][st], Sh[st], Y1);
-    }
-    // both blocks accumulate onto the 16x16x32 products with a 16x16x32 product (block a's
-    // Mqk in the lower four k of each lane, zeros above): a 16x16x16 product taking a
-    // 16x16x32 result as its accumulator a few instructions later read it too early
-    const f16x8 d32 = cat(dh0, dh1);
-    const f32x4 O0 = mfma32(cat(f.mqa, f16x4{0, 0, 0, 0}), d32, Y0);
-    const f32x4 O1 = mfma32(f.mqb, d32, Y1);
-    nxt.load_out(f);
-    // C(O) holds four rows of one column per lane; the identity product C(O^T) holds four
-    // consecutive columns of one row, so each block goes out as one 8-byte store per lane (the
-    // values are bf16 already, so the product changes none of them)
-    const bf16x4 T0 = to_bf16x4(mfma16(to_bf16x4(O0), Ib, zero4()));
-    const bf16x4 T1 = to_bf16x4(mfma16(to_bf16x4(O1), Ib, zero4()));
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T0), orows, ooff[0], 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T1), orows, ooff[1], 0, 0);
-}
-
 // Barrier schedule for nc chunks: every wave passes nc + 1 barriers. Barrier c (c < nc)
 // follows the chain waves' hand-off of chunk c (fp16 rows of S in slot c % 3, the W S
 // partials in slot c % 2); between barriers c and c+1 the chain waves form delta_c (half 0
@@ -328,61 +293,131 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
 // c+1 and c+2 respectively), each after its readers are done. The chain waves pass barrier nc
 // after their last update.
 
-// One V-slice (16 columns of S and o) of one (sequence, value head) unit, as three waves: role
-// 0 and 1 are the chain halves, role 2 the output wave; every role passes the same barriers.
-// AUX is the cache policy of the workspace loads.
+// The record base and chunk count of one (sequence, value head) unit.
 template <int K, int V, int AUX>
-__device__ __forceinline__ void state32_slice(const FwdParams &p, Handoff32<K> &ho, int unit,
-                                              int slice, int role, int lane)
-{
-    constexpr int CT = 32;
+struct Unit32 {
     using WS = WsBf16x32<K, V>;
-    const int grp = lane >> 4, n = lane & 15;
-    const int j = unit % p.HV;
-    const int s = unit / p.HV;
-    const int64_t bos = seq_bos(p.seq, s);
-    const int64_t eos = seq_eos(p.seq, s, bos);
-    const int nc = (int)((eos - bos + CT - 1) / CT);
-    const int col = 16 * slice + n;
-    const uint8_t *base =
-        p.ws + ((size_t)j * p.seq.n_slots + (size_t)(bos / CT + s)) * (size_t)WS::BYTES;
-    auto at = [&](int c) {
+    int j, s, nc;
+    int64_t bos, eos;
+    const uint8_t *base;
+    __device__ Unit32(const FwdParams &p, int unit) {
+        j = unit % p.HV;
+        s = unit / p.HV;
+        bos = seq_bos(p.seq, s);
+        eos = seq_eos(p.seq, s, bos);
+        nc = (int)((eos - bos + 31) / 32);
+        base = p.ws + ((size_t)j * p.seq.n_slots + (size_t)(bos / 32 + s)) * (size_t)WS::BYTES;
+    }
+    __device__ Chunk32<K, V, AUX> at(int c, int lane, int slice) const {
         return Chunk32<K, V, AUX>{
             buffer_rsrc(base + (size_t)min(c, nc - 1) * WS::BYTES, WS::BYTES), lane, slice};
-    };
-
-    if (role == 0) {
-        chain_wave<K, V, 0, AUX>(p, ho, base, nc, s, j, col, slice, lane);
-    } else if (role == 1) {
-        chain_wave<K, V, 1, AUX>(p, ho, base, nc, s, j, col, slice, lane);
-    } else if (nc > 0) {
-        const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)j * V * 2;
-        // after the transposing product lane (g, n) holds row n (block a) / 16 + n (block b),
-        // columns 16 slice + 4g .. + 3
-        const int ocol = 16 * slice + 4 * grp;
-        const int ooff[2] = {(int)(n * row_bytes + ocol * 2),
-                             (int)((16 + n) * row_bytes + ocol * 2)};
-        float eye[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) eye[i] = 4 * grp + i == n ? 1.f : 0.f;
-        const bf16x4 Ib = to_bf16x4(eye);
-        auto rows = [&](int c) {
-            const int64_t r0 = bos + CT * c;
-            const int64_t nv = eos - r0;
-            return rows_rsrc(p.o, r0, (int)(nv < CT ? nv : CT), row_bytes, head_bytes);
-        };
-        OutFrag32<K, V> fa, fb;
-        at(0).load_out(fa);
-        at(1).load_out(fb);
-        vm_drain();
-        lds_barrier();        // barrier 0
-        int c = 0;
-        for (; c + 2 <= nc; c += 2) {
-            out_step32<K, V, AUX>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff, Ib);
-            out_step32<K, V, AUX>(fb, at(c + 3), ho, (c + 1) % 3, 1, lane, rows(c + 1), ooff, Ib);
-        }
-        if (c < nc) out_step32<K, V, AUX>(fa, at(c + 2), ho, c % 3, 0, lane, rows(c), ooff, Ib);
     }
+};
+
+// Output wave, chunk c, after barrier c + 1, for OPW slices of one unit (handoffs ho[0 ..]):
+// o = QD S + Mqk delta of each, stored as bf16. The QD / Mqk operands are the same for every
+// slice of the unit, so an output wave serving two slices loads them once.
+template <int K, int V, int AUX, int OPW>
+__device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V, AUX> &nxt,
+                                           const Handoff32<K> *ho, int slot, int par, int lane,
+                                           __amdgpu_buffer_rsrc_t orows,
+                                           const int (&ooff)[OPW][2], bf16x4 Ib)
+{
+    constexpr int NS = K / 32;
+    lds_barrier();
+    f32x4 O0[OPW], O1[OPW];
+#pragma unroll
+    for (int q = 0; q < OPW; ++q) {
+        f16x8 Sh[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) Sh[st] = ho[q].sh[slot][st][lane];
+        const f16x4 dh0 = ho[q].dh[par][0][lane], dh1 = ho[q].dh[par][1][lane];
+        f32x4 Y0 = zero4(), Y1 = zero4();
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            Y0 = mfma32(f.qd[0][st], Sh[st], Y0);
+            Y1 = mfma32(f.qd[1][st], Sh[st], Y1);
+        }
+        // both blocks accumulate onto the 16x16x32 products with a 16x16x32 product (block a's
+        // Mqk in the lower four k of each lane, zeros above): a 16x16x16 product taking a
+        // 16x16x32 result as its accumulator a few instructions later read it too early
+        const f16x8 d32 = cat(dh0, dh1);
+        O0[q] = mfma32(cat(f.mqa, f16x4{0, 0, 0, 0}), d32, Y0);
+        O1[q] = mfma32(f.mqb, d32, Y1);
+    }
+    nxt.load_out(f);
+    // C(O) holds four rows of one column per lane; the identity product C(O^T) holds four
+    // consecutive columns of one row, so each block goes out as one 8-byte store per lane (the
+    // values are bf16 already, so the product changes none of them)
+#pragma unroll
+    for (int q = 0; q < OPW; ++q) {
+        const bf16x4 T0 = to_bf16x4(mfma16(to_bf16x4(O0[q]), Ib, zero4()));
+        const bf16x4 T1 = to_bf16x4(mfma16(to_bf16x4(O1[q]), Ib, zero4()));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T0), orows, ooff[q][0],
+                                              0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T1), orows, ooff[q][1],
+                                              0, 0);
+    }
+}
+
+// Chain half h of one V-slice (16 columns of S) of one (sequence, value head) unit.
+// AUX is the cache policy of the workspace loads.
+template <int K, int V, int AUX>
+__device__ __forceinline__ void state32_chain(const FwdParams &p, Handoff32<K> &ho,
+                                              const Unit32<K, V, AUX> &u, int slice, int h,
+                                              int lane)
+{
+    const int col = 16 * slice + (lane & 15);
+    if (h == 0)
+        chain_wave<K, V, 0, AUX>(p, ho, u.base, u.nc, u.s, u.j, col, slice, lane);
+    else
+        chain_wave<K, V, 1, AUX>(p, ho, u.base, u.nc, u.s, u.j, col, slice, lane);
+}
+
+// The output wave of OPW consecutive V-slices (slice0 ..) of one unit, whose hand-offs are
+// ho[0 .. OPW - 1]; it passes the same barriers as their chain waves.
+template <int K, int V, int AUX, int OPW>
+__device__ __forceinline__ void state32_out(const FwdParams &p, const Handoff32<K> *ho,
+                                            const Unit32<K, V, AUX> &u, int slice0, int lane)
+{
+    constexpr int CT = 32;
+    if (u.nc == 0) return;
+    const int grp = lane >> 4, n = lane & 15;
+    const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)u.j * V * 2;
+    // after the transposing product lane (g, n) holds row n (block a) / 16 + n (block b),
+    // columns 16 slice + 4g .. + 3
+    int ooff[OPW][2];
+#pragma unroll
+    for (int q = 0; q < OPW; ++q) {
+        const int ocol = 16 * (slice0 + q) + 4 * grp;
+        ooff[q][0] = (int)(n * row_bytes + ocol * 2);
+        ooff[q][1] = (int)((16 + n) * row_bytes + ocol * 2);
+    }
+    float eye[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = 4 * grp + i == n ? 1.f : 0.f;
+    const bf16x4 Ib = to_bf16x4(eye);
+    auto rows = [&](int c) {
+        const int64_t r0 = u.bos + CT * c;
+        const int64_t nv = u.eos - r0;
+        return rows_rsrc(p.o, r0, (int)(nv < CT ? nv : CT), row_bytes, head_bytes);
+    };
+    const int nc = u.nc;
+    OutFrag32<K, V> fa, fb;
+    u.at(0, lane, slice0).load_out(fa);
+    u.at(1, lane, slice0).load_out(fb);
+    vm_drain();
+    lds_barrier();        // barrier 0
+    int c = 0;
+    for (; c + 2 <= nc; c += 2) {
+        out_step32<K, V, AUX, OPW>(fa, u.at(c + 2, lane, slice0), ho, c % 3, 0, lane, rows(c),
+                                   ooff, Ib);
+        out_step32<K, V, AUX, OPW>(fb, u.at(c + 3, lane, slice0), ho, (c + 1) % 3, 1, lane,
+                                   rows(c + 1), ooff, Ib);
+    }
+    if (c < nc)
+        out_step32<K, V, AUX, OPW>(fa, u.at(c + 2, lane, slice0), ho, c % 3, 0, lane, rows(c),
+                                   ooff, Ib);
 }
 
 }  // namespace

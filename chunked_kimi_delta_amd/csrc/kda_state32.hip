@@ -4,25 +4,39 @@
 
 namespace kda {
 
-// SPW V-slices of one (sequence, value head) per workgroup, three waves each (two chain halves
-// and the output wave). With several slices per workgroup the slices pass their barriers
-// together and read each chunk record at the same time, so a record is fetched once per
-// workgroup instead of once per slice; with one slice per workgroup small launches spread over
-// more CUs.
+// SPW V-slices of one (sequence, value head) per workgroup: two chain waves per slice (the two
+// halves of its key rows) and one output wave per slice, or per two slices once a workgroup
+// holds several (their QD / Mqk operands are the same, so the pair's output wave loads them
+// once: 0.431 -> 0.388 ms at 4 x 8192 tokens x 32 value heads, 0.487 -> 0.440 ms for 8
+// packed sequences x 32 heads). With several slices per workgroup the slices pass their
+// barriers together and read each chunk record at the same time, so a record is fetched once
+// per workgroup instead of once per slice; with one slice per workgroup small launches spread
+// over more CUs.
+template <int SPW> constexpr int out_slices32() { return SPW == 1 ? 1 : 2; }
+template <int SPW> constexpr int waves32() {
+    return SPW / out_slices32<SPW>() * (2 * out_slices32<SPW>() + 1);
+}
+
 template <int K, int V, int SPW>
-__global__ __launch_bounds__(192 * SPW) void state32_bf16_kernel(FwdParams p)
+__global__ __launch_bounds__(64 * waves32<SPW>()) void state32_bf16_kernel(FwdParams p)
 {
-    constexpr int NV = V / 16, NG = NV / SPW;
+    constexpr int NV = V / 16, NG = NV / SPW, OPW = out_slices32<SPW>(), GW = 2 * OPW + 1;
     __shared__ Handoff32<K> hos[SPW];
     // the wave index is uniform per wave; readfirstlane makes that visible to the compiler,
     // so field offsets derived from it stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int sw = wave / 3, role = wave % 3;
     const int lane = threadIdx.x & 63;
     int unit, group;
     if (!state_unit32(blockIdx.x, NG, p.seq.N * p.HV, &unit, &group)) return;
-    const int slice = group * SPW + sw;
-    state32_slice<K, V, 0>(p, hos[sw], unit, slice, role, lane);
+    const Unit32<K, V, 0> u(p, unit);
+    // waves in groups of GW: the two chain halves of each of OPW slices, then their output wave
+    const int gi = wave / GW, r = wave % GW;
+    if (r < 2 * OPW) {
+        const int sw = gi * OPW + (r >> 1);
+        state32_chain<K, V, 0>(p, hos[sw], u, group * SPW + sw, r & 1, lane);
+    } else {
+        state32_out<K, V, 0, OPW>(p, &hos[gi * OPW], u, group * SPW + gi * OPW, lane);
+    }
 }
 
 template <int K, int V, int SPW>
@@ -31,7 +45,7 @@ static hipError_t launch_state32_spw(const FwdParams &p, hipStream_t st)
     const int64_t units = (int64_t)p.seq.N * p.HV;
     const int64_t nblk = (units + 7) / 8 * 8 * (V / 16 / SPW);
     if (nblk == 0) return hipSuccess;
-    state32_bf16_kernel<K, V, SPW><<<dim3((unsigned)nblk), dim3(192 * SPW), 0, st>>>(p);
+    state32_bf16_kernel<K, V, SPW><<<dim3((unsigned)nblk), dim3(64 * waves32<SPW>()), 0, st>>>(p);
     return hipGetLastError();
 }
 
