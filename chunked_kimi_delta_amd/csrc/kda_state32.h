@@ -48,7 +48,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void *o, int64_t row
 }
 
 // Operands of one chunk for the chain wave that owns key rows [K/2 h, K/2 (h + 1)).
-template <int K, int V>
+template <int K, int V, int CS = 1>
 struct HalfFrag {
     static constexpr int NSH = K / 64, NKH = K / 32;   // 32-row slabs and 16-row tiles owned
     f16x8 w[2][NSH];          // W rows of blocks a and b, this half's columns
@@ -56,7 +56,7 @@ struct HalfFrag {
     f32x4 eg[NKH];            // exp(gam) of the four rows 16t + 4g + i each lane holds
     float e1;                 // exp(gam) of row K/2 h + lane % (K/2) as loaded; it reaches eg
                               // through this wave's LDS stage one step later (stage_eg)
-    f16x8 nu;                 // -U of blocks a (0..3) and b (4..7), this slice (half 0 only)
+    f16x8 nu[CS];             // -U of blocks a (0..3) and b (4..7) of each slice (half 0 only)
 };
 
 template <int K, int V>
@@ -76,8 +76,8 @@ struct Chunk32 {
     static constexpr int NSH = HalfFrag<K, V>::NSH, NKH = HalfFrag<K, V>::NKH;
     __amdgpu_buffer_rsrc_t rs;
     int lane, slice;
-    template <int h>
-    __device__ __forceinline__ void load_w(HalfFrag<K, V> &f) const {
+    template <int h, int CS>
+    __device__ __forceinline__ void load_w(HalfFrag<K, V, CS> &f) const {
         // first, so that waiting for it (one step later) waits for no load issued after it
         f.e1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              rs, (lane % (K / 2)) * 4, WS::EG + h * (K / 2) * 4,
@@ -88,11 +88,15 @@ struct Chunk32 {
             for (int j = 0; j < NSH; ++j)
                 f.w[b][j] = __builtin_bit_cast(
                     f16x8, bload16<AUX>(rs, lane * 16, WS::W + (b * NS + h * NSH + j) * 1024));
-        if constexpr (h == 0)
-            f.nu = __builtin_bit_cast(f16x8, bload16<AUX>(rs, lane * 16, WS::NU + slice * 1024));
+        if constexpr (h == 0) {
+#pragma unroll
+            for (int q = 0; q < CS; ++q)
+                f.nu[q] = __builtin_bit_cast(
+                    f16x8, bload16<AUX>(rs, lane * 16, WS::NU + (slice + q) * 1024));
+        }
     }
-    template <int h>
-    __device__ __forceinline__ void load_kreg(HalfFrag<K, V> &f) const {
+    template <int h, int CS>
+    __device__ __forceinline__ void load_kreg(HalfFrag<K, V, CS> &f) const {
 #pragma unroll
         for (int t = 0; t < NKH; ++t)
             f.kr[t] = __builtin_bit_cast(f16x8,
@@ -125,8 +129,8 @@ struct Handoff32 {
 // A 16-byte load per tile had fetched every value 16 times through the CU's vector-memory path,
 // a quarter of the chain waves' operand traffic (46.4 -> 45.5 us at 16 heads x 4096 tokens,
 // 0.465 -> 0.428 ms at 4 x 8192 tokens x 32 value heads).
-template <int K, int V, int h>
-__device__ __forceinline__ void stage_eg(HalfFrag<K, V> &o, Handoff32<K> &ho, int lane)
+template <int K, int V, int h, int CS>
+__device__ __forceinline__ void stage_eg(HalfFrag<K, V, CS> &o, Handoff32<K> &ho, int lane)
 {
     ho.egs[h][lane] = o.e1;
 #pragma unroll
@@ -138,44 +142,61 @@ __device__ __forceinline__ void stage_eg(HalfFrag<K, V> &o, Handoff32<K> &ho, in
 // and including barrier c: fp16 rows to the hand-off and the partial of W S to the other half;
 // the decay of its rows by e^{gam} fills the W S products' latency. No load precedes the
 // barrier (loads issued here delayed both halves' arrival: 46.3 -> 47.9 us at 16 x 4096).
-template <int K, int V, int h>
-__device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, f32x4 (&S)[K / 32],
-                                             f32x4 &Xa, f32x4 &Xb, Handoff32<K> &ho, int slot,
+template <int K, int V, int h, int CS>
+__device__ __forceinline__ void chain_half_a(const HalfFrag<K, V, CS> &f,
+                                             f32x4 (&S)[CS][K / 32], f32x4 (&Xa)[CS],
+                                             f32x4 (&Xb)[CS], Handoff32<K> *ho, int slot,
                                              int par, int lane)
 {
     constexpr int NSH = K / 64;
-    if constexpr (h == 0) {
-        // -U of both blocks is stored in the B layout of a 16x16x16 product (lane (n, g): rows
-        // 4g .. 4g + 3 of column n), so the identity times it is -U in C layout, exactly: two
-        // matrix-core products instead of eight conversions in this wave's stream. They are
-        // 16x16x32 products (the four upper k of each lane zero), the W S products' own shape:
-        // copies that fed a 16x16x16 result into a 16x16x32 accumulator four or five
-        // instructions later computed wrong sums (the compiler's wait for that pair is too
-        // short on this part); tests/test_codegen.py keeps the pair out of the library.
-        const int n = lane & 15, g = lane >> 4;
-        f16x8 ih;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ih[i] = (_Float16)(i < 4 && 4 * g + i == n ? 1.f : 0.f);
-        const f16x4 z = {0, 0, 0, 0};
-        Xa = mfma32(ih, cat(__builtin_shufflevector(f.nu, f.nu, 0, 1, 2, 3), z), zero4());
-        Xb = mfma32(ih, cat(__builtin_shufflevector(f.nu, f.nu, 4, 5, 6, 7), z), zero4());
-    } else {
-        Xa = zero4();
-        Xb = zero4();
+    for (int q = 0; q < CS; ++q) {
+        if constexpr (h == 0) {
+            // -U of both blocks is stored in the B layout of a 16x16x16 product (lane (n, g):
+            // rows 4g .. 4g + 3 of column n), so the identity times it is -U in C layout,
+            // exactly: two matrix-core products instead of eight conversions in this wave's
+            // stream. They are 16x16x32 products (the four upper k of each lane zero), the
+            // W S products' own shape: copies that fed a 16x16x16 result into a 16x16x32
+            // accumulator four or five instructions later computed wrong sums (the compiler's
+            // wait for that pair is too short on this part); tests/test_codegen.py keeps the
+            // pair out of the library.
+            const int n = lane & 15, g = lane >> 4;
+            f16x8 ih;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ih[i] = (_Float16)(i < 4 && 4 * g + i == n ? 1.f : 0.f);
+            const f16x4 z = {0, 0, 0, 0};
+            Xa[q] = mfma32(ih, cat(__builtin_shufflevector(f.nu[q], f.nu[q], 0, 1, 2, 3), z),
+                           zero4());
+            Xb[q] = mfma32(ih, cat(__builtin_shufflevector(f.nu[q], f.nu[q], 4, 5, 6, 7), z),
+                           zero4());
+        } else {
+            Xa[q] = zero4();
+            Xb[q] = zero4();
+        }
     }
 #pragma unroll
-    for (int j = 0; j < NSH; ++j) {
-        const f16x8 Sh = cat(to_f16x4(S[2 * j]), to_f16x4(S[2 * j + 1]));
-        ho.sh[slot][h * NSH + j][lane] = Sh;
-        Xa = mfma32(f.w[0][j], Sh, Xa);
-        Xb = mfma32(f.w[1][j], Sh, Xb);
+    for (int j = 0; j < NSH; ++j)
+#pragma unroll
+        for (int q = 0; q < CS; ++q) {
+            const f16x8 Sh = cat(to_f16x4(S[q][2 * j]), to_f16x4(S[q][2 * j + 1]));
+            ho[q].sh[slot][h * NSH + j][lane] = Sh;
+            Xa[q] = mfma32(f.w[0][j], Sh, Xa[q]);
+            Xb[q] = mfma32(f.w[1][j], Sh, Xb[q]);
+        }
+    // the decay behind every W S product (left to itself the compiler put some of it ahead of
+    // the first product, on the chain: 45.3 against 46.4 us at 16 heads x 4096 tokens)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < CS; ++q)
+#pragma unroll
+        for (int t = 0; t < K / 32; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[q][t][i] *= f.eg[t][i];
+#pragma unroll
+    for (int q = 0; q < CS; ++q) {
+        ho[q].xp[par][h][0][lane] = Xa[q];
+        ho[q].xp[par][h][1][lane] = Xb[q];
     }
-#pragma unroll
-    for (int t = 0; t < K / 32; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] *= f.eg[t][i];
-    ho.xp[par][h][0][lane] = Xa;
-    ho.xp[par][h][1][lane] = Xb;
     lds_barrier();
 }
 
@@ -186,55 +207,66 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V> &f, f32x4 (&S)
 // its exp(gam) tiles from its staged value. The scheduling barriers keep the compiler from
 // moving the refills between the update products, where their issue delayed the next step
 // (48.8 -> 46.3 us per launch at 16 x 4096, 0.474 -> 0.461 ms at 4 x 8192 x 32 heads).
-template <int K, int V, int h, int AUX>
-__device__ __forceinline__ void chain_half_b(HalfFrag<K, V> &f, HalfFrag<K, V> &o,
+template <int K, int V, int h, int AUX, int CS>
+__device__ __forceinline__ void chain_half_b(HalfFrag<K, V, CS> &f, HalfFrag<K, V, CS> &o,
                                              const Chunk32<K, V, AUX> &nxt,
-                                             f32x4 (&S)[K / 32], f32x4 Xa, f32x4 Xb,
-                                             Handoff32<K> &ho, int par, int lane)
+                                             f32x4 (&S)[CS][K / 32], const f32x4 (&Xa)[CS],
+                                             const f32x4 (&Xb)[CS], Handoff32<K> *ho, int par,
+                                             int lane)
 {
     constexpr int NKH = K / 32;
-    const f32x4 Pa = ho.xp[par][1 - h][0][lane], Pb = ho.xp[par][1 - h][1][lane];
-    __builtin_amdgcn_sched_barrier(0);
-    nxt.template load_w<h>(f);
-    __builtin_amdgcn_sched_barrier(0);
-    f16x4 dh0, dh1;
+    f32x4 Pa[CS], Pb[CS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // half 0 adds (own + other) and half 1 (other + own): the same two fp32 operands, so
-        // both halves round to the same delta
-        dh0[i] = (_Float16)(-(Xa[i] + Pa[i]));
-        dh1[i] = (_Float16)(-(Xb[i] + Pb[i]));
+    for (int q = 0; q < CS; ++q) {
+        Pa[q] = ho[q].xp[par][1 - h][0][lane];
+        Pb[q] = ho[q].xp[par][1 - h][1][lane];
     }
-    if constexpr (h == 0) {
-        ho.dh[par][0][lane] = dh0;
-        ho.dh[par][1][lane] = dh1;
-    }
-    const f16x8 d32 = cat(dh0, dh1);
+    __builtin_amdgcn_sched_barrier(0);
+    nxt.template load_w<h, CS>(f);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < NKH; ++t) S[t] = mfma32(f.kr[t], d32, S[t]);
+    for (int q = 0; q < CS; ++q) {
+        f16x4 dh0, dh1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // half 0 adds (own + other) and half 1 (other + own): the same two fp32 operands,
+            // so both halves round to the same delta
+            dh0[i] = (_Float16)(-(Xa[q][i] + Pa[q][i]));
+            dh1[i] = (_Float16)(-(Xb[q][i] + Pb[q][i]));
+        }
+        if constexpr (h == 0) {
+            ho[q].dh[par][0][lane] = dh0;
+            ho[q].dh[par][1][lane] = dh1;
+        }
+        const f16x8 d32 = cat(dh0, dh1);
+#pragma unroll
+        for (int t = 0; t < NKH; ++t) S[q][t] = mfma32(f.kr[t], d32, S[q][t]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    nxt.template load_kreg<h>(f);
+    nxt.template load_kreg<h, CS>(f);
     __builtin_amdgcn_sched_barrier(0);
-    stage_eg<K, V, h>(o, ho, lane);     // the next chunk's exp(gam), loaded one step ago
+    stage_eg<K, V, h, CS>(o, ho[0], lane);     // the next chunk's exp(gam), loaded one step ago
 }
 
-template <int K, int V, int h, int AUX>
-__device__ __forceinline__ void chain_step(HalfFrag<K, V> &f, HalfFrag<K, V> &o,
+template <int K, int V, int h, int AUX, int CS>
+__device__ __forceinline__ void chain_step(HalfFrag<K, V, CS> &f, HalfFrag<K, V, CS> &o,
                                            const Chunk32<K, V, AUX> &nxt,
-                                           f32x4 (&S)[K / 32], Handoff32<K> &ho, int c,
+                                           f32x4 (&S)[CS][K / 32], Handoff32<K> *ho, int c,
                                            int par, int lane)
 {
-    f32x4 Xa, Xb;
-    chain_half_a<K, V, h>(f, S, Xa, Xb, ho, c % 3, par, lane);
-    chain_half_b<K, V, h, AUX>(f, o, nxt, S, Xa, Xb, ho, par, lane);
+    f32x4 Xa[CS], Xb[CS];
+    chain_half_a<K, V, h, CS>(f, S, Xa, Xb, ho, c % 3, par, lane);
+    chain_half_b<K, V, h, AUX, CS>(f, o, nxt, S, Xa, Xb, ho, par, lane);
 }
 
-// Chain wave h over the whole sequence: S rows [K/2 h, K/2 (h + 1)) from initial_state (or 0),
-// the chunk loop, barrier nc, and the final state.
-template <int K, int V, int h, int AUX>
-__device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
-                                           const uint8_t *base, int nc, int s, int j, int col,
-                                           int slice, int lane)
+// Chain wave h of CS consecutive slices (slice ..) over the whole sequence: their S rows
+// [K/2 h, K/2 (h + 1)) from initial_state (or 0), the chunk loop, barrier nc, and the final
+// state. The slices share every operand but -U, so one wave serving two loads W, KR and e^gam
+// once for both.
+template <int K, int V, int h, int AUX, int CS>
+__device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> *ho,
+                                           const uint8_t *base, int nc, int s, int j, int slice,
+                                           int lane)
 {
     constexpr int NKH = K / 32;
     using WS = WsBf16x32<K, V>;
@@ -244,43 +276,51 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> &ho,
         return Chunk32<K, V, AUX>{
             buffer_rsrc(base + (size_t)min(c, nc - 1) * WS::BYTES, WS::BYTES), lane, slice};
     };
-    f32x4 S[NKH];
-    if (p.h0) {
-        const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+    f32x4 S[CS][NKH];
 #pragma unroll
-        for (int t = 0; t < NKH; ++t)
+    for (int q = 0; q < CS; ++q) {
+        const int col = 16 * (slice + q) + (lane & 15);
+        if (p.h0) {
+            const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + col;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[t][i] = h0[(size_t)(row0 + 16 * t + 4 * grp + i) * V];
-    } else {
+            for (int t = 0; t < NKH; ++t)
 #pragma unroll
-        for (int t = 0; t < NKH; ++t) S[t] = zero4();
+                for (int i = 0; i < 4; ++i)
+                    S[q][t][i] = h0[(size_t)(row0 + 16 * t + 4 * grp + i) * V];
+        } else {
+#pragma unroll
+            for (int t = 0; t < NKH; ++t) S[q][t] = zero4();
+        }
     }
     if (nc > 0) {
-        HalfFrag<K, V> fa, fb;
-        at(0).template load_w<h>(fa); at(0).template load_kreg<h>(fa);
-        at(1).template load_w<h>(fb); at(1).template load_kreg<h>(fb);
+        HalfFrag<K, V, CS> fa, fb;
+        at(0).template load_w<h, CS>(fa); at(0).template load_kreg<h, CS>(fa);
+        at(1).template load_w<h, CS>(fb); at(1).template load_kreg<h, CS>(fb);
         // drain the prologue loads: the loop header then carries only the loop's own pending
         // loads, and the waits inside the loop count back to the right group
         vm_drain();
-        stage_eg<K, V, h>(fa, ho, lane);    // chunk 1's is staged by step 0
+        stage_eg<K, V, h, CS>(fa, ho[0], lane);    // chunk 1's is staged by step 0
         // no exit between the loop body's two steps: an exit there would merge a half-step
         // state into the loop header and make every iteration wait for the loads just issued
         int c = 0;
         for (; c + 2 <= nc; c += 2) {
-            chain_step<K, V, h, AUX>(fa, fb, at(c + 2), S, ho, c, 0, lane);
-            chain_step<K, V, h, AUX>(fb, fa, at(c + 3), S, ho, c + 1, 1, lane);
+            chain_step<K, V, h, AUX, CS>(fa, fb, at(c + 2), S, ho, c, 0, lane);
+            chain_step<K, V, h, AUX, CS>(fb, fa, at(c + 3), S, ho, c + 1, 1, lane);
         }
-        if (c < nc) chain_step<K, V, h, AUX>(fa, fb, at(c + 2), S, ho, c, 0, lane);
+        if (c < nc) chain_step<K, V, h, AUX, CS>(fa, fb, at(c + 2), S, ho, c, 0, lane);
         lds_barrier();    // barrier nc: delta of the last chunk is in the hand-off
     }
     if (p.ht) {
-        float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
 #pragma unroll
-        for (int t = 0; t < NKH; ++t)
+        for (int q = 0; q < CS; ++q) {
+            const int col = 16 * (slice + q) + (lane & 15);
+            float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ht[(size_t)(row0 + 16 * t + 4 * grp + i) * V] = S[t][i];
+            for (int t = 0; t < NKH; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ht[(size_t)(row0 + 16 * t + 4 * grp + i) * V] = S[q][t][i];
+        }
     }
 }
 
@@ -360,18 +400,17 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
     }
 }
 
-// Chain half h of one V-slice (16 columns of S) of one (sequence, value head) unit.
+// Chain half h of CS consecutive V-slices (slice ..) of one unit, with hand-offs ho[0 ..].
 // AUX is the cache policy of the workspace loads.
-template <int K, int V, int AUX>
-__device__ __forceinline__ void state32_chain(const FwdParams &p, Handoff32<K> &ho,
+template <int K, int V, int AUX, int CS>
+__device__ __forceinline__ void state32_chain(const FwdParams &p, Handoff32<K> *ho,
                                               const Unit32<K, V, AUX> &u, int slice, int h,
                                               int lane)
 {
-    const int col = 16 * slice + (lane & 15);
     if (h == 0)
-        chain_wave<K, V, 0, AUX>(p, ho, u.base, u.nc, u.s, u.j, col, slice, lane);
+        chain_wave<K, V, 0, AUX, CS>(p, ho, u.base, u.nc, u.s, u.j, slice, lane);
     else
-        chain_wave<K, V, 1, AUX>(p, ho, u.base, u.nc, u.s, u.j, col, slice, lane);
+        chain_wave<K, V, 1, AUX, CS>(p, ho, u.base, u.nc, u.s, u.j, slice, lane);
 }
 
 // The output wave of OPW consecutive V-slices (slice0 ..) of one unit, whose hand-offs are

@@ -4,23 +4,30 @@
 
 namespace kda {
 
-// SPW V-slices of one (sequence, value head) per workgroup: two chain waves per slice (the two
-// halves of its key rows) and one output wave per slice, or per two slices once a workgroup
-// holds several (their QD / Mqk operands are the same, so the pair's output wave loads them
-// once: 0.431 -> 0.388 ms at 4 x 8192 tokens x 32 value heads, 0.487 -> 0.440 ms for 8
-// packed sequences x 32 heads). With several slices per workgroup the slices pass their
-// barriers together and read each chunk record at the same time, so a record is fetched once
-// per workgroup instead of once per slice; with one slice per workgroup small launches spread
-// over more CUs.
-template <int SPW> constexpr int out_slices32() { return SPW == 1 ? 1 : 2; }
+// SPW V-slices of one (sequence, value head) per workgroup. Each slice has two chain halves
+// (the two halves of its key rows) and an output wave; the slices of a unit share every operand
+// but -U, so once a workgroup holds several, one output wave serves two slices (QD / Mqk loaded
+// once: 0.431 -> 0.388 ms at 4 x 8192 tokens x 32 value heads, 0.487 -> 0.440 ms for 8 packed
+// sequences x 32 heads) and, with four, one chain wave serves the same half of two slices (W,
+// KR, e^gam loaded once: 0.392 -> 0.330 ms at 4 x 8192 x 32; with two slices per workgroup it
+// lengthened each step of the packed sequences' longest units, 0.440 -> 0.484 ms). With several
+// slices per workgroup the slices pass their barriers together and read each chunk record at
+// the same time, so a record is fetched once per workgroup instead of once per slice; with one
+// slice per workgroup small launches spread over more CUs.
+template <int SPW> constexpr int out_slices32() { return SPW == 1 ? 1 : 2; }     // per output wave
+template <int SPW> constexpr int chain_slices32() { return SPW == 4 ? 2 : 1; }   // per chain wave
+template <int SPW> constexpr int group_waves32() {
+    return 2 * (out_slices32<SPW>() / chain_slices32<SPW>()) + 1;
+}
 template <int SPW> constexpr int waves32() {
-    return SPW / out_slices32<SPW>() * (2 * out_slices32<SPW>() + 1);
+    return SPW / out_slices32<SPW>() * group_waves32<SPW>();
 }
 
 template <int K, int V, int SPW>
 __global__ __launch_bounds__(64 * waves32<SPW>()) void state32_bf16_kernel(FwdParams p)
 {
-    constexpr int NV = V / 16, NG = NV / SPW, OPW = out_slices32<SPW>(), GW = 2 * OPW + 1;
+    constexpr int NV = V / 16, NG = NV / SPW, OPW = out_slices32<SPW>(),
+                  CS = chain_slices32<SPW>(), GW = group_waves32<SPW>();
     __shared__ Handoff32<K> hos[SPW];
     // the wave index is uniform per wave; readfirstlane makes that visible to the compiler,
     // so field offsets derived from it stay scalar
@@ -29,11 +36,12 @@ __global__ __launch_bounds__(64 * waves32<SPW>()) void state32_bf16_kernel(FwdPa
     int unit, group;
     if (!state_unit32(blockIdx.x, NG, p.seq.N * p.HV, &unit, &group)) return;
     const Unit32<K, V, 0> u(p, unit);
-    // waves in groups of GW: the two chain halves of each of OPW slices, then their output wave
+    // waves in groups of GW per OPW slices: the two chain halves of each CS of them, then the
+    // group's output wave
     const int gi = wave / GW, r = wave % GW;
-    if (r < 2 * OPW) {
-        const int sw = gi * OPW + (r >> 1);
-        state32_chain<K, V, 0>(p, hos[sw], u, group * SPW + sw, r & 1, lane);
+    if (r < GW - 1) {
+        const int sw = gi * OPW + (r >> 1) * CS;
+        state32_chain<K, V, 0, CS>(p, &hos[sw], u, group * SPW + sw, r & 1, lane);
     } else {
         state32_out<K, V, 0, OPW>(p, &hos[gi * OPW], u, group * SPW + gi * OPW, lane);
     }

@@ -124,7 +124,8 @@ def load_then_full_wait(asm: str, window: int = 3):
     ins = [(i, l) for i, l in enumerate(lines) if l and not l.startswith(".") and not l.endswith(":")]
     out = []
     for n, (i, l) in enumerate(ins):
-        if l.startswith("s_waitcnt") and "vmcnt(0)" in l:
+        # a kernel's deliberate drain (vm_drain: "vmcnt(0) expcnt(6)") is not this pattern
+        if l.startswith("s_waitcnt") and "vmcnt(0)" in l and "expcnt(6)" not in l:
             for _, p in ins[max(0, n - window):n]:
                 if re.match(r"(global|buffer|flat)_load", p):
                     out.append((i, p))
@@ -137,6 +138,7 @@ def test_detector_finds_a_load_then_full_wait():
                      "s_waitcnt vmcnt(0)", "v_lshlrev_b32_e32 v1, 16, v1"])
     assert len(load_then_full_wait(asm)) == 1
     assert load_then_full_wait(asm.replace("vmcnt(0)", "vmcnt(3)")) == []
+    assert load_then_full_wait(asm.replace("vmcnt(0)", "vmcnt(0) expcnt(6)")) == []
 
 
 # Forward kernels: their loads are issued unconditionally and converted where they are used,
