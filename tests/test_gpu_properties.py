@@ -10,6 +10,8 @@
   packed          packed sequences (cu_seqlens) give bit for bit what each sequence gives as
                   a batch of its own (chunk slots, workgroup maps and launch shapes differ; the
                   arithmetic of a (sequence, head) unit does not)
+  slice grouping  a launch large enough for several V-slices per workgroup gives bit for bit
+                  what one slice per workgroup gives (each sequence run alone)
 """
 from __future__ import annotations
 
@@ -88,3 +90,20 @@ def test_packed_equals_per_sequence(chunk):
                        inp.scale, h0=inp.h0[s:s + 1], chunk=chunk)
         assert torch.equal(o[:, a:b], o_s), f"o of sequence {s} differs from its own run"
         assert torch.equal(f[s:s + 1], f_s), f"final state of sequence {s} differs"
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_slice_grouping_bitwise(chunk):
+    # 4 sequences x 32 value heads: 1,024 16-column slices, so the state kernel puts four slices
+    # of a unit in one workgroup (chain and output waves serving two slices each at chunk 32);
+    # each sequence alone (256 slices) runs one slice per workgroup. The arithmetic of a slice
+    # is the same either way, so the results agree bit for bit.
+    w = W.custom(B=4, T=300, H=16, HV=32, K=128, V=128, h0_std=0.1)
+    inp = W.make_inputs(w, seed=9)
+    o, f = run(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, h0=inp.h0, chunk=chunk)
+    for b in range(w.B):
+        one = lambda x: x[b:b + 1].contiguous()
+        o_b, f_b = run(one(inp.q), one(inp.k), one(inp.v), one(inp.g), one(inp.beta),
+                       inp.scale, h0=inp.h0[b:b + 1], chunk=chunk)
+        assert torch.equal(o[b:b + 1], o_b), f"o of sequence {b} differs from its own run"
+        assert torch.equal(f[b:b + 1], f_b), f"final state of sequence {b} differs"
