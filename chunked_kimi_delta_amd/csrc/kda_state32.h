@@ -8,8 +8,9 @@
 //     S    <- diag(e^{gam}) S + KR^T delta
 //
 // Per (sequence, value head, 16-column slice of V) two chain waves that each own half of the
-// key rows of S (fp32 registers), and an output wave for the slice (or for two slices of the
-// unit in one workgroup, kda_state32.hip).
+// key rows of S (fp32 registers), and an output wave. With several slices of a unit in one
+// workgroup an output wave, and with four a chain wave too, serves two slices, whose operands
+// are the same but for -U (kda_state32.hip).
 // A chain step is split where the contraction over the key dimension allows it: each chain
 // wave forms its half of W S from its fp16 rows and hands the 32 x 16 fp32 partial to the
 // other through LDS; after the step's barrier both add the two partials (in the same order of
