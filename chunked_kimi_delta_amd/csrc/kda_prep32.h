@@ -215,17 +215,38 @@ __device__ __forceinline__ void prep32_chunk(const FwdParams &p, Prep32Share<K, 
 
     // ---------------------------------------------------------------- cumsum over 32 tokens
     float G2[NK][4];
+    if (!gated) {
+        // The block's running sums on the matrix core: the identity product turns the TPL tile
+        // of g into C layout (lane (g, n): tokens 4g .. 4g + 3 of column n), which read as an A
+        // operand is g^T; times the upper-triangular ones matrix T (T[s][t] = 1 for s <= t) it
+        // gives C(g^T T), whose lane (g, r) holds the sums over tokens 0 .. r of columns
+        // 4g .. 4g + 3: TPL again. g is bf16, so both products are exact up to the fp32 sums.
+        // (A DPP scan per element cost about nine VALU instructions and hazard waits each.)
+        float eye[4], up[4];
 #pragma unroll
-    for (int c = 0; c < NK; ++c) {
-        float gl[4];
-        unpack_bf16x4(gr[c], gl);
-        if (gated) {
+        for (int i = 0; i < 4; ++i) {
+            eye[i] = 4 * grp + i == r ? 1.f : 0.f;
+            up[i] = 4 * grp + i <= r ? 1.f : 0.f;
+        }
+        const bf16x4 Ib = to_bf16x4(eye), Tb = to_bf16x4(up);
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            const f32x4 gc = mfma16(__builtin_bit_cast(bf16x4, gr[c]), Ib, zero4());
+            const f32x4 cs = mfma16(to_bf16x4(gc), Tb, zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G2[c][i] = cs[i] * LOG2E;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            float gl[4];
+            unpack_bf16x4(gr[c], gl);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 gl[i] = r < in.nrows ? gate_activation(p.pre, gl[i] + dtv[c][i], aexp) : 0.f;
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[i] * LOG2E);
+            for (int i = 0; i < 4; ++i) G2[c][i] = row_inclusive_scan(gl[i] * LOG2E);
+        }
     }
     if (wave == 0) {
         if (r == 15) {
