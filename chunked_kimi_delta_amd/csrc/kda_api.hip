@@ -47,10 +47,53 @@ size_t record_bytes(int K, int V)
                    : (V == 64 ? WS<128, 64>::BYTES : WS<128, 128>::BYTES);
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Share of a sequence's chunks given to segment A of the two-segment state pass, in parts per
+// thousand. Segment A's workgroups hold one value slice, segment B's two (a value slice and a
+// transition slice sharing every chunk operand); measured at 16 heads x 4096 tokens, a chunk
+// step takes about 355 ns with one slice per workgroup and 534 ns with two, so A takes
+// 534 / (355 + 534) of the chunks for both segments to end together.
+#ifndef KDA_SPLIT_A_PERMILLE
+#define KDA_SPLIT_A_PERMILLE 600
+#endif
+
+// The two-segment state pass (Split32) and its scratch after the chunk records: bf16 io,
+// 32-token chunks, dense sequences of at least 16 chunks, K == V, and a batch whose value
+// slices (N HV V / 16 workgroups of the one-segment pass) fill at most half of the compute
+// units, so that both segments' workgroups run at once, one per CU.
+struct SplitPlan {
+    int c0 = 0, nb = 0;
+    size_t smf = 0, phf = 0, o0 = 0, y = 0, end = 0;   // byte offsets in the workspace
+};
+
+SplitPlan split_plan(const kda_fwd_args *a, int ct, size_t records)
+{
+    SplitPlan sp;
+    if (ct != 32 || a->io != KDA_BF16 || a->cu_seqlens || a->K != a->V || a->T < 512)
+        return sp;
+    const int64_t units = (int64_t)a->N * a->HV;
+    if (2 * units * (a->V / 16) > (int64_t)current_device_cus()) return sp;
+    const int64_t nc = ((int64_t)a->T + 31) / 32;
+    int64_t c0 = (nc * KDA_SPLIT_A_PERMILLE + 500) / 1000;
+    c0 = c0 < 1 ? 1 : (c0 > nc - 1 ? nc - 1 : c0);
+    const int64_t nb = nc - c0;
+    const size_t o0_unit = (size_t)nb * 32 * a->V * 2, y_unit = (size_t)nb * 32 * a->K * 2;
+    if (o0_unit >= (1u << 31)) return sp;      // per-unit buffer resources stay 32-bit
+    sp.c0 = (int)c0;
+    sp.nb = (int)nb;
+    sp.smf = align256(records);
+    sp.phf = sp.smf + align256((size_t)units * a->K * a->V * 2);
+    sp.o0 = sp.phf + align256((size_t)units * a->K * a->K * 2);
+    sp.y = sp.o0 + align256((size_t)units * o0_unit);
+    sp.end = sp.y + align256((size_t)units * y_unit);
+    return sp;
+}
+
 // Returns KDA_OK and fills the derived sizes (`need`: workspace bytes), or the status kda_fwd
 // must return.
 kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots,
-                        size_t *need, int *chunk)
+                        size_t *need, int *chunk, SplitPlan *split = nullptr)
 {
     if (!a) return KDA_ERR_INVALID_ARG;
     if (a->B < 1 || a->T < 0 || a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H)
@@ -87,6 +130,9 @@ kda_status check_shapes(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slot
     *n_slots = ns;
     *need = (size_t)ns * (size_t)a->HV * cb;
     *chunk = ct;
+    const SplitPlan sp = split_plan(a, ct, *need);
+    if (sp.c0 > 0) *need = sp.end;
+    if (split) *split = sp;
     return KDA_OK;
 }
 
@@ -136,7 +182,8 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     int64_t tt, ns;
     size_t need;
     int ct;
-    const kda_status st = check_shapes(a, &tt, &ns, &need, &ct);
+    SplitPlan sp;
+    const kda_status st = check_shapes(a, &tt, &ns, &need, &ct, &sp);
     if (st != KDA_OK) return st;
     if (a->N > 0 || tt > 0) {
         const void *ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
@@ -177,6 +224,15 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
     p.pre.lower_bound = a->gate_lower_bound;
     p.pre.A_log = a->A_log;
     p.pre.dt_bias = a->dt_bias;
+    if (sp.c0 > 0) {
+        uint8_t *w = (uint8_t *)workspace;
+        p.split.c0 = sp.c0;
+        p.split.nb = sp.nb;
+        p.split.smf = (_Float16 *)(w + sp.smf);
+        p.split.phf = (_Float16 *)(w + sp.phf);
+        p.split.o0 = (_Float16 *)(w + sp.o0);
+        p.split.y = (_Float16 *)(w + sp.y);
+    }
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -195,8 +251,6 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
 struct BwdLayout {
     size_t rec, ck_S, ck_L, part_q, part_k, part_A, part_dt, total;
 };
-
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Shape checks of the backward (the forward's, at chunk 16) and its workspace layout.
 kda_status check_bwd(const kda_fwd_args *a, int64_t *T_total, int64_t *n_slots, BwdLayout *L)

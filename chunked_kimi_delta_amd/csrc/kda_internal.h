@@ -58,6 +58,26 @@ struct Prestage {
     const float *dt_bias;                    // [HV, K] or nullptr
 };
 
+// Two-segment state pass of the 32-token path, for dense batches whose state slices would
+// leave at least half of the compute units idle: segment A (chunks [0, c0)) runs from the
+// initial state as usual and leaves its end state S_A in s_mid; at the same time segment B
+// (chunks [c0, c0 + nb)) runs from a zero state, and next to it its transition from the
+// identity (the K x K state of the same recurrence with U = 0). The state is affine in the
+// state at a segment's start ("手撕KDA" section 1: S_c = diag(e^gam) S + KR^T (U - W S) per
+// chunk), so for every token of B the output is o0 + y S_A and the final state is
+// S0_end + phi S_A, which a third kernel forms. S_A and phi are kept as the fp16 operand
+// fragments of those products (the precision of the chain's own S operand).
+struct Split32 {
+    int32_t c0 = 0;             // chunks of segment A; 0: one segment
+    int32_t nb = 0;             // chunks of segment B (the same for every sequence)
+    _Float16 *smf = nullptr;    // [N][HV][V/16][K/32][64 lanes][8]: S_A as 16x16x32 B operands
+                                // (lane (g, n): rows 32 t + 16 (e / 4) + 4g + e % 4, column n)
+    _Float16 *phf = nullptr;    // [N][HV][K/16 row tiles][K/16 column slices][64][4]: phi tile
+                                // transposed (lane (g, m): row m, columns 4g .. 4g + 3)
+    _Float16 *o0 = nullptr;     // [N][HV][nb][2 blocks][V/16][64 lanes][4] C(O^T) from zero
+    _Float16 *y = nullptr;      // [N][HV][nb][2][K/16][64][4] C(Y^T): the transition's output
+};
+
 struct FwdParams {
     SeqGeom seq;
     int32_t H, HV, G;
@@ -69,6 +89,7 @@ struct FwdParams {
     uint8_t *ws;
     Prestage pre;
     const void *d_o = nullptr;   // backward only: d loss / d o, copied into the chunk records
+    Split32 split;
 };
 
 // Arguments of the backward: the forward's (f.ws holds the fp32 chunk records), the incoming

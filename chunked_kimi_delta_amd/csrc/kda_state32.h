@@ -77,7 +77,7 @@ struct Chunk32 {
     static constexpr int NSH = HalfFrag<K, V>::NSH, NKH = HalfFrag<K, V>::NKH;
     __amdgpu_buffer_rsrc_t rs;
     int lane, slice;
-    template <int h, int CS>
+    template <int h, int CS, bool IDN = false>
     __device__ __forceinline__ void load_w(HalfFrag<K, V, CS> &f) const {
         // first, so that waiting for it (one step later) waits for no load issued after it
         f.e1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -89,7 +89,7 @@ struct Chunk32 {
             for (int j = 0; j < NSH; ++j)
                 f.w[b][j] = __builtin_bit_cast(
                     f16x8, bload16<AUX>(rs, lane * 16, WS::W + (b * NS + h * NSH + j) * 1024));
-        if constexpr (h == 0) {
+        if constexpr (h == 0 && !IDN) {
 #pragma unroll
             for (int q = 0; q < CS; ++q)
                 f.nu[q] = __builtin_bit_cast(
@@ -143,7 +143,7 @@ __device__ __forceinline__ void stage_eg(HalfFrag<K, V, CS> &o, Handoff32<K> &ho
 // and including barrier c: fp16 rows to the hand-off and the partial of W S to the other half;
 // the decay of its rows by e^{gam} fills the W S products' latency. No load precedes the
 // barrier (loads issued here delayed both halves' arrival: 46.3 -> 47.9 us at 16 x 4096).
-template <int K, int V, int h, int CS>
+template <int K, int V, int h, int CS, bool IDN>
 __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V, CS> &f,
                                              f32x4 (&S)[CS][K / 32], f32x4 (&Xa)[CS],
                                              f32x4 (&Xb)[CS], Handoff32<K> *ho, int slot,
@@ -152,7 +152,7 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V, CS> &f,
     constexpr int NSH = K / 64;
 #pragma unroll
     for (int q = 0; q < CS; ++q) {
-        if constexpr (h == 0) {
+        if constexpr (h == 0 && !IDN) {
             // -U of both blocks is stored in the B layout of a 16x16x16 product (lane (n, g):
             // rows 4g .. 4g + 3 of column n), so the identity times it is -U in C layout,
             // exactly: two matrix-core products instead of eight conversions in this wave's
@@ -208,7 +208,7 @@ __device__ __forceinline__ void chain_half_a(const HalfFrag<K, V, CS> &f,
 // its exp(gam) tiles from its staged value. The scheduling barriers keep the compiler from
 // moving the refills between the update products, where their issue delayed the next step
 // (48.8 -> 46.3 us per launch at 16 x 4096, 0.474 -> 0.461 ms at 4 x 8192 x 32 heads).
-template <int K, int V, int h, int AUX, int CS>
+template <int K, int V, int h, int AUX, int CS, bool IDN>
 __device__ __forceinline__ void chain_half_b(HalfFrag<K, V, CS> &f, HalfFrag<K, V, CS> &o,
                                              const Chunk32<K, V, AUX> &nxt,
                                              f32x4 (&S)[CS][K / 32], const f32x4 (&Xa)[CS],
@@ -223,7 +223,7 @@ __device__ __forceinline__ void chain_half_b(HalfFrag<K, V, CS> &f, HalfFrag<K, 
         Pb[q] = ho[q].xp[par][1 - h][1][lane];
     }
     __builtin_amdgcn_sched_barrier(0);
-    nxt.template load_w<h, CS>(f);
+    nxt.template load_w<h, CS, IDN>(f);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < CS; ++q) {
@@ -249,25 +249,34 @@ __device__ __forceinline__ void chain_half_b(HalfFrag<K, V, CS> &f, HalfFrag<K, 
     stage_eg<K, V, h, CS>(o, ho[0], lane);     // the next chunk's exp(gam), loaded one step ago
 }
 
-template <int K, int V, int h, int AUX, int CS>
+template <int K, int V, int h, int AUX, int CS, bool IDN>
 __device__ __forceinline__ void chain_step(HalfFrag<K, V, CS> &f, HalfFrag<K, V, CS> &o,
                                            const Chunk32<K, V, AUX> &nxt,
                                            f32x4 (&S)[CS][K / 32], Handoff32<K> *ho, int c,
                                            int par, int lane)
 {
     f32x4 Xa[CS], Xb[CS];
-    chain_half_a<K, V, h, CS>(f, S, Xa, Xb, ho, c % 3, par, lane);
-    chain_half_b<K, V, h, AUX, CS>(f, o, nxt, S, Xa, Xb, ho, par, lane);
+    chain_half_a<K, V, h, CS, IDN>(f, S, Xa, Xb, ho, c % 3, par, lane);
+    chain_half_b<K, V, h, AUX, CS, IDN>(f, o, nxt, S, Xa, Xb, ho, par, lane);
 }
 
-// Chain wave h of CS consecutive slices (slice ..) over the whole sequence: their S rows
-// [K/2 h, K/2 (h + 1)) from initial_state (or 0), the chunk loop, barrier nc, and the final
-// state. The slices share every operand but -U, so one wave serving two loads W, KR and e^gam
-// once for both.
-template <int K, int V, int h, int AUX, int CS>
-__device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> *ho,
-                                           const uint8_t *base, int nc, int s, int j, int slice,
-                                           int lane)
+// Chain wave h of CS consecutive slices (slice ..) over nc chunks from `base`: their S rows
+// [K/2 h, K/2 (h + 1)) from h0u (the unit's K x V initial state, or 0 when null), the chunk
+// loop, barrier nc, and the state at the end to htu (when not null). The slices share every
+// operand but -U, so one wave serving two loads W, KR and e^gam once for both.
+// IDN: the slices are 16-column slices of the K x K transition instead: S starts from the
+// identity (row == column) and U is taken as 0, so the chain runs the homogeneous recurrence
+// S <- (diag(e^gam) - KR^T W) S.
+// FIN says how the end state goes out (CS = 1 for the two fragment forms):
+//   FIN_ROWS  fp32 rows of the unit's K x V state at htu;
+//   FIN_BFRAG the 16x16x32 B operands of the slice in fp16 (Split32::smf, the unit's
+//             fragments at htu: [V/16][K/32][64][8]);
+//   FIN_TTILE each 16 x 16 tile transposed, in fp16 (Split32::phf, [K/16][K/16][64][4]).
+enum { FIN_ROWS = 0, FIN_BFRAG = 1, FIN_TTILE = 2 };
+
+template <int K, int V, int h, int AUX, int CS, bool IDN = false, int FIN = FIN_ROWS>
+__device__ __forceinline__ void chain_wave(Handoff32<K> *ho, const uint8_t *base, int nc,
+                                           const float *h0u, void *htu, int slice, int lane)
 {
     constexpr int NKH = K / 32;
     using WS = WsBf16x32<K, V>;
@@ -281,8 +290,14 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> *ho,
 #pragma unroll
     for (int q = 0; q < CS; ++q) {
         const int col = 16 * (slice + q) + (lane & 15);
-        if (p.h0) {
-            const float *h0 = p.h0 + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+        if (IDN) {
+#pragma unroll
+            for (int t = 0; t < NKH; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[q][t][i] = row0 + 16 * t + 4 * grp + i == col ? 1.f : 0.f;
+        } else if (h0u) {
+            const float *h0 = h0u + col;
 #pragma unroll
             for (int t = 0; t < NKH; ++t)
 #pragma unroll
@@ -295,8 +310,8 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> *ho,
     }
     if (nc > 0) {
         HalfFrag<K, V, CS> fa, fb;
-        at(0).template load_w<h, CS>(fa); at(0).template load_kreg<h, CS>(fa);
-        at(1).template load_w<h, CS>(fb); at(1).template load_kreg<h, CS>(fb);
+        at(0).template load_w<h, CS, IDN>(fa); at(0).template load_kreg<h, CS>(fa);
+        at(1).template load_w<h, CS, IDN>(fb); at(1).template load_kreg<h, CS>(fb);
         // drain the prologue loads: the loop header then carries only the loop's own pending
         // loads, and the waits inside the loop count back to the right group
         vm_drain();
@@ -305,22 +320,44 @@ __device__ __forceinline__ void chain_wave(const FwdParams &p, Handoff32<K> *ho,
         // state into the loop header and make every iteration wait for the loads just issued
         int c = 0;
         for (; c + 2 <= nc; c += 2) {
-            chain_step<K, V, h, AUX, CS>(fa, fb, at(c + 2), S, ho, c, 0, lane);
-            chain_step<K, V, h, AUX, CS>(fb, fa, at(c + 3), S, ho, c + 1, 1, lane);
+            chain_step<K, V, h, AUX, CS, IDN>(fa, fb, at(c + 2), S, ho, c, 0, lane);
+            chain_step<K, V, h, AUX, CS, IDN>(fb, fa, at(c + 3), S, ho, c + 1, 1, lane);
         }
-        if (c < nc) chain_step<K, V, h, AUX, CS>(fa, fb, at(c + 2), S, ho, c, 0, lane);
+        if (c < nc) chain_step<K, V, h, AUX, CS, IDN>(fa, fb, at(c + 2), S, ho, c, 0, lane);
         lds_barrier();    // barrier nc: delta of the last chunk is in the hand-off
     }
-    if (p.ht) {
+    if (!htu) return;
+    if constexpr (FIN == FIN_ROWS) {
 #pragma unroll
         for (int q = 0; q < CS; ++q) {
             const int col = 16 * (slice + q) + (lane & 15);
-            float *ht = p.ht + ((size_t)s * p.HV + j) * (size_t)K * V + col;
+            float *ht = (float *)htu + col;
 #pragma unroll
             for (int t = 0; t < NKH; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     ht[(size_t)(row0 + 16 * t + 4 * grp + i) * V] = S[q][t][i];
+        }
+    } else if constexpr (FIN == FIN_BFRAG) {
+        // the hand-off's own operand: slab h K/64 + j pairs tiles 2j, 2j + 1 of this half
+        const __amdgpu_buffer_rsrc_t fr = buffer_rsrc(htu, (uint32_t)(K * V * 2));
+#pragma unroll
+        for (int j = 0; j < K / 64; ++j) {
+            const int at = (slice * (K / 32) + h * (K / 64) + j) * 64 + lane;
+            bstore16<0>(fr, at * 16, 0, cat(to_f16x4(S[0][2 * j]), to_f16x4(S[0][2 * j + 1])));
+        }
+    } else {
+        // C(X^T) of each tile by the identity product: lane (g, n) then holds row n of the
+        // tile, columns 4g .. 4g + 3 (fp16 values, so the product is exact)
+        f16x4 Ih;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ih[i] = (_Float16)(4 * grp + i == (lane & 15) ? 1.f : 0.f);
+        const __amdgpu_buffer_rsrc_t fr = buffer_rsrc(htu, (uint32_t)(K * K * 2));
+#pragma unroll
+        for (int t = 0; t < NKH; ++t) {
+            const int rt = h * NKH + t;
+            bstore8<0>(fr, ((rt * (K / 16) + slice) * 64 + lane) * 8, 0,
+                       to_f16x4(mfma16(to_f16x4(S[0][t]), Ih, zero4())));
         }
     }
 }
@@ -356,13 +393,13 @@ struct Unit32 {
 };
 
 // Output wave, chunk c, after barrier c + 1, for OPW slices of one unit (handoffs ho[0 ..]):
-// o = QD S + Mqk delta of each, stored as bf16. The QD / Mqk operands are the same for every
-// slice of the unit, so an output wave serving two slices loads them once.
-template <int K, int V, int AUX, int OPW>
+// o = QD S + Mqk delta of each, handed to store(q, C(O_a^T), C(O_b^T)) per slice q (blocks a
+// and b). The QD / Mqk operands are the same for every slice of the unit, so an output wave
+// serving two slices loads them once.
+template <int K, int V, int AUX, int OPW, class STORE>
 __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, V, AUX> &nxt,
                                            const Handoff32<K> *ho, int slot, int par, int lane,
-                                           __amdgpu_buffer_rsrc_t orows,
-                                           const int (&ooff)[OPW][2], bf16x4 Ib)
+                                           const STORE &store)
 {
     constexpr int NS = K / 32;
     lds_barrier();
@@ -373,33 +410,43 @@ __device__ __forceinline__ void out_step32(OutFrag32<K, V> &f, const Chunk32<K, 
 #pragma unroll
         for (int st = 0; st < NS; ++st) Sh[st] = ho[q].sh[slot][st][lane];
         const f16x4 dh0 = ho[q].dh[par][0][lane], dh1 = ho[q].dh[par][1][lane];
+        // Each product takes its operands in swapped roles, so it forms the transpose of the
+        // block's output: (A B)^T = B^T A^T, and the A operand registers of a matrix are the B
+        // operand registers of its transpose. C(O^T) holds four consecutive columns of one
+        // token row per lane, the layout of an 8-byte row store.
         f32x4 Y0 = zero4(), Y1 = zero4();
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            Y0 = mfma32(f.qd[0][st], Sh[st], Y0);
-            Y1 = mfma32(f.qd[1][st], Sh[st], Y1);
+            Y0 = mfma32(Sh[st], f.qd[0][st], Y0);
+            Y1 = mfma32(Sh[st], f.qd[1][st], Y1);
         }
         // both blocks accumulate onto the 16x16x32 products with a 16x16x32 product (block a's
         // Mqk in the lower four k of each lane, zeros above): a 16x16x16 product taking a
         // 16x16x32 result as its accumulator a few instructions later read it too early
         const f16x8 d32 = cat(dh0, dh1);
-        O0[q] = mfma32(cat(f.mqa, f16x4{0, 0, 0, 0}), d32, Y0);
-        O1[q] = mfma32(f.mqb, d32, Y1);
+        O0[q] = mfma32(d32, cat(f.mqa, f16x4{0, 0, 0, 0}), Y0);
+        O1[q] = mfma32(d32, f.mqb, Y1);
     }
     nxt.load_out(f);
-    // C(O) holds four rows of one column per lane; the identity product C(O^T) holds four
-    // consecutive columns of one row, so each block goes out as one 8-byte store per lane (the
-    // values are bf16 already, so the product changes none of them)
 #pragma unroll
-    for (int q = 0; q < OPW; ++q) {
-        const bf16x4 T0 = to_bf16x4(mfma16(to_bf16x4(O0[q]), Ib, zero4()));
-        const bf16x4 T1 = to_bf16x4(mfma16(to_bf16x4(O1[q]), Ib, zero4()));
+    for (int q = 0; q < OPW; ++q) store(q, O0[q], O1[q]);
+}
+
+// Stores of one chunk of o as bf16 rows: lane (g, n) of C(O^T) holds token n (block a) /
+// 16 + n (block b), columns 16 slice + 4g .. + 3, one 8-byte store per block.
+template <int OPW>
+struct RowStore32 {
+    __amdgpu_buffer_rsrc_t orows;
+    const int (&ooff)[OPW][2];
+    __device__ __forceinline__ void operator()(int q, f32x4 Oa, f32x4 Ob) const {
+        const bf16x4 T0 = to_bf16x4(Oa);
+        const bf16x4 T1 = to_bf16x4(Ob);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T0), orows, ooff[q][0],
                                               0, 0);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, T1), orows, ooff[q][1],
                                               0, 0);
     }
-}
+};
 
 // Chain half h of CS consecutive V-slices (slice ..) of one unit, with hand-offs ho[0 ..].
 // AUX is the cache policy of the workspace loads.
@@ -408,10 +455,13 @@ __device__ __forceinline__ void state32_chain(const FwdParams &p, Handoff32<K> *
                                               const Unit32<K, V, AUX> &u, int slice, int h,
                                               int lane)
 {
+    const size_t st = ((size_t)u.s * p.HV + u.j) * (size_t)K * V;
+    const float *h0u = p.h0 ? p.h0 + st : nullptr;
+    float *htu = p.ht ? p.ht + st : nullptr;
     if (h == 0)
-        chain_wave<K, V, 0, AUX, CS>(p, ho, u.base, u.nc, u.s, u.j, slice, lane);
+        chain_wave<K, V, 0, AUX, CS>(ho, u.base, u.nc, h0u, htu, slice, lane);
     else
-        chain_wave<K, V, 1, AUX, CS>(p, ho, u.base, u.nc, u.s, u.j, slice, lane);
+        chain_wave<K, V, 1, AUX, CS>(ho, u.base, u.nc, h0u, htu, slice, lane);
 }
 
 // The output wave of OPW consecutive V-slices (slice0 ..) of one unit, whose hand-offs are
@@ -424,8 +474,8 @@ __device__ __forceinline__ void state32_out(const FwdParams &p, const Handoff32<
     if (u.nc == 0) return;
     const int grp = lane >> 4, n = lane & 15;
     const int64_t row_bytes = (int64_t)p.HV * V * 2, head_bytes = (int64_t)u.j * V * 2;
-    // after the transposing product lane (g, n) holds row n (block a) / 16 + n (block b),
-    // columns 16 slice + 4g .. + 3
+    // the output products leave lane (g, n) with row n (block a) / 16 + n (block b), columns
+    // 16 slice + 4g .. + 3
     int ooff[OPW][2];
 #pragma unroll
     for (int q = 0; q < OPW; ++q) {
@@ -433,10 +483,6 @@ __device__ __forceinline__ void state32_out(const FwdParams &p, const Handoff32<
         ooff[q][0] = (int)(n * row_bytes + ocol * 2);
         ooff[q][1] = (int)((16 + n) * row_bytes + ocol * 2);
     }
-    float eye[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) eye[i] = 4 * grp + i == n ? 1.f : 0.f;
-    const bf16x4 Ib = to_bf16x4(eye);
     auto rows = [&](int c) {
         const int64_t r0 = u.bos + CT * c;
         const int64_t nv = u.eos - r0;
@@ -450,14 +496,69 @@ __device__ __forceinline__ void state32_out(const FwdParams &p, const Handoff32<
     lds_barrier();        // barrier 0
     int c = 0;
     for (; c + 2 <= nc; c += 2) {
-        out_step32<K, V, AUX, OPW>(fa, u.at(c + 2, lane, slice0), ho, c % 3, 0, lane, rows(c),
-                                   ooff, Ib);
+        out_step32<K, V, AUX, OPW>(fa, u.at(c + 2, lane, slice0), ho, c % 3, 0, lane,
+                                   RowStore32<OPW>{rows(c), ooff});
         out_step32<K, V, AUX, OPW>(fb, u.at(c + 3, lane, slice0), ho, (c + 1) % 3, 1, lane,
-                                   rows(c + 1), ooff, Ib);
+                                   RowStore32<OPW>{rows(c + 1), ooff});
     }
     if (c < nc)
-        out_step32<K, V, AUX, OPW>(fa, u.at(c + 2, lane, slice0), ho, c % 3, 0, lane, rows(c),
-                                   ooff, Ib);
+        out_step32<K, V, AUX, OPW>(fa, u.at(c + 2, lane, slice0), ho, c % 3, 0, lane,
+                                   RowStore32<OPW>{rows(c), ooff});
+}
+
+// Segment B of the two-segment pass (Split32): the stores of one chunk for the slice pair of
+// a workgroup, slice q = 0 the value slice (its output from a zero state, C(O^T)) and q = 1
+// the same-numbered 16-column slice of the transition (C(Y^T)). Both go to the unit's scratch
+// in fp16 as 64-lane fragments, chunk c block b at [c][b][slice][lane]. fp16 keeps 11
+// significant bits, so o0 rounded there moves o by at most 2^-12 of its magnitude before the
+// correction's one bf16 rounding; its range is that of the chain's own fp16 S and delta.
+template <int K, int V>
+struct SplitStore32 {
+    __amdgpu_buffer_rsrc_t o0, y;
+    int c, slice, lane;
+    __device__ __forceinline__ void operator()(int q, f32x4 Oa, f32x4 Ob) const {
+        if (q == 0) {
+            const int at = ((2 * c) * (V / 16) + slice) * 64 + lane;
+            bstore8<0>(o0, at * 8, 0, to_f16x4(Oa));
+            bstore8<0>(o0, (at + (V / 16) * 64) * 8, 0, to_f16x4(Ob));
+        } else {
+            const int at = ((2 * c) * (K / 16) + slice) * 64 + lane;
+            bstore8<0>(y, at * 8, 0, to_f16x4(Oa));
+            bstore8<0>(y, (at + (K / 16) * 64) * 8, 0, to_f16x4(Ob));
+        }
+    }
+};
+
+// The output wave of a segment-B workgroup (hand-offs ho[0]: the value slice, ho[1]: the
+// transition slice); `unit_idx` numbers the unit's scratch.
+template <int K, int V>
+__device__ __forceinline__ void state32_out_split(const FwdParams &p, const Handoff32<K> *ho,
+                                                  const Unit32<K, V, 0> &u, size_t unit_idx,
+                                                  int slice, int lane)
+{
+    const int nc = u.nc;
+    if (nc == 0) return;
+    const size_t o0_bytes = (size_t)nc * 2 * (V / 16) * 64 * 8;
+    const size_t y_bytes = (size_t)nc * 2 * (K / 16) * 64 * 8;
+    const __amdgpu_buffer_rsrc_t o0 =
+        buffer_rsrc((uint8_t *)p.split.o0 + unit_idx * o0_bytes, (uint32_t)o0_bytes);
+    const __amdgpu_buffer_rsrc_t y =
+        buffer_rsrc((uint8_t *)p.split.y + unit_idx * y_bytes, (uint32_t)y_bytes);
+    OutFrag32<K, V> fa, fb;
+    u.at(0, lane, slice).load_out(fa);
+    u.at(1, lane, slice).load_out(fb);
+    vm_drain();
+    lds_barrier();        // barrier 0
+    int c = 0;
+    for (; c + 2 <= nc; c += 2) {
+        out_step32<K, V, 0, 2>(fa, u.at(c + 2, lane, slice), ho, c % 3, 0, lane,
+                               SplitStore32<K, V>{o0, y, c, slice, lane});
+        out_step32<K, V, 0, 2>(fb, u.at(c + 3, lane, slice), ho, (c + 1) % 3, 1, lane,
+                               SplitStore32<K, V>{o0, y, c + 1, slice, lane});
+    }
+    if (c < nc)
+        out_step32<K, V, 0, 2>(fa, u.at(c + 2, lane, slice), ho, c % 3, 0, lane,
+                               SplitStore32<K, V>{o0, y, c, slice, lane});
 }
 
 }  // namespace

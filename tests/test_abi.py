@@ -53,6 +53,19 @@ def args(**kw):
     return a
 
 
+def split_bytes(records, units, K, T, a_permille=600):
+    """Workspace of the two-segment 32-token state pass: the chunk records, then (each
+    256-aligned) the state after segment A and segment B's K x K transition (fp16 operand
+    fragments), segment B's output fragments and the transition's output fragments (both
+    fp16)."""
+    al = lambda x: (x + 255) // 256 * 256
+    nc = (T + 31) // 32
+    c0 = min(max((nc * a_permille + 500) // 1000, 1), nc - 1)
+    nb = nc - c0
+    return (al(records) + al(units * K * K * 2) + al(units * K * K * 2) +
+            al(units * nb * 32 * K * 2) + al(units * nb * 32 * K * 2))
+
+
 def test_workspace_bytes(lib):
     f = lambda a: lib.kda_fwd_workspace_bytes(ctypes.byref(a))
     assert f(args()) == (4096 // 16 + 1) * 16 * 17408
@@ -60,7 +73,9 @@ def test_workspace_bytes(lib):
     assert f(args(io=1)) == (4096 // 16 + 1) * 16 * 34304
     assert f(args(B=4, T=8192, N=4, H=16, HV=32)) == (4 * 8192 // 16 + 4) * 32 * 17408
     assert f(args(T=45, N=1)) == (45 // 16 + 1) * 16 * 17408
-    assert f(args(chunk=32)) == (4096 // 32 + 1) * 16 * 34816
+    # 16 x 4096 at chunk 32 fills at most half of the (fallback, without a device: 256) compute
+    # units, so the state pass runs as two segments whose scratch follows the records
+    assert f(args(chunk=32)) == split_bytes((4096 // 32 + 1) * 16 * 34816, 16, 128, 4096)
     assert f(args(chunk=0)) == f(args(chunk=32))          # bf16 default: 32-token chunks
     assert f(args(io=1, chunk=0)) == f(args(io=1, chunk=16))
     assert f(args(chunk=32, T=45)) == (45 // 32 + 1) * 16 * 34816

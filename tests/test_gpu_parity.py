@@ -92,6 +92,14 @@ SMALL = {
     "bf16_b4_h16_t70_slices2": W.custom(B=4, T=70, H=8, HV=16, K=128, V=128, h0_std=0.1),
     "bf16_b8_h16_t45_slices4": W.custom(B=8, T=45, H=16, HV=16, K=128, V=128),
     "bf16_b16_h16_k64v64_slices4": W.custom(B=16, T=40, H=16, HV=16, K=64, V=64, h0_std=0.1),
+    # dense batches of at least 16 chunks whose value slices fill at most half of a 256-CU part:
+    # at chunk 32 the state pass runs as two segments (the second from a zero state next to
+    # its transition, then the correction); ragged last chunks, an initial state, grouped value
+    # heads, K = V = 64 and strong decays
+    "bf16_split_t600_h0": W.custom(B=1, T=600, H=2, HV=2, K=128, V=128, h0_std=0.1),
+    "bf16_split_gva_k64_t1000": W.custom(B=2, T=1000, H=1, HV=2, K=64, V=64, h0_std=0.1),
+    "bf16_split_strong_t700": W.custom(B=1, T=700, H=1, HV=1, K=128, V=128, g_lo=0.5,
+                                       g_hi=0.9999, beta_std=2.0),
 }
 
 

@@ -86,8 +86,12 @@ def test_packed_equals_per_sequence(chunk):
             assert torch.equal(f[s], inp.h0[s]), f"empty sequence {s} changed its state"
             continue
         seq = lambda x: x[:, a:b].contiguous()
+        # the sequence alone, also packed (cu_seqlens of one sequence), so that both runs take
+        # the one-segment state pass (a dense batch this small runs as two segments at chunk
+        # 32, with other rounding; that path is compared with the oracle on its own)
+        one = torch.tensor([0, b - a], dtype=torch.int64)
         o_s, f_s = run(seq(inp.q), seq(inp.k), seq(inp.v), seq(inp.g), seq(inp.beta),
-                       inp.scale, h0=inp.h0[s:s + 1], chunk=chunk)
+                       inp.scale, h0=inp.h0[s:s + 1], cu=one, chunk=chunk)
         assert torch.equal(o[:, a:b], o_s), f"o of sequence {s} differs from its own run"
         assert torch.equal(f[s:s + 1], f_s), f"final state of sequence {s} differs"
 
