@@ -119,9 +119,10 @@ def summarize_trace(d: str, command: str) -> str:
             if "kda::" not in name:
                 seen = set()                  # the flush's copy and read kernels
                 continue
-            kind = "prepare" if "prepare" in name else "state"
-            (again if kind in seen else first).setdefault(name, []).append(dur)
-            seen.add(kind)
+            # each kernel name once per stage call (the state stage of the two-segment pass
+            # is two kernels)
+            (again if name in seen else first).setdefault(name, []).append(dur)
+            seen.add(name)
         out += ["", "Forward kernels by launch kind: the first launch of each stage after a "
                     "cache flush (the timed steps' kernels), and the launches that follow it "
                     "back to back before the next flush (warm steps and the per-kernel timing "
@@ -161,13 +162,20 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, command: st
             raise SystemExit(f"no calibration copy kernel in {d}")
         scale = copy_bytes / statistics.median(copy)
         for k, v in vals.items():
-            m = re.search(r"kda::(prepare|state|recurrent)(?:32)?_", k)
-            if m:
-                e = res.setdefault(f"kda_{m.group(1)}", {})
-                e[counter.lower() + "_raw_bytes"] = statistics.mean(v)
-                e[counter.lower() + "_scale"] = round(scale, 4)
-                e[counter.lower() + "_bytes"] = statistics.mean(v) * scale
-                e["kernel_name"] = k
+            if "kda::" not in k:
+                continue
+            # the stage a kernel belongs to: the state stage of the two-segment pass is two
+            # kernels (the pass and its correction), each launched once per stage call
+            stage = ("prepare" if "prepare" in k else
+                     "recurrent" if "recurrent" in k else "state")
+            e = res.setdefault(f"kda_{stage}", {})
+            e[counter.lower() + "_raw_bytes"] = (e.get(counter.lower() + "_raw_bytes", 0.0) +
+                                                 statistics.mean(v))
+            e[counter.lower() + "_scale"] = round(scale, 4)
+            e[counter.lower() + "_bytes"] = (e.get(counter.lower() + "_bytes", 0.0) +
+                                             statistics.mean(v) * scale)
+            e.setdefault("kernels", {}).setdefault(k, {})[counter.lower() + "_bytes"] = (
+                statistics.mean(v) * scale)
     for k, e in res.items():
         e["hbm_bytes_per_launch"] = e["fetch_size_bytes"] + e["write_size_bytes"]
         e.update(kernel=k, workload=workload, source_digest=source_digest(), command=command)

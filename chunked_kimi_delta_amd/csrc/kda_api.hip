@@ -51,11 +51,13 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Share of a sequence's chunks given to segment A of the two-segment state pass, in parts per
 // thousand. Segment A's workgroups hold one value slice, segment B's two (a value slice and a
-// transition slice sharing every chunk operand); measured at 16 heads x 4096 tokens, a chunk
-// step takes about 355 ns with one slice per workgroup and 534 ns with two, so A takes
-// 534 / (355 + 534) of the chunks for both segments to end together.
+// transition slice sharing every chunk operand). Measured at 16 heads x 4096 tokens with each
+// segment alone, a workgroup takes about 2 us plus 355 ns per chunk in A and 2 us plus 478 ns
+// per chunk in B, so both end together with A at 478 / (355 + 478) = 0.57 of the chunks;
+// 0.58 measured best (the split kernel took 30.8 us at 0.56, 30.1 at 0.58, 31.3 at 0.60, 33.0
+// at 0.65 and 34.8 at 0.70).
 #ifndef KDA_SPLIT_A_PERMILLE
-#define KDA_SPLIT_A_PERMILLE 600
+#define KDA_SPLIT_A_PERMILLE 580
 #endif
 
 // The two-segment state pass (Split32) and its scratch after the chunk records: bf16 io,

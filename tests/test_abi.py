@@ -53,7 +53,7 @@ def args(**kw):
     return a
 
 
-def split_bytes(records, units, K, T, a_permille=600):
+def split_bytes(records, units, K, T, a_permille=580):
     """Workspace of the two-segment 32-token state pass: the chunk records, then (each
     256-aligned) the state after segment A and segment B's K x K transition (fp16 operand
     fragments), segment B's output fragments and the transition's output fragments (both
