@@ -448,10 +448,13 @@ __device__ __forceinline__ float l2norm_factor(float sumsq) {
 
 // The bf16 prepare kernels factor e^{Gam_i - Gam_j} = e^{Gam_i - ref} e^{ref - Gam_j} around a
 // reference token of the chunk. The factors of a block's diagonal Gram products then span
-// e^{+-(decay between the reference and the block's far end)}; beyond 2^{+-FACTOR_SPAN_MAX} (log2
-// units) their fp32 / bf16 hi-lo representation loses the small factor's low bits or
-// overflows, and the block's diagonal products are formed by exact_block_gram instead.
-constexpr float FACTOR_SPAN_MAX = 64.f;
+// 2^{+-span}, span the decay (log2 units) between the reference and the block's far end; the
+// kept products (j <= i) are at most 1 and the discarded upper triangle at most 2^span. Up to
+// span 100 every factor, the low bf16 part of its hi + lo split (about 2^-9 of it, so at least
+// about 2^-119 |k|) and every sum stay in the normal fp32 / bf16 range; beyond it the small
+// factors' low parts would turn subnormal, and the block's diagonal products are formed by
+// exact_block_gram instead.
+constexpr float FACTOR_SPAN_MAX = 100.f;
 
 // Lane I of each 16-lane DPP row, broadcast to the whole row (row_newbcast).
 template <int I>

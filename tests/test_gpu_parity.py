@@ -426,10 +426,15 @@ def test_prestage_full_size_bounded_gate():
 
 # --------------------------------------------------------------------------- strong gates
 # Decays far beyond what factors centred on a reference token can hold (their exponents
-# would span more than 2^64 within a 16- or 32-token chunk). The kernels then form the
+# would span more than 2^100 within a 16- or 32-token chunk). The kernels then form the
 # diagonal Gram blocks from exact per-token decay products; the result must meet the same bars.
+# One case stays just inside the factored form's range.
 
 STRONG_G = {
+    # log decays of -3.8 .. -4.2 per token: the 32-token blocks' factors span 2^82 .. 2^92,
+    # still on the factored path (hi + lo bf16 factors)
+    "span90_g": W.custom(B=1, T=100, H=2, HV=2, K=128, V=128, h0_std=0.1, g_lo=0.015,
+                         g_hi=0.022),
     # plain log decays of -6.9 .. -18.4 per token and key dim
     "strong_g": W.custom(B=1, T=100, H=2, HV=2, K=128, V=128, h0_std=0.1, g_lo=1e-8,
                          g_hi=1e-3),
