@@ -92,9 +92,10 @@ typedef struct {
                                  units (exp(g) multiplies the state). Any g <= 0 is exact to
                                  rounding at every chunk length: where a chunk's decay is too
                                  strong for the bf16 prepare kernels' factorised decay products
-                                 (exponents spanning more than 2^64 between a chunk's
-                                 reference token and its far end, e.g. below about -5.5 per
-                                 token over 8 tokens), they form that chunk's diagonal Gram
+                                 (exponents spanning more than 2^100 between a chunk's
+                                 reference token and its far end, e.g. below about -4.3 per
+                                 token over the 16 tokens of a 32-token chunk's block), they
+                                 form that chunk's diagonal Gram
                                  blocks from exact products of per-token decays instead.
                                  g <= 0 is expected but not enforced.                       */
     const void *beta;         /* [B, T, HV]     io dtype; used as given (no sigmoid)        */
@@ -129,12 +130,19 @@ typedef struct {
     const float *dt_bias;     /* [HV, K] fp32 device (16-byte aligned), or NULL for zeros    */
 } kda_fwd_args;
 
-/* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read).
-   Returns 0 for arguments kda_fwd would reject. The workspace holds the prepare kernel's
-   per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma)) for ceil-bounded chunk slots of every
-   value head: (B*T/chunk + N) * HV slots of 17,408 B (chunk 16), 34,816 B (chunk 32) or
-   2 x 36,864 B (chunk 64: two 32-token records per slot) at bf16 io and K = V = 128. Chunk 1
-   needs none (0; kda_fwd then accepts a NULL workspace). */
+/* Bytes of device workspace kda_fwd needs for these arguments (only shapes and io are read,
+   and the current device's compute-unit count). Returns 0 for arguments kda_fwd would reject.
+   The workspace holds the prepare kernel's per-chunk outputs (w, qd, kr, u, Mqk, exp(gamma))
+   for ceil-bounded chunk slots of every value head: (B*T/chunk + N) * HV slots of 17,408 B
+   (chunk 16), 34,816 B (chunk 32) or 2 x 36,864 B (chunk 64: two 32-token records per slot)
+   at bf16 io and K = V = 128. At chunk 32 a dense batch (no cu_seqlens) with K == V, at least
+   512 tokens per sequence and at most CUs / 2 sixteen-column state slices (N * HV * V / 16)
+   runs the state pass as two segments whose scratch follows the records (about 2 * 2 * K
+   bytes per token of the second segment and value head, plus two K x K fp16 states per
+   (sequence, value head)); the size therefore depends on the device the call is sized for,
+   and a workspace sized on a device with more compute units than the one it runs on may be
+   too small (KDA_ERR_WORKSPACE). Chunk 1 needs none (0; kda_fwd then accepts a NULL
+   workspace). */
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
 
 /* Enqueue the forward: prepare kernel, then state kernel, on `stream` (hipStream_t or NULL).
@@ -146,7 +154,8 @@ kda_status kda_fwd(const kda_fwd_args *args, void *workspace, size_t ws_bytes, v
 /* The two stages of kda_fwd as separate launches, for callers that schedule or time them
    individually. kda_fwd_prepare enqueues the token-parallel prepare kernel, which writes the
    per-chunk quantities of every (chunk, value head) into `workspace`; kda_fwd_state enqueues
-   the chunk-sequential state kernel, which reads them and writes o and final_state. Running
+   the chunk-sequential state kernel (for a two-segment state pass, the pass and its
+   correction kernel), which reads them and writes o and final_state. Running
    kda_fwd_prepare then kda_fwd_state on one stream with the same arguments and workspace is
    exactly kda_fwd. Same arguments, checks and status codes as kda_fwd. */
 kda_status kda_fwd_prepare(const kda_fwd_args *args, void *workspace, size_t ws_bytes,
@@ -205,7 +214,7 @@ kda_status kda_bwd(const kda_fwd_args *args, const void *d_o, const float *dht,
    library holds on every device it runs on until the process ends; it calls no allocating
    routine. Same arguments (no workspace), checks, results and status codes as kda_fwd, plus
    KDA_ERR_NOALLOC_TOO_LARGE when kda_fwd_workspace_bytes(args) exceeds the array (128 MiB:
-   for example 16 value heads of up to about 7,700 tokens at bf16 io; chunk 1 needs none, so
+   for example 16 value heads of up to about 6,300 tokens at bf16 io; chunk 1 needs none, so
    decoding steps have no limit). The work runs on the calling thread's current device and
    uses that device's array. Every call on one device shares that array: calls whose work
    overlaps on one device (several streams or threads) race on it, so the caller serialises
