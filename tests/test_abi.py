@@ -66,6 +66,29 @@ def split_bytes(records, units, K, T, a_permille=580):
             al(units * nb * 32 * K * 2) + al(units * nb * 32 * K * 2))
 
 
+def test_two_segment_plan_boundaries(lib):
+    # the two-segment state pass (and its scratch) applies exactly to bf16 io, 32-token chunks,
+    # dense sequences of at least 512 tokens, K == V, and at most CUs / 2 (without a device the
+    # library assumes 256 CUs) sixteen-column slices N * HV * V / 16
+    f = lambda **kw: lib.kda_fwd_workspace_bytes(ctypes.byref(args(**kw)))
+    # 32-token record bytes: W, QD, KR (64 K each), -U (64 V), the two Mqk blocks (1,536)
+    # and e^gam (4 K), rounded up to 256
+    rb = lambda K, V: (192 * K + 64 * V + 1536 + 4 * K + 255) // 256 * 256
+    rec = lambda T, HV, K=128, V=128, N=1: ((N * T) // 32 + N) * HV * rb(K, V)
+    assert rb(128, 128) == 34816
+    assert f(chunk=32, T=512) == split_bytes(rec(512, 16), 16, 128, 512)
+    assert f(chunk=32, T=511) == rec(511, 16)                      # fewer than 16 chunks
+    assert f(chunk=32, H=16, HV=16) > rec(4096, 16)                 # 256 slices: split
+    assert f(chunk=32, H=17, HV=17) == rec(4096, 17)                # 272 slices: one segment
+    assert f(chunk=32, H=8, HV=32, K=64, V=64) == split_bytes(rec(4096, 32, 64, 64), 32, 64,
+                                                              4096)  # 32 x 4 slices x 2
+    assert f(chunk=32, K=64, V=128, H=4, HV=4) == rec(4096, 4, 64, 128)   # K != V
+    assert f(chunk=32, B=2, N=2, H=8, HV=8) == split_bytes(rec(4096, 8, N=2), 16, 128, 4096)
+    assert f(chunk=16) == (4096 // 16 + 1) * 16 * 17408            # other chunks: no split
+    assert f(chunk=64) == (4096 // 64 + 1) * 16 * 2 * 36864
+    assert f(io=1, chunk=16) == (4096 // 16 + 1) * 16 * 34304
+
+
 def test_workspace_bytes(lib):
     f = lambda a: lib.kda_fwd_workspace_bytes(ctypes.byref(a))
     assert f(args()) == (4096 // 16 + 1) * 16 * 17408

@@ -100,6 +100,8 @@ SMALL = {
     "bf16_split_gva_k64_t1000": W.custom(B=2, T=1000, H=1, HV=2, K=64, V=64, h0_std=0.1),
     "bf16_split_strong_t700": W.custom(B=1, T=700, H=1, HV=1, K=128, V=128, g_lo=0.5,
                                        g_hi=0.9999, beta_std=2.0),
+    # exactly 16 chunks (the smallest split: 9 + 7), three heads (padded workgroups)
+    "bf16_split_t512_h3": W.custom(B=1, T=512, H=3, HV=3, K=128, V=128),
 }
 
 
@@ -165,13 +167,14 @@ def test_deltanet_retrieval_property(chunk):
 
 
 @pytest.mark.parametrize("chunk", [1, 16, 32, 64])
-def test_no_final_state_and_explicit_scale(chunk):
-    w = W.custom(B=1, T=64, H=1, HV=2, K=128, V=128)
+@pytest.mark.parametrize("T", [64, 1000])      # 1000 tokens at chunk 32: the two-segment pass
+def test_no_final_state_and_explicit_scale(chunk, T):
+    w = W.custom(B=1, T=T, H=1, HV=2, K=128, V=128)
     inp = W.make_inputs(w, seed=2)
     o, fin = gpu_run(inp, scale=0.3, output_final_state=False, chunk=chunk)
     assert fin is None
     o_ref, _ = oracle_run(inp, scale=0.3)
-    assert rel_l2(o, o_ref) <= TOL["bf16"]
+    check_all(inp, o, None, o_ref, None, "bf16", what=f"no final state, T {T}")
 
 
 @pytest.mark.parametrize("chunk", [1, 16, 32, 64])
