@@ -58,11 +58,11 @@ static hipError_t launch_state32_spw(const FwdParams &p, hipStream_t st)
 }
 
 // Two-segment pass (Split32), one launch: the first nA workgroups are segment A (one value
-// slice each: two chain waves and an output wave; waves 3 and 4 only pass the barriers), the next nA
-// segment B (a value slice and the same-numbered slice of the transition: two chain waves each
-// and one output wave for both). Both halves use the XCD map of the one-segment kernel. The
-// launch reserves enough LDS that no CU holds two of these workgroups: the grid is sized to
-// the CU count, and two on one CU would share its SIMDs while another CU idles.
+// slice each: two chain waves and an output wave; waves 3 and 4 only pass the barriers), the
+// next nA segment B (a value slice and the same-numbered slice of the transition: two chain
+// waves each and one output wave for both). Both halves use the XCD map of the one-segment
+// kernel. The launch reserves enough LDS that no CU holds two of these workgroups: the grid is
+// sized to the CU count, and two on one CU would share its SIMDs while another CU idles.
 template <int K, int V>
 __global__ __launch_bounds__(320) void state32_split_kernel(FwdParams p)
 {
