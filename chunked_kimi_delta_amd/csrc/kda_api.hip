@@ -66,7 +66,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // units, so that both segments' workgroups run at once, one per CU.
 struct SplitPlan {
     int c0 = 0, nb = 0;
-    size_t smf = 0, phf = 0, o0 = 0, y = 0, end = 0;   // byte offsets in the workspace
+    size_t smf = 0, phf = 0, s0 = 0, o0 = 0, y = 0, end = 0;   // byte offsets in the workspace
 };
 
 SplitPlan split_plan(const kda_fwd_args *a, int ct, size_t records)
@@ -86,7 +86,8 @@ SplitPlan split_plan(const kda_fwd_args *a, int ct, size_t records)
     sp.nb = (int)nb;
     sp.smf = align256(records);
     sp.phf = sp.smf + align256((size_t)units * a->K * a->V * 2);
-    sp.o0 = sp.phf + align256((size_t)units * a->K * a->K * 2);
+    sp.s0 = sp.phf + align256((size_t)units * a->K * a->K * 2);
+    sp.o0 = sp.s0 + align256((size_t)units * a->K * a->V * 4);
     sp.y = sp.o0 + align256((size_t)units * o0_unit);
     sp.end = sp.y + align256((size_t)units * y_unit);
     return sp;
@@ -232,6 +233,7 @@ kda_status run_stages(const kda_fwd_args *a, void *workspace, size_t ws_bytes, v
         p.split.nb = sp.nb;
         p.split.smf = (_Float16 *)(w + sp.smf);
         p.split.phf = (_Float16 *)(w + sp.phf);
+        p.split.s0 = (float *)(w + sp.s0);
         p.split.o0 = (_Float16 *)(w + sp.o0);
         p.split.y = (_Float16 *)(w + sp.y);
     }

@@ -74,6 +74,9 @@ struct Split32 {
                                 // (lane (g, n): rows 32 t + 16 (e / 4) + 4g + e % 4, column n)
     _Float16 *phf = nullptr;    // [N][HV][K/16 row tiles][K/16 column slices][64][4]: phi tile
                                 // transposed (lane (g, m): row m, columns 4g .. 4g + 3)
+    float *s0 = nullptr;        // [N][HV][K][V] segment B's end state from zero (final_state
+                                // is written only by the correction, after every read of
+                                // initial_state, so the two may be one buffer)
     _Float16 *o0 = nullptr;     // [N][HV][nb][2 blocks][V/16][64 lanes][4] C(O^T) from zero
     _Float16 *y = nullptr;      // [N][HV][nb][2][K/16][64][4] C(Y^T): the transition's output
 };

@@ -98,11 +98,11 @@ __global__ __launch_bounds__(320) void state32_split_kernel(FwdParams p)
     u.base += (size_t)c0 * WS::BYTES;
     u.bos += 32 * (int64_t)c0;
     u.nc = p.split.nb;
-    float *ht = p.ht ? p.ht + st : nullptr;
+    float *s0 = p.ht ? p.split.s0 + st : nullptr;
     _Float16 *phi = p.ht ? p.split.phf + st : nullptr;
     switch (wave) {
-    case 0: chain_wave<K, V, 0, 0, 1>(&hos[0], u.base, u.nc, nullptr, ht, slice, lane); break;
-    case 1: chain_wave<K, V, 1, 0, 1>(&hos[0], u.base, u.nc, nullptr, ht, slice, lane); break;
+    case 0: chain_wave<K, V, 0, 0, 1>(&hos[0], u.base, u.nc, nullptr, s0, slice, lane); break;
+    case 1: chain_wave<K, V, 1, 0, 1>(&hos[0], u.base, u.nc, nullptr, s0, slice, lane); break;
     case 2:
         chain_wave<K, V, 0, 0, 1, true, FIN_TTILE>(&hos[1], u.base, u.nc, nullptr, phi, slice,
                                                    lane);
@@ -119,7 +119,8 @@ __global__ __launch_bounds__(320) void state32_split_kernel(FwdParams p)
 constexpr int SPLIT_FIX_CHUNKS = 1;
 
 // The correction after the two-segment pass: for every token of segment B, o = o0 + y S_A
-// (stored as bf16), and the final state S0_end + phi S_A. Workgroups of V/32 waves, per unit
+// (stored as bf16), and the final state S0_end + phi S_A (S0_end from the scratch: this kernel
+// is the only writer of final_state, after every read of initial_state). Workgroups of V/32 waves, per unit
 // first one per SPLIT_FIX_CHUNKS chunks of B, then one per 16-row tile of the final state;
 // wave w owns the output columns [32 w, 32 w + 32). Every product is a 16x16x32 MFMA:
 // C(O^T) = S_A^T Y^T takes the S_A fragment (the B operand of S_A) as the A operand of S_A^T,
@@ -153,13 +154,14 @@ __global__ __launch_bounds__(64 * (V / 32)) void split32_fix_kernel(FwdParams p)
 #pragma unroll
         for (int t = 0; t < NS; ++t)
             PA[t] = cat(phf[(rt * NK + 2 * t) * 64 + lane], phf[(rt * NK + 2 * t + 1) * 64 + lane]);
+        const float *s0 = p.split.s0 + st;
         float *ht = p.ht + st;
         f32x4 acc[2];
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                acc[vt][i] = ht[(size_t)(16 * rt + 4 * grp + i) * V + 16 * (2 * wave + vt) + n];
+                acc[vt][i] = s0[(size_t)(16 * rt + 4 * grp + i) * V + 16 * (2 * wave + vt) + n];
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt) {
 #pragma unroll

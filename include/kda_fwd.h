@@ -106,7 +106,8 @@ typedef struct {
                                  undefined values but every access stays in bounds.         */
     const float *initial_state; /* [N, HV, K, V] fp32, or NULL for zeros                    */
     void *o;                  /* [B, T, HV, V]  io dtype, written for every token            */
-    float *final_state;       /* [N, HV, K, V] fp32, or NULL to skip                        */
+    float *final_state;       /* [N, HV, K, V] fp32, or NULL to skip; may be the same
+                                 buffer as initial_state (the state updated in place)       */
     int32_t chunk;            /* tokens per serial step of the state kernel: 16 (the FlashKDA
                                  tile of "KDA源码剖析之FlashKDA（上）"), 32 (two 16-token blocks
                                  joined by block forward substitution; bf16 io only), 64 (pairs
@@ -138,11 +139,11 @@ typedef struct {
    at bf16 io and K = V = 128. At chunk 32 a dense batch (no cu_seqlens) with K == V, at least
    512 tokens per sequence and at most CUs / 2 sixteen-column state slices (N * HV * V / 16)
    runs the state pass as two segments whose scratch follows the records (about 2 * 2 * K
-   bytes per token of the second segment and value head, plus two K x K fp16 states per
-   (sequence, value head)); the size therefore depends on the device the call is sized for,
-   and a workspace sized on a device with more compute units than the one it runs on may be
-   too small (KDA_ERR_WORKSPACE). Chunk 1 needs none (0; kda_fwd then accepts a NULL
-   workspace). */
+   bytes per token of the second segment and value head, plus two K x K fp16 states and one
+   K x V fp32 state per (sequence, value head)); the size therefore depends on the device the
+   call is sized for, and a workspace sized on a device with more compute units than the one
+   it runs on may be too small (KDA_ERR_WORKSPACE). Chunk 1 needs none (0; kda_fwd then
+   accepts a NULL workspace). */
 size_t kda_fwd_workspace_bytes(const kda_fwd_args *args);
 
 /* Enqueue the forward: prepare kernel, then state kernel, on `stream` (hipStream_t or NULL).

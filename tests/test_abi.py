@@ -56,14 +56,14 @@ def args(**kw):
 def split_bytes(records, units, K, T, a_permille=580):
     """Workspace of the two-segment 32-token state pass: the chunk records, then (each
     256-aligned) the state after segment A and segment B's K x K transition (fp16 operand
-    fragments), segment B's output fragments and the transition's output fragments (both
-    fp16)."""
+    fragments), segment B's end state from zero (fp32), segment B's output fragments and the
+    transition's output fragments (both fp16)."""
     al = lambda x: (x + 255) // 256 * 256
     nc = (T + 31) // 32
     c0 = min(max((nc * a_permille + 500) // 1000, 1), nc - 1)
     nb = nc - c0
     return (al(records) + al(units * K * K * 2) + al(units * K * K * 2) +
-            al(units * nb * 32 * K * 2) + al(units * nb * 32 * K * 2))
+            al(units * K * K * 4) + al(units * nb * 32 * K * 2) + al(units * nb * 32 * K * 2))
 
 
 def test_two_segment_plan_boundaries(lib):

@@ -96,6 +96,28 @@ def test_packed_equals_per_sequence(chunk):
         assert torch.equal(f[s:s + 1], f_s), f"final state of sequence {s} differs"
 
 
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
+@pytest.mark.parametrize("case", ["dense_t1000", "packed"])
+def test_state_update_in_place(case, chunk):
+    # initial_state and final_state as one buffer (a state carried in place from call to
+    # call): the same o and final state, bit for bit, as with separate buffers. At chunk 32 the
+    # dense case runs as two segments, whose final state is written only by the correction.
+    w = (W.custom(B=1, T=1000, H=2, HV=2, K=128, V=128, h0_std=0.1) if case == "dense_t1000"
+         else W.custom(H=2, HV=4, K=128, V=128, h0_std=0.1, lengths=(600, 0, 77, 1100)))
+    inp = W.make_inputs(w, seed=12)
+    o_ref, f_ref = run(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, h0=inp.h0,
+                       cu=inp.cu_seqlens, chunk=chunk)
+    h = inp.h0.to(DEV).contiguous()
+    plan = kda.KdaFwdPlan(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                          scale=inp.scale, cu_seqlens=dev(inp.cu_seqlens), initial_state=h,
+                          final_state=h, chunk=chunk)
+    o, fin = plan()
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == h.data_ptr()
+    assert torch.equal(o.float().cpu(), o_ref), "o differs with the state updated in place"
+    assert torch.equal(h.cpu(), f_ref), "final state differs with the state updated in place"
+
+
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_slice_grouping_bitwise(chunk):
     # 4 sequences x 32 value heads: 1,024 16-column slices, so the state kernel puts four slices
