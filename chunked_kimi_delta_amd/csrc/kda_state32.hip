@@ -120,11 +120,11 @@ constexpr int SPLIT_FIX_CHUNKS = 1;
 
 // The correction after the two-segment pass: for every token of segment B, o = o0 + y S_A
 // (stored as bf16), and the final state S0_end + phi S_A (S0_end from the scratch: this kernel
-// is the only writer of final_state, after every read of initial_state). Workgroups of V/32 waves, per unit
-// first one per SPLIT_FIX_CHUNKS chunks of B, then one per 16-row tile of the final state;
-// wave w owns the output columns [32 w, 32 w + 32). Every product is a 16x16x32 MFMA:
-// C(O^T) = S_A^T Y^T takes the S_A fragment (the B operand of S_A) as the A operand of S_A^T,
-// and phi S_A takes it as the B operand it is.
+// is the only writer of final_state, after every read of initial_state). Workgroups of V/32
+// waves, per unit first one per SPLIT_FIX_CHUNKS chunks of B, then one per 16-row tile of the
+// final state; wave w owns the output columns [32 w, 32 w + 32). Every product is a 16x16x32
+// MFMA: C(O^T) = S_A^T Y^T takes the S_A fragment (the B operand of S_A) as the A operand of
+// S_A^T, and phi S_A takes it as the B operand it is.
 template <int K, int V>
 __global__ __launch_bounds__(64 * (V / 32)) void split32_fix_kernel(FwdParams p)
 {
@@ -135,7 +135,10 @@ __global__ __launch_bounds__(64 * (V / 32)) void split32_fix_kernel(FwdParams p)
     const int grp = lane >> 4, n = lane & 15;
     const int nb = p.split.nb;
     const int ngrp = (nb + SPLIT_FIX_CHUNKS - 1) / SPLIT_FIX_CHUNKS;
-    const int unit = (int)blockIdx.x / (ngrp + NK), gi = (int)blockIdx.x % (ngrp + NK);
+    // unit u's workgroups on XCD u % 8 (dispatch is round-robin over the 8 XCDs), the XCD
+    // whose L2 last held the unit's scratch: the pass ran all of the unit's slices there
+    const int xcd = (int)blockIdx.x & 7, r = (int)blockIdx.x >> 3;
+    const int unit = r / (ngrp + NK) * 8 + xcd, gi = r % (ngrp + NK);
     if (unit >= p.seq.N * p.HV) return;
     const int j = unit % p.HV, s = unit / p.HV;
     const size_t st = ((size_t)s * p.HV + j) * (size_t)K * V;
@@ -242,7 +245,7 @@ static hipError_t launch_state32_split(const FwdParams &p, hipStream_t st)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t ngrp = (p.split.nb + SPLIT_FIX_CHUNKS - 1) / SPLIT_FIX_CHUNKS;
-        split32_fix_kernel<K, V><<<dim3((unsigned)(units * (ngrp + K / 16))),
+        split32_fix_kernel<K, V><<<dim3((unsigned)((units + 7) / 8 * 8 * (ngrp + K / 16))),
                                    dim3(64 * (V / 32)), 0, st>>>(p);
         return hipGetLastError();
     }
