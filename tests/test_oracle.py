@@ -413,3 +413,32 @@ def test_c_oracle_matches_numpy_and_samples():
     assert np.array_equal(f3[2, 3], f2[2, 3]) and np.array_equal(f3[0, 1], f2[0, 1])
     assert np.all(f3[1] == 0) and np.array_equal(o3[0, 30:70, 3], o2[0, 30:70, 3])
     del lens
+
+
+def test_state_affine_in_a_segment_start():
+    # The decomposition the 32-token path's two-segment state pass relies on, checked on the
+    # fp64 recurrence itself: a sequence's later segment run from a start state S_A equals the
+    # run from zero plus y S_A (outputs) and phi S_A (final state), where y and phi are the
+    # outputs and final state of the same tokens run with v = 0 from the identity (K columns).
+    rng = np.random.default_rng(21)
+    T, T_A, H, HV, K, V = 70, 29, 1, 2, 16, 8
+    q = rng.standard_normal((1, T, H, K)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((1, T, H, K)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, T, HV, V))
+    g = np.log(rng.uniform(0.8, 0.999, (1, T, HV, K)))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((1, T, HV))))
+    h0 = 0.1 * rng.standard_normal((1, HV, K, V))
+    o, fin = kda_recurrent(q, k, v, g, beta, initial_state=h0)
+    seg = lambda x, a, b: x[:, a:b]
+    _, S_A = kda_recurrent(*(seg(x, 0, T_A) for x in (q, k, v, g, beta)), initial_state=h0)
+    b = [seg(x, T_A, T) for x in (q, k, v, g, beta)]
+    o0, S0 = kda_recurrent(*b)
+    eye = np.broadcast_to(np.eye(K), (1, HV, K, K)).copy()
+    y, phi = kda_recurrent(b[0], b[1], np.zeros((1, T - T_A, HV, K)), b[3], b[4],
+                           initial_state=eye)
+    o_b = o0 + np.einsum("btjk,jkv->btjv", y, S_A[0])
+    fin_b = S0 + np.einsum("njkl,njlv->njkv", phi, S_A)
+    assert np.allclose(o_b, o[:, T_A:], rtol=1e-11, atol=1e-12)
+    assert np.allclose(fin_b, fin, rtol=1e-11, atol=1e-12)
+    # the transition is not trivial here: S_A changes the later outputs
+    assert np.abs(np.einsum("btjk,jkv->btjv", y, S_A[0])).max() > 1e-3
