@@ -133,3 +133,36 @@ def test_slice_grouping_bitwise(chunk):
                        inp.scale, h0=inp.h0[b:b + 1], chunk=chunk)
         assert torch.equal(o[b:b + 1], o_b), f"o of sequence {b} differs from its own run"
         assert torch.equal(f[b:b + 1], f_b), f"final state of sequence {b} differs"
+
+
+@pytest.mark.parametrize("case", ["dense_split", "packed"])
+def test_forward_replays_in_a_hip_graph(case):
+    # The forward captured in a HIP graph (the library records kernel launches only: no memset,
+    # copy or allocation) and replayed three times, with new inputs copied into the captured
+    # buffers and eager work in between: every replay equals an eager run bit for bit. The
+    # dense case runs the two-segment state pass (two kernels after the prepare).
+    w = (W.custom(B=1, T=1000, H=2, HV=2, K=128, V=128, h0_std=0.1) if case == "dense_split"
+         else W.custom(H=2, HV=4, K=128, V=128, h0_std=0.1, lengths=(300, 77, 700)))
+    inp = W.make_inputs(w, seed=50)
+    bufs = [dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0)]
+    cu = dev(inp.cu_seqlens)
+    plan = kda.KdaFwdPlan(*bufs[:5], scale=inp.scale, cu_seqlens=cu, initial_state=bufs[5])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan()
+    for seed in (51, 52, 53):
+        new = W.make_inputs(w, seed=seed)
+        for b, x in zip(bufs, (new.q, new.k, new.v, new.g, new.beta, new.h0)):
+            b.copy_(x.to(DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        o_g, f_g = plan.o.float().cpu(), plan.final_state.cpu()
+        o_e, f_e = run(new.q, new.k, new.v, new.g, new.beta, new.scale, h0=new.h0,
+                       cu=new.cu_seqlens)
+        assert torch.equal(o_g, o_e), f"o of replay (seed {seed}) differs from the eager run"
+        assert torch.equal(f_g, f_e), f"final state of replay (seed {seed}) differs"
