@@ -615,7 +615,11 @@ def main():
                           "alg_bytes": work["state_bytes"], "alg_flops": work16["state_flops"],
                           "issued_flops_this_chunk": work["state_flops"],
                           "achieved_TFLOPs": round(work16["state_flops"] / (state_ms * 1e-3)
-                                                   / 1e12, 2)},
+                                                   / 1e12, 2),
+                          "launches": "the state stage (kda_fwd_state): one kernel, or, for a "
+                                      "dense 32-token batch whose state slices fill at most "
+                                      "half of the CUs, the two-segment pass and its "
+                                      "correction kernel"},
         }
     if chunk == 1:
         # the token recurrence is one kernel (the prepare launch is empty): everything it reads
