@@ -39,6 +39,7 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void bwd_chains_kernel(BwdParams 
     constexpr int NSL = V / 16;
     int unit, sub;
     if (!state_unit(blockIdx.x, 2 * NSL, b.f.seq.N * b.f.HV, &unit, &sub)) return;
+    unit = longest_first(b.f.seq, b.f.HV, unit);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n0 = (sub >> 1) * 16;
     constexpr int RB = WsF32B<K, V>::BYTES;
     if (sub & 1)

@@ -626,6 +626,36 @@ __device__ __forceinline__ void vm_drain() {
     __builtin_amdgcn_s_waitcnt(0x0f60);
 }
 
+// Packed sequences, longest first: the unit of ordinal u is value head u % HV of the sequence
+// whose length ranks u / HV (ties by index). Workgroups start in blockIdx order, so the longest
+// chains, which set the end of a launch of several rounds, start first and the short ones fill
+// in behind them. The bounds are read with wave-uniform loads (the scalar memory path), lane n
+// keeps sequence n's length, and each lane ranks its length against the other lanes' through
+// readlane; each wave computes the same answer, so no workgroup barrier is needed. More than 64
+// sequences keep the input order. The map only reorders whole units: every workgroup of a
+// unit computes the same unit.
+__device__ __forceinline__ int longest_first(const SeqGeom &sg, int HV, int u) {
+    const int N = sg.N;
+    if (sg.cu == nullptr || N <= 1 || N > 64) return u;
+    const int lane = threadIdx.x & 63;
+    int64_t len = -1;
+    for (int k = 0; k < N; ++k) {
+        const int64_t bk = seq_bos(sg, k);
+        const int64_t lk = seq_eos(sg, k, bk) - bk;
+        len = lane == k ? lk : len;
+    }
+    const int lo = (int)(uint32_t)len, hi = (int)(len >> 32);
+    int rank = 0;
+    for (int k = 0; k < N; ++k) {
+        const int64_t lk = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, k) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readlane(lo, k));
+        rank += (lk > len || (lk == len && k < lane)) ? 1 : 0;
+    }
+    // ranks of lanes < N are a permutation of 0 .. N - 1: exactly one lane matches
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < N && rank == u / HV);
+    return m ? __builtin_ctzll(m) * HV + u % HV : u;
+}
+
 }  // namespace kda
 
 // Host-side launchers (defined next to their kernels).

@@ -181,6 +181,7 @@ __global__ __launch_bounds__(128) void state_bf16_kernel(FwdParams p)
     const int grp = lane >> 4, n = lane & 15;
     int unit, slice;
     if (!state_unit(blockIdx.x, NV, p.seq.N * p.HV, &unit, &slice)) return;
+    unit = longest_first(p.seq, p.HV, unit);
     const int j = unit % p.HV;
     const int s = unit / p.HV;
     const int64_t bos = seq_bos(p.seq, s);
@@ -259,6 +260,7 @@ __global__ __launch_bounds__(64 * CHAIN_WAVES) void state_f32_kernel(FwdParams p
 {
     int unit, slice;
     if (!state_unit(blockIdx.x, V / 16, p.seq.N * p.HV, &unit, &slice)) return;
+    unit = longest_first(p.seq, p.HV, unit);
     chain_run<K, V, CHAIN_FORWARD>(p, unit, slice * 16, threadIdx.x >> 6, threadIdx.x & 63,
                                    p.h0, nullptr, p.ht, (float *)p.o, WsF32<K, V>::BYTES);
 }

@@ -16,6 +16,7 @@ __global__ __launch_bounds__(256 * SPW) void state64_bf16_kernel(FwdParams p)
     const int lane = threadIdx.x & 63;
     int unit, group;
     if (!state_unit64(blockIdx.x, NG, p.seq.N * p.HV, &unit, &group)) return;
+    unit = longest_first(p.seq, p.HV, unit);
     const int slice = group * SPW + sw;
     state64_slice<K, V, 0, TWOK>(p, hos[sw], unit, slice, role, lane);
 }
