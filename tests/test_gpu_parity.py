@@ -93,12 +93,14 @@ SMALL = {
     "bf16_b8_h16_t45_slices4": W.custom(B=8, T=45, H=16, HV=16, K=128, V=128),
     "bf16_b16_h16_k64v64_slices4": W.custom(B=16, T=40, H=16, HV=16, K=64, V=64, h0_std=0.1),
     # packed sequences run longest first: tied and empty lengths (ties keep the input order),
-    # uneven lengths with enough units for four slices per workgroup, and more than 64
-    # sequences (input order)
+    # uneven lengths with enough units for four slices per workgroup, exactly 64 sequences
+    # (every lane of the ranking wave holds one) and more than 64 (input order)
     "bf16_varlen_ties_h0": W.custom(H=1, HV=2, K=128, V=128, h0_std=0.1,
                                     lengths=(40, 100, 40, 0, 100, 0, 7)),
     "bf16_varlen_gva_slices4": W.custom(H=8, HV=16, K=128, V=128, h0_std=0.1,
                                         lengths=(3, 70, 150, 64, 33, 0, 97, 12)),
+    "bf16_varlen_n64": W.custom(H=1, HV=2, K=64, V=64,
+                                lengths=tuple((5 * i) % 37 for i in range(64))),
     "bf16_varlen_n70": W.custom(H=1, HV=1, K=64, V=64,
                                 lengths=tuple((7 * i) % 23 for i in range(70))),
     # dense batches of at least 16 chunks whose value slices fill at most half of a 256-CU part:
